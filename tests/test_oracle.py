@@ -1,0 +1,493 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+* hand-worked closed-form cases (tests/golden/hand_worked.json);
+* Top-K against NumPy's lexsort and against exhaustive search over subsets;
+* the gathered-token formulation against a dense masked one (tiny inputs);
+* k = C with all gates equal, and k = 0, against torch's CPU
+  scaled_dot_product_attention (library routine, float64);
+* gate shift invariance and normalisation;
+* the log-gate gradient, eq. 5's g-space gradient and dQ/dK/dV against central
+  finite differences, plus exact identities of the backward;
+* summaries and scores on inputs with closed-form answers, a planted-key
+  recall check, and decode/prefill score consistency;
+* planted mistakes: each mutation of the oracle must make some pin fail.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_amd import synth
+from oracle import sas_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = json.load(open(os.path.join(HERE, "golden", "hand_worked.json")))
+
+
+# --------------------------------------------------------------------------
+# helpers (plain NumPy / torch library calls, no oracle arithmetic)
+# --------------------------------------------------------------------------
+def _rand_prefill(seed, Hq=4, Hkv=2, d=8, S=20):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((Hq, S, d))
+    K = rng.standard_normal((Hkv, S, d))
+    V = rng.standard_normal((Hkv, S, d))
+    dO = rng.standard_normal((Hq, S, d))
+    return Q, K, V, dO
+
+
+def _random_selection(rng, Hkv, n_tiles, k):
+    idx = np.full((Hkv, n_tiles, k), -1, np.int64)
+    lg = np.full((Hkv, n_tiles, k), -np.inf)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            n = min(k, t)
+            ch = np.sort(rng.choice(t, size=n, replace=False)) if n else []
+            for s, m in enumerate(ch):
+                idx[r, t, s] = m
+                lg[r, t, s] = -abs(rng.standard_normal()) - 0.5
+    return idx, lg
+
+
+def _sdpa(q, k, v, mask, scale):
+    """torch CPU SDPA in float64; q [H,L,d], k/v [H,S,d], mask [H or 1, L, S] additive."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        attn_mask=torch.from_numpy(mask)[None], scale=scale)
+    return out[0].numpy()
+
+
+# --------------------------------------------------------------------------
+# hand-worked cases
+# --------------------------------------------------------------------------
+def check_hand_worked():
+    g = GOLDEN["gate"]
+    lse, logg = O.gate(np.asarray(g["s"]))
+    assert abs(lse - g["lse"]) < 1e-12
+    np.testing.assert_allclose(logg, g["log_g"], atol=1e-12)
+    for case in GOLDEN["decode"]:
+        b, T = case["b"], case["T"]
+        q = np.asarray(case["q"]).reshape(1, 1)
+        K = np.asarray(case["K"]).reshape(1, T, 1)
+        V = np.asarray(case["V"]).reshape(1, T, 1)
+        idx, lg, _, _ = O.select_rows([np.asarray(case["s"])], case["k"])
+        assert [int(m) for m in idx[0] if m >= 0] == case["idx"], case["name"]
+        o, l = O.decode_attend(q, K, V, T, idx, lg, 1.0, 1, b=b, gated=case["gated"])
+        assert abs(o[0, 0] - case["o"]) < 1e-12, case["name"]
+        assert abs(l[0] - case["lse"]) < 1e-12, case["name"]
+    pb = GOLDEN["prefill_backward"]
+    b, S = pb["b"], pb["S"]
+    Q = np.asarray(pb["Q"]).reshape(1, S, 1)
+    K = np.asarray(pb["K"]).reshape(1, S, 1)
+    V = np.asarray(pb["V"]).reshape(1, S, 1)
+    dO = np.asarray(pb["dO"]).reshape(1, S, 1)
+    idx = np.asarray(pb["idx"]).reshape(1, S, 2)
+    lg = np.asarray([[np.nan if x is None else x for x in row] for row in pb["log_gate"]])
+    lg = np.where(np.isnan(lg), -np.inf, lg).reshape(1, S, 2)
+    Ot, _ = O.prefill_attend(Q, K, V, S, idx, lg, 1.0, 1, b=b)
+    np.testing.assert_allclose(Ot[0, :, 0], pb["O"], atol=1e-12)
+    _, _, _, dlg = O.prefill_backward(Q, K, V, dO, S, idx, lg, 1.0, 1, b=b)
+    np.testing.assert_allclose(dlg[0], pb["dlog_gate"], atol=1e-12)
+
+
+def test_hand_worked_cases():
+    check_hand_worked()
+
+
+# --------------------------------------------------------------------------
+# Top-K
+# --------------------------------------------------------------------------
+def check_topk_lexsort(seed=0):
+    rng = np.random.default_rng(seed)
+    for trial in range(200):
+        C = int(rng.integers(0, 300))
+        k = int(rng.integers(0, 40))
+        # coarse values make exact ties common
+        s = np.round(rng.standard_normal(C) * 4) / 4 if trial % 2 else rng.standard_normal(C)
+        chosen, gap = O.topk(s, k)
+        ref = np.lexsort((np.arange(C), -s))[:min(k, C)]
+        assert chosen == sorted(ref.tolist())
+        if 0 < k < C:
+            srt = np.sort(s)[::-1]
+            assert gap == srt[k - 1] - srt[k]
+        else:
+            assert gap == math.inf
+
+
+def test_topk_matches_lexsort():
+    check_topk_lexsort()
+
+
+def check_topk_exhaustive(seed=1):
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        C = int(rng.integers(1, 11))
+        k = int(rng.integers(0, C + 2))
+        s = rng.integers(-3, 4, size=C).astype(np.float64)   # integer scores: exact sums, many ties
+        kk = min(k, C)
+        best = None
+        for sub in itertools.combinations(range(C), kk):
+            key = (-sum(s[list(sub)]), sub)                  # max sum, then lexicographically smallest
+            if best is None or key < best:
+                best = key
+        chosen, _ = O.topk(s, k)
+        assert tuple(chosen) == best[1]
+
+
+def test_topk_exhaustive_small():
+    check_topk_exhaustive()
+
+
+def test_topk_on_scores_equals_topk_on_gate():
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        s = rng.standard_normal(100) * 3
+        _, logg = O.gate(s)
+        g = np.exp(logg)
+        assert O.topk(s, 16)[0] == sorted(np.argsort(-g, kind="stable")[:16].tolist())
+
+
+# --------------------------------------------------------------------------
+# two formulations agree (brute force on tiny inputs)
+# --------------------------------------------------------------------------
+def check_gather_vs_dense(seed=3):
+    rng = np.random.default_rng(seed)
+    for b in (4, 64):
+        for T in (1, b - 1, b, b + 1, 3 * b + 5, 7 * b):
+            Hq, Hkv, d = 4, 2, 8
+            q = rng.standard_normal((Hq, d))
+            K = rng.standard_normal((Hkv, T, d))
+            V = rng.standard_normal((Hkv, T, d))
+            C = O.n_history_blocks(T, b)
+            for k in (0, 1, 3, C + 2):
+                s = [rng.standard_normal(C) for _ in range(Hkv)]
+                idx, lg, _, _ = O.select_rows(s, k)
+                for gated in (True, False):
+                    o1, l1 = O.decode_attend(q, K, V, T, idx, lg, 0.35, 2, b, gated)
+                    o2, l2 = O.dense_masked_decode(q, K, V, T, idx, lg, 0.35, 2, b, gated)
+                    np.testing.assert_allclose(o1, o2, atol=1e-12)
+                    np.testing.assert_allclose(l1, l2, atol=1e-12)
+    for b, S in ((4, 1), (4, 7), (4, 17), (4, 24), (8, 45)):
+        Q, K, V, _ = _rand_prefill(seed + S, S=S)
+        n_tiles = -(-S // b)
+        for k in (0, 2, n_tiles):
+            idx, lg = _random_selection(rng, 2, n_tiles, k)
+            o1, l1 = O.prefill_attend(Q, K, V, S, idx, lg, 0.3, 2, b)
+            o2, l2 = O.dense_masked_prefill(Q, K, V, S, idx, lg, 0.3, 2, b)
+            np.testing.assert_allclose(o1, o2, atol=1e-12)
+            np.testing.assert_allclose(l1, l2, atol=1e-12)
+
+
+def test_gather_equals_dense_masked():
+    check_gather_vs_dense()
+
+
+# --------------------------------------------------------------------------
+# k = C with equal gates, and k = 0, against torch SDPA
+# --------------------------------------------------------------------------
+def _decode_problem(seed, T, b=64, k=None, zero_wq=False, Hq=4, Hkv=2, d=16):
+    wl = synth.custom_workload("decode", n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, sel_dim=d,
+                               top_k=k if k is not None else 4, seq_len=T)
+    return synth.make_problem(wl, seed, zero_wq=zero_wq)
+
+
+def check_uniform_gate_is_dense_with_bias(seed=4):
+    for T in (65, 200, 257, 64 * 6):
+        C = O.n_history_blocks(T)
+        p = _decode_problem(seed, T, k=C + 3, zero_wq=True)
+        q, K, V = p.f64("q")[0], p.f64("K")[0], p.f64("V")[0]
+        d = q.shape[1]
+        res = O.decode_step(p.f64("q"), p.f64("K"), p.f64("V"), p.seq_lens, p.f64("Wq_sel"),
+                            p.f64("Wk_sel"), C + 3)
+        mask = np.zeros((1, 1, T))
+        mask[..., :64 * C] = -math.log(C) if C else 0.0
+        for h in range(4):
+            r = h // 2
+            ref = _sdpa(q[h][None, None], K[r][None, :T], V[r][None, :T], mask, 1 / math.sqrt(d))
+            np.testing.assert_allclose(res["o"][0, h], ref[0, 0], atol=1e-10)
+    # prefill: every tile selects all its history with log g = -ln t
+    S, b = 23, 4
+    Q, K, V, _ = _rand_prefill(seed, S=S)
+    Wk = np.random.default_rng(seed).standard_normal((8, 8))
+    sel = O.prefill_select(Q, K, S, np.zeros((8, 8)), Wk, k=10, G=2, b=b)
+    Ot, _ = O.prefill_attend(Q, K, V, S, sel["idx"], sel["log_gate"], 0.4, 2, b)
+    mask = np.full((1, S, S), -np.inf)
+    for i in range(S):
+        t = i // b
+        if t:
+            mask[0, i, :b * t] = -math.log(t)
+        mask[0, i, b * t:i + 1] = 0.0
+    for h in range(4):
+        ref = _sdpa(Q[h][None], K[h // 2][None], V[h // 2][None], mask, 0.4)
+        np.testing.assert_allclose(Ot[h], ref[0], atol=1e-10)
+
+
+def test_k_equals_C_uniform_gate_is_dense_attention_with_bias():
+    check_uniform_gate_is_dense_with_bias()
+
+
+def check_k0_is_local_causal(seed=5):
+    for T in (1, 63, 64, 65, 130):
+        p = _decode_problem(seed, T, k=0)
+        q, K, V = p.f64("q")[0], p.f64("K")[0], p.f64("V")[0]
+        res = O.decode_step(p.f64("q"), p.f64("K"), p.f64("V"), p.seq_lens, p.f64("Wq_sel"),
+                            p.f64("Wk_sel"), 0)
+        b0 = 64 * O.n_history_blocks(T)
+        for h in range(4):
+            r = h // 2
+            ref = _sdpa(q[h][None, None], K[r][None, b0:T], V[r][None, b0:T],
+                        np.zeros((1, 1, T - b0)), 0.25)
+            np.testing.assert_allclose(res["o"][0, h], ref[0, 0], atol=1e-10)
+    S, b = 22, 4
+    Q, K, V, _ = _rand_prefill(seed, S=S)
+    idx = np.full((2, 6, 0), -1, np.int64)
+    lg = np.zeros((2, 6, 0))
+    Ot, _ = O.prefill_attend(Q, K, V, S, idx, lg, 0.5, 2, b)
+    for t in range(6):
+        i0, i1 = b * t, min(b * t + b, S)
+        n = i1 - i0
+        causal = np.triu(np.full((n, n), -np.inf), 1)[None]
+        for h in range(4):
+            ref = _sdpa(Q[h][None, i0:i1], K[h // 2][None, i0:i1], V[h // 2][None, i0:i1],
+                        causal, 0.5)
+            np.testing.assert_allclose(Ot[h, i0:i1], ref[0], atol=1e-10)
+
+
+def test_k0_is_local_causal_attention():
+    check_k0_is_local_causal()
+
+
+# --------------------------------------------------------------------------
+# gate properties
+# --------------------------------------------------------------------------
+def test_gate_shift_invariance_and_normalisation():
+    rng = np.random.default_rng(6)
+    p = _decode_problem(6, 64 * 9 + 3, k=3)
+    q, K, V = p.f64("q")[0], p.f64("K")[0], p.f64("V")[0]
+    T = int(p.seq_lens[0])
+    for _ in range(10):
+        s = rng.standard_normal(9) * 2
+        c = rng.standard_normal() * 50
+        l1, g1 = O.gate(s)
+        l2, g2 = O.gate(s + c)
+        np.testing.assert_allclose(g1, g2, atol=1e-12)
+        assert abs(l2 - l1 - c) < 1e-9
+        assert abs(np.exp(g1).sum() - 1.0) < 1e-12
+        i1, lg1, _, _ = O.select_rows([s, s[::-1].copy()], 3)
+        i2, lg2, _, _ = O.select_rows([s + c, s[::-1] + c], 3)
+        assert (i1 == i2).all()
+        o1, _ = O.decode_attend(q, K, V, T, i1, lg1, 0.25, 2)
+        o2, _ = O.decode_attend(q, K, V, T, i2, lg2, 0.25, 2)
+        np.testing.assert_allclose(o1, o2, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# backward: finite differences and identities
+# --------------------------------------------------------------------------
+def _loss(Q, K, V, dO, S, idx, lg, scale, G, b):
+    Ot, _ = O.prefill_attend(Q, K, V, S, idx, lg, scale, G, b)
+    return float(np.sum(Ot * dO))
+
+
+def check_dlog_gate_fd(seed=7):
+    S, b, k, G, scale = 21, 4, 2, 2, 0.37
+    Q, K, V, dO = _rand_prefill(seed, S=S)
+    rng = np.random.default_rng(seed)
+    idx, lg = _random_selection(rng, 2, 6, k)
+    _, _, _, dlg = O.prefill_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    h = 1e-6
+    fd = np.zeros_like(dlg)
+    fd_g = np.zeros_like(dlg)
+    for r, t, s in zip(*np.nonzero(idx >= 0)):
+        lp, lm = lg.copy(), lg.copy()
+        lp[r, t, s] += h
+        lm[r, t, s] -= h
+        fd[r, t, s] = (_loss(Q, K, V, dO, S, idx, lp, scale, G, b) -
+                       _loss(Q, K, V, dO, S, idx, lm, scale, G, b)) / (2 * h)
+        # eq. 5 lives in g-space: dL/dg_m; log g is the input, so perturb g itself
+        g = math.exp(lg[r, t, s])
+        lp[r, t, s] = math.log(g + h)
+        lm[r, t, s] = math.log(g - h)
+        dLdg = (_loss(Q, K, V, dO, S, idx, lp, scale, G, b) -
+                _loss(Q, K, V, dO, S, idx, lm, scale, G, b)) / (2 * h)
+        fd_g[r, t, s] = g * dLdg
+    assert np.abs(fd).max() > 1e-3
+    np.testing.assert_allclose(dlg, fd, atol=1e-6 * np.abs(fd).max(), rtol=1e-6)
+    np.testing.assert_allclose(dlg, fd_g, atol=1e-6 * np.abs(fd).max(), rtol=1e-6)
+    assert (dlg[idx < 0] == 0).all()
+
+
+def test_dlog_gate_matches_finite_differences():
+    check_dlog_gate_fd()
+
+
+def check_qkv_grads_fd(seed=8):
+    S, b, k, G, scale = 19, 4, 2, 2, 0.41
+    Q, K, V, dO = _rand_prefill(seed, S=S)
+    rng = np.random.default_rng(seed + 1)
+    idx, lg = _random_selection(rng, 2, 5, k)
+    dQ, dK, dV, _ = O.prefill_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    h = 1e-6
+    for name, X, grad in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, n)) for n in X.shape)
+            Xp, Xm = X.copy(), X.copy()
+            Xp[pos] += h
+            Xm[pos] -= h
+            args_p = {"Q": Q, "K": K, "V": V}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = Xp, Xm
+            fd = (_loss(args_p["Q"], args_p["K"], args_p["V"], dO, S, idx, lg, scale, G, b) -
+                  _loss(args_m["Q"], args_m["K"], args_m["V"], dO, S, idx, lg, scale, G, b)) / (2 * h)
+            assert abs(fd - grad[pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, grad[pos])
+
+
+def test_qkv_grads_match_finite_differences():
+    check_qkv_grads_fd()
+
+
+def test_backward_identities():
+    """Sum_j dV_j = Sum_rows dO per group (softmax rows sum to 1) and
+    Sum_j dK_j = 0 per group (a shift of every key leaves each row unchanged)."""
+    S, b, k, G = 30, 4, 3, 2
+    Q, K, V, dO = _rand_prefill(9, S=S)
+    idx, lg = _random_selection(np.random.default_rng(9), 2, 8, k)
+    dQ, dK, dV, _ = O.prefill_backward(Q, K, V, dO, S, idx, lg, 0.3, G, b)
+    for r in range(2):
+        np.testing.assert_allclose(dV[r].sum(axis=0), dO[r * G:(r + 1) * G].sum(axis=(0, 1)),
+                                   atol=1e-12)
+        np.testing.assert_allclose(dK[r].sum(axis=0), 0.0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# summaries and scores
+# --------------------------------------------------------------------------
+def check_summaries(seed=10):
+    rng = np.random.default_rng(seed)
+    d, ds, b = 8, 6, 4
+    W = rng.standard_normal((ds, d))
+    for T in (1, 4, 5, 17, 32, 33):
+        C = O.n_history_blocks(T, b)
+        consts = rng.standard_normal((2, C + 2, d))
+        K = np.repeat(consts, b, axis=1)[:, :T + b]          # constant keys inside each block
+        K = K + 0.0
+        summ = O.block_summaries(K, T, W, b)
+        assert summ.shape == (2, C, ds)
+        for r in range(2):
+            for m in range(C):
+                np.testing.assert_allclose(summ[r, m], W @ consts[r, m], atol=1e-12)
+        # reordering keys inside a block, or changing B0 / later tokens, changes nothing
+        K2 = K.copy()
+        for m in range(C):
+            K2[:, b * m:b * m + b] = K2[:, b * m:b * m + b][:, ::-1]
+        K2[:, b * C:] = rng.standard_normal(K2[:, b * C:].shape)
+        np.testing.assert_allclose(O.block_summaries(K2, T, W, b), summ, atol=1e-12)
+
+
+def test_summaries_closed_forms():
+    check_summaries()
+
+
+def test_scores_closed_form_identity_projection():
+    """Wq_sel = Wk_sel = I and block-constant keys c_m: s_m = mean_h(q_h).c_m / sqrt(d)."""
+    rng = np.random.default_rng(11)
+    d, b, T, G = 8, 4, 23, 3
+    C = O.n_history_blocks(T, b)
+    c = rng.standard_normal((1, C + 1, d))
+    K = np.repeat(c, b, axis=1)
+    q = rng.standard_normal((G, d))
+    summ = O.block_summaries(K, T, np.eye(d), b)
+    s = O.decode_scores(q, np.eye(d), summ, G)
+    expect = np.array([q.mean(axis=0) @ c[0, m] for m in range(C)]) / math.sqrt(d)
+    np.testing.assert_allclose(s[0], expect, atol=1e-12)
+
+
+def test_tile_scores_match_decode_scores():
+    """A prefill tile whose queries all equal one decode query scores history
+    blocks exactly like that decode query."""
+    rng = np.random.default_rng(12)
+    d, ds, b, G, S = 8, 5, 4, 2, 20
+    K = rng.standard_normal((2, S, d))
+    Wq, Wk = rng.standard_normal((ds, d)), rng.standard_normal((ds, d))
+    qdec = rng.standard_normal((4, d))
+    Q = np.repeat(qdec[:, None, :], S, axis=1)
+    summ = O.block_summaries(K, S, Wk, b)
+    rows = O.tile_scores(Q, S, Wq, summ, G, b)
+    for t in range(1, -(-S // b)):
+        sd = O.decode_scores(qdec, Wq, summ[:, :t], G)
+        np.testing.assert_allclose(rows[t], sd, atol=1e-12)
+
+
+def test_planted_blocks_are_recalled():
+    """With identity selector projections, blocks whose keys carry a strong copy
+    of the group query outrank random blocks, so Top-k lands inside the plant."""
+    wl = synth.custom_workload("decode", n_q_heads=8, n_kv_heads=2, head_dim=32, sel_dim=32,
+                               top_k=8, seq_len=64 * 400 + 1, plant_frac=0.03)
+    p = synth.make_problem(wl, 0)
+    d = 32
+    res = O.decode_step(p.f64("q"), p.f64("K"), p.f64("V"), p.seq_lens, np.eye(d), np.eye(d), 8)
+    for r in range(2):
+        chosen = res["idx"][0, r]
+        assert p.planted[0, r, chosen].all()
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: every mutation must break at least one pin
+# --------------------------------------------------------------------------
+PINS = [check_hand_worked, check_topk_lexsort, check_topk_exhaustive, check_gather_vs_dense,
+        check_uniform_gate_is_dense_with_bias, check_k0_is_local_causal, check_dlog_gate_fd,
+        check_qkv_grads_fd, check_summaries]
+
+
+def _some_pin_fails():
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            return True
+    return False
+
+
+def _wrong_gate_sign(s):
+    lse, logg = _ORIG["gate"](s)
+    return lse, -logg
+
+
+def _topk_highest_index_ties(s, k):
+    C = int(s.size)
+    kk = max(0, min(int(k), C))
+    order = sorted(range(C), key=lambda m: (-float(s[m]), -m))
+    return sorted(order[:kk]), _ORIG["topk"](s, k)[1]
+
+
+def _summaries_sum_not_mean(K, T, Wk, b=O.BLOCK):
+    return _ORIG["block_summaries"](K, T, Wk, b) * b
+
+
+_ORIG = {"gate": O.gate, "topk": O.topk, "block_summaries": O.block_summaries,
+         "_selected_tokens": O._selected_tokens}
+
+
+def _drop_gate_bias(idx_row, lg_row, b, gated):
+    return _ORIG["_selected_tokens"](idx_row, lg_row, b, False)
+
+
+def _off_by_one_block(idx_row, lg_row, b, gated):
+    toks, bias = _ORIG["_selected_tokens"](idx_row, lg_row, b, gated)
+    return [t + 1 if t + 1 < 10 ** 9 else t for t in toks], bias
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("gate", _wrong_gate_sign),
+    ("topk", _topk_highest_index_ties),
+    ("block_summaries", _summaries_sum_not_mean),
+    ("_selected_tokens", _drop_gate_bias),
+    ("_selected_tokens", _off_by_one_block),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    assert _some_pin_fails()
