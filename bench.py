@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the SAS hot path on one MI355X (prints ONE JSON line).
+
+Default workload: one decode step of one attention layer at the Qwen3-4B
+attention shape (32 query heads, 8 KV heads, d=128, bf16 KV cache, fp32
+accumulation), 64K context, block 64, top-k=16 + the current block, selector
+dim 128, synthetic seeded inputs.  A step is the whole decode-time path:
+
+  1. sas_block_summaries on the newest complete block (the steady-state
+     refresh; it is due once every 64 steps, run here every step),
+  2. sas_select (selector score over every history-block summary, softmax-gate
+     LSE, Top-K),
+  3. sas_decode_fwd (split-KV gated attention over the selected blocks + B0,
+     then the LSE merge).
+
+Inputs are resident in HBM before timing starts.  Each timed step is
+bracketed by HIP events on the stream the library launches on; between steps
+(outside the events) a 512 MiB write evicts the 256 MB Infinity Cache and the
+L2, so every step reads its bytes from HBM.  ``--workload qwen3_4b_prefill_16k``
+times the training-style prefill forward + backward instead.
+
+Extra fields beside the contract keys: ``breakdown_us`` (per-op medians),
+``roofline`` for the dominant kernel, ``cpu_baseline`` (the float64 CPU
+oracle on a bounded sample of the same step, timed on this host).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="qwen3_4b_decode_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle sample")
+    ap.add_argument("--no-flush", action="store_true", help="hot-cache timing only")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for PMC byte calibration)")
+    return ap.parse_args()
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+# --------------------------------------------------------------------------
+# decode
+# --------------------------------------------------------------------------
+def decode_bytes(wl, lens):
+    """Algorithmic bytes of one decode step, split by stage."""
+    es = 2 if wl.dtype == "bf16" else 4
+    d, Hq, Hkv, k, ds = wl.head_dim, wl.n_q_heads, wl.n_kv_heads, wl.top_k, wl.sel_dim
+    kv = 0
+    summ = 0
+    for T in lens:
+        C = (int(T) - 1) // 64
+        n0 = int(T) - 64 * C
+        kv += Hkv * (min(k, C) * 64 + n0) * d * es * 2
+        summ += Hkv * C * ds * 4
+    B = len(lens)
+    attn = kv + 2 * B * Hq * d * es + 2 * B * Hkv * k * 4 + B * Hq * 4
+    select = summ + ds * d * 4 + B * Hq * d * es + 2 * B * Hkv * k * 4 + B * Hkv * 4
+    refresh = B * Hkv * 64 * d * es + ds * d * 4 + B * Hkv * ds * 4
+    return {"attention": attn, "kv": kv, "select": select, "refresh": refresh,
+            "step": attn + select + refresh}
+
+
+def run_decode(args, wl):
+    import torch
+    from gated_block_sparse_amd import binding as S
+    from gated_block_sparse_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    p = synth.make_problem(wl, seed=0)
+    B, Hq, Hkv, d, ds, k = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.sel_dim, wl.top_k
+    t_max = p.K.shape[2]
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, K, V = up(p.q), up(p.K), up(p.V)
+    lens = torch.from_numpy(p.seq_lens).to(dev)
+    Wq, Wk = up(p.Wq_sel), up(p.Wk_sel)
+    # prefilled state: summaries of every complete block
+    summ = S.sas_block_summaries(K, lens, Wk)
+    idx, lg, slse, _ = S.sas_select(S.SAS_SELECT_DECODE, q, lens, Wq, summ, k)
+    o, lse = S.sas_decode_fwd(q, K, V, lens, idx, lg)
+    torch.cuda.synchronize()
+
+    lib = S.load_library()
+    import ctypes
+    dims = S.make_dims(B, Hq, Hkv, d, ds, k, t_max, S.SAS_BF16 if wl.dtype == "bf16" else S.SAS_F32)
+    pd = ctypes.byref(dims)
+    ws_sel = torch.empty(max(1, S.sas_workspace_bytes(S.SAS_OP_SELECT_DECODE, dims)), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(1, S.sas_workspace_bytes(S.SAS_OP_DECODE_FWD, dims)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    c_new = int(min((int(T) - 1) // 64 for T in p.seq_lens))
+    blk0, blk1 = max(c_new - 1, 0), max(c_new, 0)
+    scale = 1.0 / math.sqrt(d)
+    a_sum = (pd, K.data_ptr(), lens.data_ptr(), Wk.data_ptr(), blk0, blk1, summ.data_ptr(), sp)
+    a_sel = (pd, S.SAS_SELECT_DECODE, q.data_ptr(), 0, lens.data_ptr(), Wq.data_ptr(),
+             summ.data_ptr(), idx.data_ptr(), lg.data_ptr(), slse.data_ptr(), None,
+             ws_sel.data_ptr(), ws_sel.numel(), sp)
+    a_dec = (pd, q.data_ptr(), K.data_ptr(), V.data_ptr(), lens.data_ptr(), idx.data_ptr(),
+             lg.data_ptr(), scale, o.data_ptr(), lse.data_ptr(), ws_dec.data_ptr(),
+             ws_dec.numel(), sp)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        st = lib.sas_block_summaries(*a_sum)
+        if evs:
+            evs[1].record(stream)
+        st |= lib.sas_select(*a_sel)
+        if evs:
+            evs[2].record(stream)
+        st |= lib.sas_decode_fwd(*a_dec)
+        if evs:
+            evs[3].record(stream)
+        if st:
+            raise S.SasError(st, lib.sas_last_error().decode())
+
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        if not args.no_flush:
+            flush.fill_(float(i))          # evict MALL/L2; also covers host launch latency
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tot = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    t_sum = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    t_sel = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    t_dec = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+
+    # hot-cache figure: the same step replayed back to back from a HIP graph
+    hot_us = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(stream)
+        with torch.cuda.stream(s2):
+            sp2 = s2.cuda_stream
+            a2 = [tuple(sp2 if x is sp else x for x in a) for a in (a_sum, a_sel, a_dec)]
+            g.capture_begin()
+            lib.sas_block_summaries(*a2[0])
+            lib.sas_select(*a2[1])
+            lib.sas_decode_fwd(*a2[2])
+            g.capture_end()
+        stream.wait_stream(s2)
+        for _ in range(5):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n_hot = 200
+        for _ in range(n_hot):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        hot_us = e0.elapsed_time(e1) * 1e3 / n_hot
+    except Exception as exc:  # graph capture is a reported extra, never the headline
+        print(f"# hot-cache graph timing skipped: {exc}", file=sys.stderr)
+
+    by = decode_bytes(wl, p.seq_lens)
+    med = statistics.median
+    us_step, us_dec = med(tot), med(t_dec)
+    achieved = by["attention"] / (us_dec * 1e-6) / 1e9
+    res = {
+        "metric": "SAS decode attn us/step + achieved HBM GB/s (% peak), Qwen3-4B shape @64K",
+        "value": round(us_step, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, K x U(0.5,2) per channel; random selector weights)",
+        "config": {"workload": wl.name, "batch": B, "context": [int(x) for x in p.seq_lens][:8],
+                   "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "sel_dim": ds,
+                   "block": 64, "top_k": k, "cache": "hot" if args.no_flush else "cold (MALL+L2 flushed)"},
+        "tokens_per_s": round(B / (us_step * 1e-6), 1),
+        "breakdown_us": {
+            "summary_refresh": {"median": round(med(t_sum), 3)},
+            "select": {"median": round(med(t_sel), 3), "p10": round(_pct(t_sel, .1), 3), "p90": round(_pct(t_sel, .9), 3)},
+            "decode_attention": {"median": round(us_dec, 3), "p10": round(_pct(t_dec, .1), 3), "p90": round(_pct(t_dec, .9), 3)},
+            "step": {"median": round(us_step, 3), "p10": round(_pct(tot, .1), 3), "p90": round(_pct(tot, .9), 3)},
+            "step_hot_graph": None if hot_us is None else round(hot_us, 3),
+        },
+        "bytes": by,
+        "step_GBps": round(by["step"] / (us_step * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "sas_decode_fwd (split-KV + merge)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    return res, p
+
+
+def cpu_baseline_decode(p, budget_s):
+    """The float64 oracle on the same decode step, repeated for ~budget_s."""
+    from oracle import sas_oracle as O
+    from gated_block_sparse_amd import synth
+    wl = p.wl
+    G = wl.n_q_heads // wl.n_kv_heads
+    d = wl.head_dim
+    b = 0
+    T = int(p.seq_lens[b])
+    # prefilled state for the oracle: its own summaries of every history block
+    per = []
+    for r in range(wl.n_kv_heads):
+        Kr = synth.to_f64(p.K[b, r:r + 1, :T], wl.dtype)
+        Vr = synth.to_f64(p.V[b, r:r + 1, :T], wl.dtype)
+        per.append((Kr, Vr, O.block_summaries(Kr, T, p.f64("Wk_sel"))))
+    q = synth.to_f64(p.q[b], wl.dtype)
+    Wq, Wk = p.f64("Wq_sel"), p.f64("Wk_sel")
+    C = O.n_history_blocks(T)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for r, (Kr, Vr, summ) in enumerate(per):
+            # refresh the newest block, score, gate, Top-K, attend
+            O.block_summaries(Kr[:, 64 * (C - 1):64 * C + 1], 65, Wk)
+            qg = q[r * G:(r + 1) * G]
+            s = O.decode_scores(qg, Wq, summ, G)[0]
+            idx, lg, _, _ = O.select_rows([s], wl.top_k)
+            O.decode_attend(qg, Kr, Vr, T, idx, lg, 1.0 / math.sqrt(d), G)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    us = el / n * 1e6
+    return us, n
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [x for x in threadpool_info() if x.get("user_api") == "blas"]
+        if info:
+            return int(info[0]["num_threads"])
+    except Exception:
+        pass
+    return 1
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the sharding plan is described in DESIGN.md)"}))
+        sys.exit(2)
+    from gated_block_sparse_amd import synth
+    wl = synth.WORKLOADS[args.workload]
+    if wl.mode != "decode":
+        raise SystemExit("prefill benchmark not available yet")
+    res, p = run_decode(args, wl)
+    if args.calibrate_copy:
+        import torch
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        bb = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        bb.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": bb.numel() * 4}
+    if not args.no_cpu_baseline:
+        us, n = cpu_baseline_decode(p, args.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(us, 1), "unit": "us/step", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n} full decode steps of sequence 0 (all {wl.n_kv_heads} groups: newest-"
+                      f"block summary, scores over every block, gate, Top-K, attention), float64 "
+                      f"NumPy, host CPUs available: {len(os.sched_getaffinity(0))}",
+        }
+        res["gpu_speedup_vs_cpu_oracle"] = round(us / res["value"], 1)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,67 @@
+// Internal declarations shared by the libsas translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/sas.h"
+
+namespace sas {
+
+constexpr int kBlock = 64;          // tokens per block (the only size built)
+constexpr int kMaxTopK = 64;        // largest k built
+constexpr int kSelChunk = 256;      // history blocks scored per workgroup in decode select
+constexpr int kMaxTileRows = 1024;  // prefill tiles supported by the tile selector
+
+// Set the thread-local error text (printf-style) and return `st`.
+sas_status fail(sas_status st, const char* fmt, ...);
+// Check hipGetLastError() after a launch; returns SAS_OK or SAS_ERR_HIP.
+sas_status check_launch(const char* what);
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- bf16 ---
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ------------------------------------------------------------- launchers ---
+// Each returns SAS_OK or an error after enqueuing on `st`.  Arguments are
+// already validated by the C entry points.
+
+sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
+                                  const float* Wk, int blk_begin, int blk_end, float* summ,
+                                  hipStream_t st);
+
+size_t select_decode_ws_bytes(const sas_dims& d);
+sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t* seq_lens,
+                                const float* Wq, const float* summ, int32_t* idx, float* log_gate,
+                                float* score_lse, float* scores, void* ws, hipStream_t st);
+sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, const float* Wq,
+                               const float* summ, int32_t* idx, float* log_gate,
+                               float* score_lse, float* scores, hipStream_t st);
+
+size_t decode_ws_bytes(const sas_dims& d);
+sas_status launch_decode_fwd(const sas_dims& d, const void* q, const void* K, const void* V,
+                             const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
+                             float scale, void* o, float* lse, void* ws, hipStream_t st);
+
+size_t prefill_ws_bytes(const sas_dims& d, int seq_len);
+sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,
+                              int seq_len, const int32_t* idx, const float* log_gate,
+                              float scale, void* O, float* lse, void* ws, hipStream_t st);
+
+size_t bwd_ws_bytes(const sas_dims& d, int seq_len);
+sas_status launch_bwd(const sas_dims& d, const void* Q, const void* K, const void* V,
+                      const void* O, const void* dO, const float* lse, int seq_len,
+                      const int32_t* idx, const float* log_gate, float scale, void* dQ,
+                      void* dK, void* dV, float* dlog_gate, void* ws, hipStream_t st);
+
+}  // namespace sas

@@ -1,0 +1,131 @@
+// Block summaries (SAS close reading 2.1, block summary, mean-pooled):
+//   summ[b,r,m,:] = Wk_sel . mean_{j in block m} K[b,r,j,:]
+// Pooling first and projecting once per block is the same linear map as
+// projecting every key and pooling, at 1/64 of the arithmetic.
+//
+// HBM-bound: every key of a summarised block is read once.  One workgroup
+// (4 waves) handles kSumBlocks consecutive blocks of one (b, r): each wave
+// streams whole 64-token blocks with 16-byte loads (a row is LPR lanes, so a
+// load instruction covers 64/LPR full rows, fully coalesced), sums its rows
+// in registers and finishes the column sums with a butterfly inside the wave.
+// The block means then meet Wk_sel^T, staged once per workgroup in LDS.
+#include "sas_device.h"
+#include "sas_internal.h"
+
+namespace sas {
+
+constexpr int kSumBlocks = 16;   // blocks per workgroup
+constexpr int kSumThreads = 256;
+
+template <typename T, int D, int DS>
+__global__ void __launch_bounds__(kSumThreads)
+block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_lens,
+                       const float* __restrict__ Wk, int blk_begin, int blk_end, int Hkv,
+                       int t_max, int c_max, float* __restrict__ summ) {
+  constexpr int EPL = Vec16<T>::N;          // elements per 16-byte load
+  constexpr int LPR = D / EPL;              // lanes per K row
+  constexpr int RPI = 64 / LPR;             // rows per load instruction (per wave)
+  constexpr int NI = kBlock / RPI;          // load instructions per block
+  __shared__ float Wt[D][DS];               // Wk_sel transposed: Wt[c][j] = Wk[j][c]
+  __shared__ float mean[kSumBlocks][D];
+
+  const int b = blockIdx.z, r = blockIdx.y;
+  const int first = blk_begin + blockIdx.x * kSumBlocks;
+  const int len = clamp_len(seq_lens[b], t_max);
+  const int C = (len - 1) / kBlock;
+  const int last = min(min(blk_end, C), first + kSumBlocks);  // exclusive
+  if (first >= last) return;
+  const int nblk = last - first;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // stage Wk^T
+  for (int e = tid * 4; e < D * DS; e += kSumThreads * 4) {
+    const int j = e / D, c = e % D;
+    const float4 w = *reinterpret_cast<const float4*>(Wk + e);
+    Wt[c + 0][j] = w.x;
+    Wt[c + 1][j] = w.y;
+    Wt[c + 2][j] = w.z;
+    Wt[c + 3][j] = w.w;
+  }
+
+  const T* Kr = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
+  const int col = lane % LPR, row0 = lane / LPR;
+  for (int jb = wave; jb < nblk; jb += 4) {
+    const T* blk = Kr + static_cast<size_t>(first + jb) * kBlock * D;
+    uint4 raw[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      raw[i] = *reinterpret_cast<const uint4*>(blk + (row0 + i * RPI) * D + col * EPL);
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float f[EPL];
+      Vec16<T>::unpack(raw[i], f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = wave_sum_from(acc[e], LPR);
+    if (lane < LPR) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) mean[jb][col * EPL + e] = acc[e] * (1.0f / kBlock);
+    }
+  }
+  __syncthreads();
+
+  // projection: thread -> output channel j, blocks jb0, jb0 + step, ...
+  constexpr int STEP = kSumThreads / DS;
+  constexpr int PER = kSumBlocks / STEP;
+  const int j = tid % DS, jb0 = tid / DS;
+  float out[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) out[p] = 0.f;
+  for (int c = 0; c < D; ++c) {
+    const float w = Wt[c][j];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) out[p] += w * mean[jb0 + p * STEP][c];
+  }
+  float* dst = summ + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(c_max) * DS;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int jb = jb0 + p * STEP;
+    if (jb < nblk) dst[static_cast<size_t>(first + jb) * DS + j] = out[p];
+  }
+}
+
+template <typename T, int D, int DS>
+static void launch_sum(const sas_dims& d, const void* K, const int32_t* seq_lens, const float* Wk,
+                       int blk_begin, int blk_end, float* summ, hipStream_t st) {
+  dim3 grid(cdiv(blk_end - blk_begin, kSumBlocks), d.n_kv_heads, d.batch);
+  hipLaunchKernelGGL((block_summaries_kernel<T, D, DS>), grid, dim3(kSumThreads), 0, st,
+                     static_cast<const T*>(K), seq_lens, Wk, blk_begin, blk_end, d.n_kv_heads,
+                     d.t_max, d.t_max / kBlock, summ);
+}
+
+sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
+                                  const float* Wk, int blk_begin, int blk_end, float* summ,
+                                  hipStream_t st) {
+  const bool bf = d.dtype == SAS_BF16;
+#define SAS_SUM_CASE(TT, DD, SS)                                                      \
+  if (d.head_dim == DD && d.sel_dim == SS) {                                          \
+    launch_sum<TT, DD, SS>(d, K, seq_lens, Wk, blk_begin, blk_end, summ, st);         \
+    return check_launch("block_summaries");                                           \
+  }
+  if (bf) {
+    SAS_SUM_CASE(uint16_t, 64, 64)
+    SAS_SUM_CASE(uint16_t, 64, 128)
+    SAS_SUM_CASE(uint16_t, 128, 64)
+    SAS_SUM_CASE(uint16_t, 128, 128)
+  } else {
+    SAS_SUM_CASE(float, 64, 64)
+    SAS_SUM_CASE(float, 64, 128)
+    SAS_SUM_CASE(float, 128, 64)
+    SAS_SUM_CASE(float, 128, 128)
+  }
+#undef SAS_SUM_CASE
+  return fail(SAS_ERR_UNSUPPORTED, "block_summaries: d=%d d_sel=%d", d.head_dim, d.sel_dim);
+}
+
+}  // namespace sas

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/sas.h declares, and rejects invalid arguments during validation,
+before anything is enqueued (no GPU needed: these calls return before any HIP
+call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_block_sparse_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from gated_block_sparse_amd import build
+        build.build(verbose=False)
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("sas_block_summaries", "sas_select", "sas_decode_fwd", "sas_prefill_fwd",
+              "sas_bwd", "sas_workspace_bytes", "sas_status_str", "sas_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.sas_status_str(0) == b"SAS_OK"
+    assert lib.sas_status_str(3) == b"SAS_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.sas_status_str(99) == b"SAS_UNKNOWN_STATUS"
+
+
+def _dims(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, sel_dim=128, top_k=16,
+                t_max=65536, dtype=B.SAS_BF16)
+    base.update(kw)
+    return B.make_dims(**base)
+
+
+def _decode(lib, dims, ws_bytes=1 << 30, q=FAKE, idx=FAKE, scale=0.1):
+    return lib.sas_decode_fwd(ctypes.byref(dims) if dims is not None else None, q, FAKE, FAKE,
+                              FAKE, idx, FAKE, scale, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=30), B.SAS_ERR_INVALID_ARGUMENT),   # Hq % Hkv != 0
+    (dict(top_k=-1), B.SAS_ERR_INVALID_ARGUMENT),
+    (dict(batch=0), B.SAS_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), B.SAS_ERR_INVALID_ARGUMENT),
+    (dict(block_size=32), B.SAS_ERR_UNSUPPORTED),
+    (dict(head_dim=96), B.SAS_ERR_UNSUPPORTED),
+    (dict(sel_dim=32), B.SAS_ERR_UNSUPPORTED),
+    (dict(n_q_heads=48, n_kv_heads=8), B.SAS_ERR_UNSUPPORTED),   # G = 6
+    (dict(top_k=65), B.SAS_ERR_UNSUPPORTED),
+])
+def test_decode_rejects_bad_dims(lib, kw, status):
+    assert _decode(lib, _dims(**kw)) == status
+    assert lib.sas_last_error() != b""
+
+
+def test_decode_rejects_nulls_scale_and_small_workspace(lib):
+    assert _decode(lib, None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert b"dims" in lib.sas_last_error()
+    assert _decode(lib, _dims(), q=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert b"q is NULL" in lib.sas_last_error()
+    assert _decode(lib, _dims(), idx=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert _decode(lib, _dims(), scale=0.0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert _decode(lib, _dims(), scale=float("nan")) == B.SAS_ERR_INVALID_ARGUMENT
+    need = B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, _dims())
+    assert need > 0
+    assert _decode(lib, _dims(), ws_bytes=need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_prefill_and_bwd_validation(lib):
+    d = _dims()
+    pf = lambda dims, seq_len: lib.sas_prefill_fwd(ctypes.byref(dims), FAKE, FAKE, FAKE, seq_len,
+                                                   FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert pf(d, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert pf(d, 65537) == B.SAS_ERR_INVALID_ARGUMENT          # seq_len > t_max
+    assert pf(_dims(dtype=B.SAS_F32), 128) == B.SAS_ERR_UNSUPPORTED
+    bw = lambda dims, seq_len, dlg: lib.sas_bwd(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                FAKE, seq_len, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE,
+                                                dlg, FAKE, 1 << 40, None)
+    assert bw(d, 0, FAKE) == B.SAS_ERR_INVALID_ARGUMENT
+    assert bw(d, 128, None) == B.SAS_ERR_INVALID_ARGUMENT       # dlog_gate NULL with k > 0
+    assert bw(_dims(dtype=B.SAS_F32), 128, FAKE) == B.SAS_ERR_UNSUPPORTED
+
+
+def test_select_and_summaries_validation(lib):
+    d = _dims()
+    sel = lambda dims, mode, q_len, ws_bytes: lib.sas_select(
+        ctypes.byref(dims), mode, FAKE, q_len, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+        ws_bytes, None)
+    assert sel(d, 5, 0, 1 << 30) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sel(d, B.SAS_SELECT_TILES, 0, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sel(d, B.SAS_SELECT_TILES, 70000, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    need = B.sas_workspace_bytes(B.SAS_OP_SELECT_DECODE, d)
+    assert sel(d, B.SAS_SELECT_DECODE, 0, need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+    big = _dims(t_max=64 * 1025 * 64)
+    assert sel(big, B.SAS_SELECT_TILES, 64 * 1025, 0) == B.SAS_ERR_UNSUPPORTED
+    summ = lambda dims, b0, b1: lib.sas_block_summaries(ctypes.byref(dims), FAKE, FAKE, FAKE, b0,
+                                                        b1, FAKE, None)
+    assert summ(d, -1, 4) == B.SAS_ERR_INVALID_ARGUMENT
+    assert summ(d, 5, 4) == B.SAS_ERR_INVALID_ARGUMENT
+    assert summ(d, 7, 7) == B.SAS_OK                              # empty range: nothing to do
+
+
+def test_workspace_sizes(lib):
+    d = _dims()
+    assert B.sas_workspace_bytes(B.SAS_OP_SELECT_TILES, d, 16384) == 0
+    # decode: one partial (acc[d] + max + sum) per head and per unit (k slots + B0)
+    assert B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d) == 1 * 8 * 17 * 4 * 130 * 4
+    with pytest.raises(B.SasError):
+        B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, _dims(head_dim=96))
+    with pytest.raises(B.SasError):
+        B.sas_workspace_bytes(B.SAS_OP_PREFILL_FWD, d, 0)
