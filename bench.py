@@ -174,10 +174,11 @@ def run_decode(args, wl):
             sp2 = s2.cuda_stream
             a2 = [tuple(sp2 if x is sp else x for x in a) for a in (a_sum, a_sel, a_dec)]
             g.capture_begin()
-            lib.sas_block_summaries(*a2[0])
-            lib.sas_select(*a2[1])
-            lib.sas_decode_fwd(*a2[2])
+            sts = [lib.sas_block_summaries(*a2[0]), lib.sas_select(*a2[1]),
+                   lib.sas_decode_fwd(*a2[2])]
             g.capture_end()
+        if any(sts):
+            raise S.SasError(max(sts), lib.sas_last_error().decode())
         stream.wait_stream(s2)
         for _ in range(5):
             g.replay()

@@ -119,7 +119,8 @@ def sas_workspace_bytes(op: int, dims: SasDims, q_len: int = 0) -> int:
 def _workspace(op, dims, q_len, ws, device):
     need = sas_workspace_bytes(op, dims, q_len)
     if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        # zero-filled: the counters at the start of a workspace must start at 0
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -142,14 +143,17 @@ def sas_block_summaries(K, seq_lens, Wk_sel, blk_begin=0, blk_end=None, summ=Non
     return summ
 
 
-def sas_select(mode, Q, seq_lens, Wq_sel, summ, top_k, n_kv_heads=None, q_len=None,
+def sas_select(mode, Q, seq_lens, Wq_sel, summ, top_k, t_max=None, q_len=None,
                idx=None, log_gate=None, score_lse=None, scores=None, want_scores=False,
                ws=None):
     """Selector scores, gate and Top-K.  Returns (idx, log_gate, score_lse, scores|None).
 
-    mode SAS_SELECT_DECODE: Q is q [B,Hq,d]; SAS_SELECT_TILES: Q is [B,Hq,S,d]."""
+    mode SAS_SELECT_DECODE: Q is q [B,Hq,d]; SAS_SELECT_TILES: Q is [B,Hq,S,d].
+    t_max: K/V row capacity (default: the largest one whose summary buffer has
+    summ.shape[2] rows, so no sequence length that fits the buffer is clipped)."""
     B, Hkv, c_max, ds = summ.shape
-    t_max = c_max * BLOCK
+    if t_max is None:
+        t_max = c_max * BLOCK + BLOCK - 1
     Hq, d = Q.shape[1], Q.shape[-1]
     if mode == SAS_SELECT_TILES:
         q_len = Q.shape[2] if q_len is None else q_len

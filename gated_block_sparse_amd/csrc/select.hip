@@ -64,8 +64,10 @@ __device__ __forceinline__ void project_query(const float* __restrict__ Wq, cons
   }
 }
 
-// Scores of blocks [m0, m0 + n) of one (b, r) into sc[0..n): half a wave per
-// summary row, 16-byte loads, butterfly over the 32 lanes.
+// Scores of blocks [0, n) of one (b, r) (rows of summ_row0) into sc[0..n).
+// Each half wave owns 32 rows per round (rows hw + 8j, j < 32): all 32
+// 16-byte loads are issued before any arithmetic, then a transposed butterfly
+// (16+8+4+2+1 shuffles) leaves the full dot of row j in lane j.
 template <int DS>
 __device__ __forceinline__ void score_rows(const float* __restrict__ summ_row0, const float* qs,
                                            int n, float* sc) {
@@ -74,18 +76,41 @@ __device__ __forceinline__ void score_rows(const float* __restrict__ summ_row0, 
   float qv[PL];
 #pragma unroll
   for (int e = 0; e < PL; ++e) qv[e] = qs[l32 * PL + e];
-  for (int i = hw; i < n; i += kSelThreads / 32) {
-    const float* row = summ_row0 + static_cast<size_t>(i) * DS + l32 * PL;
-    float acc = 0.f;
+  for (int base = 0; base < n; base += 32 * (kSelThreads / 32)) {
+    float v[32];
     if constexpr (PL == 4) {
-      const float4 x = *reinterpret_cast<const float4*>(row);
-      acc = x.x * qv[0] + x.y * qv[1] + x.z * qv[2] + x.w * qv[3];
+      float4 x[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int i = base + hw + 8 * j;
+        x[j] = i < n ? *reinterpret_cast<const float4*>(summ_row0 + static_cast<size_t>(i) * DS + l32 * PL)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = x[j].x * qv[0] + x[j].y * qv[1] + x[j].z * qv[2] + x[j].w * qv[3];
     } else {
-      const float2 x = *reinterpret_cast<const float2*>(row);
-      acc = x.x * qv[0] + x.y * qv[1];
+      float2 x[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int i = base + hw + 8 * j;
+        x[j] = i < n ? *reinterpret_cast<const float2*>(summ_row0 + static_cast<size_t>(i) * DS + l32 * PL)
+                     : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = x[j].x * qv[0] + x[j].y * qv[1];
     }
-    for (int msk = 1; msk < 32; msk <<= 1) acc += __shfl_xor(acc, msk, 64);
-    if (l32 == 0) sc[i] = acc;
+#pragma unroll
+    for (int sft = 16; sft >= 1; sft >>= 1) {
+      const bool up = (l32 & sft) != 0;
+#pragma unroll
+      for (int j = 0; j < sft; ++j) {
+        const float keep = up ? v[j + sft] : v[j];
+        const float send = up ? v[j] : v[j + sft];
+        v[j] = keep + __shfl_xor(send, sft, 64);
+      }
+    }
+    const int i = base + hw + 8 * l32;
+    if (i < n) sc[i] = v[0];
   }
 }
 
@@ -107,88 +132,94 @@ __device__ __forceinline__ void write_selection(const uint64_t* keys, int kk, in
 }
 
 // ------------------------------------------------------------- decode ---
+// One launch per step: grid (chunk, group, sequence).  Every workgroup scores
+// its chunk, keeps the chunk's LSE state and its top-k keys in the workspace,
+// then bumps the row's arrival counter; the last workgroup of the row merges
+// the states and candidates in chunk order (so the result does not depend on
+// arrival order) and resets the counter to zero for the next call.
 template <typename T, int D, int DS, int G>
 __global__ void __launch_bounds__(kSelThreads)
-select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
-                           const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
-                           int t_max, int c_max, int k, int nchunk, float* __restrict__ scores,
-                           float2* __restrict__ part, uint64_t* __restrict__ cand) {
+select_decode_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                     const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
+                     int t_max, int c_max, int k, int kc, int nchunk, int npow,
+                     float* __restrict__ scores, unsigned* __restrict__ counters,
+                     float2* __restrict__ part, uint64_t* __restrict__ cand,
+                     int32_t* __restrict__ idx, float* __restrict__ log_gate,
+                     float* __restrict__ score_lse) {
   __shared__ float qm[D];
   __shared__ float qs[DS];
   __shared__ float sc[kSelChunk];
   __shared__ uint64_t keys[kSelChunk];
   __shared__ float red[kSelThreads / 64];
+  __shared__ int s_last;
+  extern __shared__ uint64_t mkeys[];
 
   const int b = blockIdx.z, r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
   const int m0 = chunk * kSelChunk;
-  const size_t p = (static_cast<size_t>(b) * Hkv + r) * nchunk + chunk;
-  if (m0 >= C) {
-    if (tid < k) cand[p * k + tid] = 0ull;
-    if (tid == 0) part[p] = make_float2(-INFINITY, 0.f);
+  const size_t row = static_cast<size_t>(b) * Hkv + r;
+  const size_t p = row * nchunk + chunk;
+  float M = -INFINITY, S = 0.f;
+  if (m0 < C) {
+    const int n = min(kSelChunk, C - m0);
+    if (tid < D) {
+      const T* qb = q + (row * G) * static_cast<size_t>(D) + tid;
+      float a = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) a += load_scalar<T>(qb + h * D);
+      qm[tid] = a / G;
+    }
+    __syncthreads();
+    project_query<D, DS>(Wq, qm, qs);
+    __syncthreads();
+    const float* srow = summ + row * static_cast<size_t>(c_max) * DS;
+    score_rows<DS>(srow + static_cast<size_t>(m0) * DS, qs, n, sc);
+    __syncthreads();
+    const bool valid = tid < n;
+    const float s = valid ? sc[tid] : -INFINITY;
+    if (scores && valid) scores[row * c_max + m0 + tid] = s;
+    M = block_max(s, red);
+    S = block_sum(valid ? expf(s - M) : 0.f, red);
+    keys[tid] = valid ? topk_key(s, m0 + tid) : 0ull;
+    bitonic_sort_desc(keys, kSelChunk);
+  }
+  const int kk = min(k, C);
+  if (nchunk == 1) {  // the row fits one chunk: finish here
+    const float lse = C > 0 ? M + logf(S) : -INFINITY;
+    write_selection(keys, kk, k, lse, idx + row * k, log_gate + row * k);
+    if (tid == 0) score_lse[row] = lse;
     return;
   }
-  const int n = min(kSelChunk, C - m0);
-
-  if (tid < D) {
-    const T* qb = q + (static_cast<size_t>(b) * Hkv * G + static_cast<size_t>(r) * G) * D + tid;
-    float a = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) a += load_scalar<T>(qb + h * D);
-    qm[tid] = a / G;
-  }
-  __syncthreads();
-  project_query<D, DS>(Wq, qm, qs);
-  __syncthreads();
-  const float* srow = summ + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(c_max) * DS;
-  score_rows<DS>(srow + static_cast<size_t>(m0) * DS, qs, n, sc);
-  __syncthreads();
-
-  const bool valid = tid < n;
-  const float s = valid ? sc[tid] : -INFINITY;
-  if (scores && valid)
-    scores[(static_cast<size_t>(b) * Hkv + r) * c_max + m0 + tid] = s;
-  const float M = block_max(s, red);
-  const float e = valid ? expf(s - M) : 0.f;
-  const float S = block_sum(e, red);
-  keys[tid] = valid ? topk_key(s, m0 + tid) : 0ull;
-  bitonic_sort_desc(keys, kSelChunk);
-  if (tid < k) cand[p * k + tid] = keys[tid];
+  if (tid < kc) cand[p * kc + tid] = (m0 < C) ? keys[tid] : 0ull;
   if (tid == 0) part[p] = make_float2(M, S);
-}
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(counters + row, 1u) == static_cast<unsigned>(nchunk - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
 
-__global__ void __launch_bounds__(kSelThreads)
-select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_max, int k,
-                           int nchunk, int npow, const float2* __restrict__ part,
-                           const uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
-                           float* __restrict__ log_gate, float* __restrict__ score_lse) {
-  extern __shared__ uint64_t mkeys[];
-  __shared__ float red[kSelThreads / 64];
-  const int b = blockIdx.y, r = blockIdx.x, tid = threadIdx.x;
-  const int len = clamp_len(seq_lens[b], t_max);
-  const int C = (len - 1) / kBlock;
-  const size_t row = static_cast<size_t>(b) * Hkv + r;
   const float2* pr = part + row * nchunk;
-
   float mloc = -INFINITY;
   for (int i = tid; i < nchunk; i += kSelThreads) mloc = fmaxf(mloc, pr[i].x);
-  const float M = block_max(mloc, red);
+  const float Mr = block_max(mloc, red);
   float sloc = 0.f;
   for (int i = tid; i < nchunk; i += kSelThreads) {
     const float2 v = pr[i];
-    if (v.x != -INFINITY) sloc += v.y * expf(v.x - M);
+    if (v.x != -INFINITY) sloc += v.y * expf(v.x - Mr);
   }
   const float L = block_sum(sloc, red);
-  const float lse = C > 0 ? M + logf(L) : -INFINITY;
-
-  const int ncand = nchunk * k;
-  const uint64_t* cr = cand + row * static_cast<size_t>(nchunk) * k;
+  const float lse = C > 0 ? Mr + logf(L) : -INFINITY;
+  const int ncand = nchunk * kc;
+  const uint64_t* cr = cand + row * static_cast<size_t>(nchunk) * kc;
   for (int i = tid; i < npow; i += kSelThreads) mkeys[i] = i < ncand ? cr[i] : 0ull;
   bitonic_sort_desc(mkeys, npow);
-  const int kk = min(k, C);
   write_selection(mkeys, kk, k, lse, idx + row * k, log_gate + row * k);
-  if (tid == 0) score_lse[row] = lse;
+  if (tid == 0) {
+    score_lse[row] = lse;
+    counters[row] = 0u;
+  }
 }
 
 static int decode_nchunk(const sas_dims& d) {
@@ -200,14 +231,14 @@ static int next_pow2(int n) {
   while (p < n) p <<= 1;
   return p;
 }
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// workspace: counters[rows] | part[rows*nchunk] | cand[rows*nchunk*max(k,1)]
 size_t select_decode_ws_bytes(const sas_dims& d) {
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
   const size_t nc = decode_nchunk(d);
-  size_t bytes = rows * nc * sizeof(float2);
-  bytes = (bytes + 255) & ~size_t(255);
-  bytes += rows * nc * static_cast<size_t>(d.top_k > 0 ? d.top_k : 1) * sizeof(uint64_t);
-  return bytes;
+  return align256(rows * sizeof(unsigned)) + align256(rows * nc * sizeof(float2)) +
+         rows * nc * static_cast<size_t>(d.top_k > 0 ? d.top_k : 1) * sizeof(uint64_t);
 }
 
 template <typename T, int D, int DS, int G>
@@ -217,25 +248,21 @@ static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq
   const int nchunk = decode_nchunk(d);
   const int k = d.top_k;
   const int kc = k > 0 ? k : 1;
-  const int npow = next_pow2(nchunk * kc);
+  const int npow = nchunk > 1 ? next_pow2(nchunk * kc) : 0;
   if (npow > 8192)
-    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge sort", nchunk * kc);
+    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge sort",
+                nchunk * kc);
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
-  float2* part = static_cast<float2*>(ws);
-  size_t off = (rows * nchunk * sizeof(float2) + 255) & ~size_t(255);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + off);
-  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G>),
-                     dim3(nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,
-                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,
-                     d.t_max / kBlock, kc, nchunk, scores, part, cand);
-  {
-    sas_status s = check_launch("select_decode_chunk");
-    if (s != SAS_OK) return s;
-  }
-  hipLaunchKernelGGL(select_decode_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kSelThreads),
-                     npow * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max, k, nchunk,
-                     npow, part, cand, idx, log_gate, score_lse);
-  return check_launch("select_decode_merge");
+  char* w = static_cast<char*>(ws);
+  unsigned* counters = reinterpret_cast<unsigned*>(w);
+  float2* part = reinterpret_cast<float2*>(w + align256(rows * sizeof(unsigned)));
+  uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(rows * sizeof(unsigned)) +
+                                               align256(rows * nchunk * sizeof(float2)));
+  hipLaunchKernelGGL((select_decode_kernel<T, D, DS, G>), dim3(nchunk, d.n_kv_heads, d.batch),
+                     dim3(kSelThreads), npow * sizeof(uint64_t), st, static_cast<const T*>(q),
+                     seq_lens, Wq, summ, d.n_kv_heads, d.t_max, d.t_max / kBlock, k, kc, nchunk,
+                     npow, scores, counters, part, cand, idx, log_gate, score_lse);
+  return check_launch("select_decode");
 }
 
 // -------------------------------------------------------------- tiles ---

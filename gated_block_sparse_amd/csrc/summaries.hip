@@ -8,7 +8,9 @@
 // streams whole 64-token blocks with 16-byte loads (a row is LPR lanes, so a
 // load instruction covers 64/LPR full rows, fully coalesced), sums its rows
 // in registers and finishes the column sums with a butterfly inside the wave.
-// The block means then meet Wk_sel^T, staged once per workgroup in LDS.
+// For the projection each thread keeps a slice of one row of Wk_sel in
+// registers (loaded while the key loads are in flight) and SPLIT adjacent
+// lanes combine their slices of one output with a butterfly.
 #include "sas_device.h"
 #include "sas_internal.h"
 
@@ -26,7 +28,8 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   constexpr int LPR = D / EPL;              // lanes per K row
   constexpr int RPI = 64 / LPR;             // rows per load instruction (per wave)
   constexpr int NI = kBlock / RPI;          // load instructions per block
-  __shared__ float Wt[D][DS];               // Wk_sel transposed: Wt[c][j] = Wk[j][c]
+  constexpr int SPLIT = kSumThreads / DS;   // lanes per output channel
+  constexpr int CW = D / SPLIT;             // input channels per lane
   __shared__ float mean[kSumBlocks][D];
 
   const int b = blockIdx.z, r = blockIdx.y;
@@ -38,14 +41,18 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   const int nblk = last - first;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // stage Wk^T
-  for (int e = tid * 4; e < D * DS; e += kSumThreads * 4) {
-    const int j = e / D, c = e % D;
-    const float4 w = *reinterpret_cast<const float4*>(Wk + e);
-    Wt[c + 0][j] = w.x;
-    Wt[c + 1][j] = w.y;
-    Wt[c + 2][j] = w.z;
-    Wt[c + 3][j] = w.w;
+  const int j = tid / SPLIT, part = tid % SPLIT;
+  float w[CW];
+  {
+    const float4* wr = reinterpret_cast<const float4*>(Wk + static_cast<size_t>(j) * D + part * CW);
+#pragma unroll
+    for (int c4 = 0; c4 < CW / 4; ++c4) {
+      const float4 x = wr[c4];
+      w[4 * c4 + 0] = x.x;
+      w[4 * c4 + 1] = x.y;
+      w[4 * c4 + 2] = x.z;
+      w[4 * c4 + 3] = x.w;
+    }
   }
 
   const T* Kr = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
@@ -75,23 +82,13 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   }
   __syncthreads();
 
-  // projection: thread -> output channel j, blocks jb0, jb0 + step, ...
-  constexpr int STEP = kSumThreads / DS;
-  constexpr int PER = kSumBlocks / STEP;
-  const int j = tid % DS, jb0 = tid / DS;
-  float out[PER];
-#pragma unroll
-  for (int p = 0; p < PER; ++p) out[p] = 0.f;
-  for (int c = 0; c < D; ++c) {
-    const float w = Wt[c][j];
-#pragma unroll
-    for (int p = 0; p < PER; ++p) out[p] += w * mean[jb0 + p * STEP][c];
-  }
   float* dst = summ + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(c_max) * DS;
+  for (int jb = 0; jb < nblk; ++jb) {
+    float a = 0.f;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    const int jb = jb0 + p * STEP;
-    if (jb < nblk) dst[static_cast<size_t>(first + jb) * DS + j] = out[p];
+    for (int c = 0; c < CW; ++c) a += w[c] * mean[jb][part * CW + c];
+    a = group_sum(a, SPLIT);
+    if (part == 0) dst[static_cast<size_t>(first + jb) * DS + j] = a;
   }
 }
 

@@ -33,12 +33,18 @@
  *  - Ownership: the caller allocates and owns every buffer, including the
  *    workspace sized by sas_workspace_bytes().  The library allocates and
  *    frees nothing and keeps no pointer after a call returns.
+ *  - Workspaces of sas_select (DECODE mode) and sas_decode_fwd begin with one
+ *    32-bit arrival counter per (sequence, group): they must be zero before
+ *    the first call that uses the workspace, and every call leaves them zero
+ *    again (so zero-fill a new workspace once).  Calls that share one
+ *    workspace must not run concurrently.
  *  - Execution: each call validates its arguments on the host, then enqueues
  *    kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
  *    The caller synchronises.  Results are bitwise deterministic.
- *  - Errors: on any non-OK status nothing has been enqueued by that call's
- *    validation failure and the outputs are untouched (SAS_ERR_HIP: a launch
- *    failed after validation; sas_last_error() has the text).
+ *  - Errors: a call that returns SAS_ERR_INVALID_ARGUMENT, SAS_ERR_UNSUPPORTED
+ *    or SAS_ERR_WORKSPACE_TOO_SMALL has enqueued nothing and left every
+ *    output untouched.  SAS_ERR_HIP means a launch failed after validation;
+ *    sas_last_error() has the text.
  *  - Device-side contents are trusted: seq_lens must lie in [1, t_max] (the
  *    kernels clamp them into that range); idx entries must be -1 or a valid
  *    history block of their row.  Inputs must be finite.

@@ -114,18 +114,22 @@ def decode_scores(q: np.ndarray, Wq_sel: np.ndarray, summ: np.ndarray, G: int) -
 
 
 def tile_scores(Q: np.ndarray, S: int, Wq_sel: np.ndarray, summ: np.ndarray, G: int,
-                b: int = BLOCK) -> List[np.ndarray]:
+                b: int = BLOCK, tiles=None) -> List[np.ndarray]:
     """Per-tile, per-group scores in prefill.  Q: [Hq, >=S, d]; summ: [Hkv, >=n_tiles-1, d_sel].
 
     Returns a list over tiles t of arrays [Hkv, t]: the score of history block
     m < t is the mean over the group's heads and the tile's queries of
-    (Wq_sel q_{h,i}) . summ_m / sqrt(d_sel).
+    (Wq_sel q_{h,i}) . summ_m / sqrt(d_sel).  With ``tiles`` only those tiles
+    are computed (the others are None).
     """
     d_sel = Wq_sel.shape[0]
     Hkv = summ.shape[0]
     n_tiles = -(-S // b)
     out = []
     for t in range(n_tiles):
+        if tiles is not None and t not in tiles:
+            out.append(None)
+            continue
         i0, i1 = b * t, min(b * t + b, S)
         s = np.zeros((Hkv, t))
         for r in range(Hkv):
@@ -254,17 +258,18 @@ def _tile_logits(Qt, K, r, t, S, idx_row, lg_row, scale, b, gated):
 
 def prefill_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, S: int, idx: np.ndarray,
                    log_gate: np.ndarray, scale: float, G: int, b: int = BLOCK,
-                   gated: bool = True):
+                   gated: bool = True, tiles=None):
     """Causal gated block-sparse attention of one sequence, one selection per tile.
 
     Q: [Hq, >=S, d]; K, V: [Hkv, >=S, d]; idx, log_gate: [Hkv, n_tiles, k].
-    Returns O [Hq, S, d] and lse [Hq, S].
+    Returns O [Hq, S, d] and lse [Hq, S] (with ``tiles``, only the queries of
+    those tiles are filled in).
     """
     Hq, _, d = Q.shape
     O = np.zeros((Hq, S, d))
     lse = np.zeros((Hq, S))
     n_tiles = -(-S // b)
-    for t in range(n_tiles):
+    for t in (range(n_tiles) if tiles is None else tiles):
         i0, i1 = b * t, min(b * t + b, S)
         for h in range(Hq):
             r = h // G
@@ -283,11 +288,13 @@ def prefill_attend(Q: np.ndarray, K: np.ndarray, V: np.ndarray, S: int, idx: np.
 # --------------------------------------------------------------------------
 def prefill_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, S: int,
                      idx: np.ndarray, log_gate: np.ndarray, scale: float, G: int,
-                     b: int = BLOCK):
+                     b: int = BLOCK, tiles=None):
     """Gradients of L = <dO, O> for prefill_attend (gated).
 
     Returns dQ [Hq,S,d], dK [Hkv,S,d], dV [Hkv,S,d], dlog_gate [Hkv, n_tiles, k]
     (zero on empty slots).  The log-gate is treated as an independent input.
+    With ``tiles``, only the terms of those query tiles are accumulated (so
+    dQ/dlog_gate are exact on those tiles and dK/dV hold their contribution).
     """
     Hq, _, d = Q.shape
     Hkv = K.shape[0]
@@ -297,7 +304,7 @@ def prefill_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray
     dK = np.zeros((Hkv, S, d))
     dV = np.zeros((Hkv, S, d))
     dlg = np.zeros((Hkv, n_tiles, k))
-    for t in range(n_tiles):
+    for t in (range(n_tiles) if tiles is None else tiles):
         i0, i1 = b * t, min(b * t + b, S)
         for h in range(Hq):
             r = h // G

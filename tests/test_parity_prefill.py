@@ -1,0 +1,128 @@
+"""GPU parity of the prefill path against the CPU oracle, through the C ABI:
+sas_block_summaries -> sas_select(TILES) -> sas_prefill_fwd (-> sas_bwd).
+
+Small shapes are checked on every tile; the full training-style workload
+(S=16384, Qwen3-4B head shape, per-tile k=16) is checked on sampled tiles
+(first, last, around the k boundary and in the middle).  The attention stage
+gets a selection that does not come from the GPU: the oracle's own Top-K on
+small shapes, a seeded random valid selection at full size."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_amd import synth
+from oracle import sas_oracle as O
+from tests.gpu_util import (TOL_OUT, check_selection_row, dev, host, idx_dev, lg_dev, log,
+                            needs_gpu, rel_l2)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+TOL_LSE = 1e-3
+
+
+def _sas():
+    from gated_block_sparse_amd import binding
+    return binding
+
+
+def _problem(S, Hq=4, Hkv=1, d=128, ds=128, k=4, seed=0):
+    wl = synth.custom_workload("prefill", n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, sel_dim=ds,
+                               top_k=k, dtype="bf16", seq_len=S)
+    return synth.make_problem(wl, seed)
+
+
+def random_selection(rng, Hkv, n_tiles, k):
+    """A seeded valid per-tile selection (ascending, -1 padded) with log g < 0."""
+    idx = np.full((Hkv, n_tiles, k), -1, np.int64)
+    lg = np.full((Hkv, n_tiles, k), -np.inf)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            n = min(k, t)
+            if n:
+                ch = np.sort(rng.choice(t, size=n, replace=False))
+                idx[r, t, :n] = ch
+                lg[r, t, :n] = -rng.uniform(0.5, 8.0, size=n)
+    return idx, lg
+
+
+def check_select_tiles(p, summ_g, tiles):
+    """GPU per-tile selection vs the oracle on the given tiles."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hkv, G, k = int(p.seq_lens[0]), wl.n_kv_heads, wl.group, wl.top_k
+    Q = dev(p.q)
+    idx_g, lg_g, slse_g, sc_g = S_.sas_select(S_.SAS_SELECT_TILES, Q, None, dev(p.Wq_sel), summ_g, k,
+                                              t_max=p.K.shape[2], want_scores=True)
+    idx_h, lg_h, slse_h, sc_h = idx_g.cpu().numpy(), host(lg_g), host(slse_g), host(sc_g)
+    Qf, Kf = synth.to_f64(p.q[0], "bf16"), synth.to_f64(p.K[0], "bf16")
+    summ = O.block_summaries(Kf, S, p.f64("Wk_sel"))
+    rows = O.tile_scores(Qf, S, p.f64("Wq_sel"), summ, G, tiles=set(tiles))
+    n_exact = 0
+    for t in tiles:
+        for r in range(Hkv):
+            s = rows[t][r]
+            lse_r, _ = O.gate(s)
+            oidx, gap = O.topk(s, k)
+            if t:
+                assert np.abs(sc_h[0, r, t, :t] - s).max() <= 1e-4
+                assert abs(slse_h[0, r, t] - lse_r) <= 1e-4
+            else:
+                assert np.isneginf(slse_h[0, r, t])
+            n_exact += check_selection_row(idx_h[0, r, t], lg_h[0, r, t], s,
+                                           np.asarray(oidx + [-1] * (k - len(oidx))), gap, k,
+                                           lse_r, 1e-4)
+    return idx_g, lg_g, n_exact
+
+
+def run_prefill_case(p, tiles=None, selection="oracle", gated=True, label=""):
+    S_ = _sas()
+    wl = p.wl
+    S, Hq, Hkv, d, k, G = int(p.seq_lens[0]), wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_k, wl.group
+    n_tiles = -(-S // 64)
+    tiles = list(range(n_tiles)) if tiles is None else tiles
+    log(f"[prefill {label}] S={S} Hq={Hq} Hkv={Hkv} d={d} k={k} tiles={tiles[:6]}...")
+    Q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    lens = torch.tensor([S], dtype=torch.int32).cuda()
+    summ_g = S_.sas_block_summaries(K, lens, dev(p.Wk_sel))
+    idx_g, lg_g, n_exact = check_select_tiles(p, summ_g, tiles)
+    log(f"[prefill {label}] tile selection exact on {n_exact}/{len(tiles) * Hkv} rows")
+
+    Qf, Kf, Vf = (synth.to_f64(x[0], "bf16") for x in (p.q, p.K, p.V))
+    if selection == "oracle":
+        sel = O.prefill_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        idx, lg = sel["idx"], sel["log_gate"]
+    else:
+        idx, lg = random_selection(np.random.default_rng(1234), Hkv, n_tiles, k)
+    scale = 1.0 / math.sqrt(d)
+    O_g, lse_g = S_.sas_prefill_fwd(Q, K, V, idx_dev(idx[None]), lg_dev(lg[None]) if gated else None)
+    Or, lser = O.prefill_attend(Qf, Kf, Vf, S, idx, lg, scale, G, gated=gated, tiles=tiles)
+    O_h, lse_h = host(O_g)[0], host(lse_g)[0]
+    rows = np.concatenate([np.arange(64 * t, min(64 * t + 64, S)) for t in tiles])
+    err_o = np.abs(O_h[:, rows] - Or[:, rows]).max()
+    err_l = np.abs(lse_h[:, rows] - lser[:, rows]).max()
+    log(f"[prefill {label}] max|O-O_ref|={err_o:.3g} max|lse-lse_ref|={err_l:.3g}")
+    assert err_o <= TOL_OUT["bf16"], err_o
+    assert err_l <= TOL_LSE, err_l
+    return dict(Q=Q, K=K, V=V, O=O_g, lse=lse_g, idx=idx, lg=lg, Qf=Qf, Kf=Kf, Vf=Vf, rows=rows,
+                tiles=tiles)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,k", [
+    (64, 4, 1, 128, 4), (100, 4, 1, 128, 4), (1000, 8, 2, 128, 3), (2048, 8, 2, 128, 16),
+    (777, 2, 2, 64, 5), (640, 8, 1, 128, 4), (700, 16, 2, 64, 6), (1, 4, 1, 128, 2),
+])
+def test_prefill_small(S, Hq, Hkv, d, k):
+    run_prefill_case(_problem(S, Hq, Hkv, d, 128, k, seed=S + Hq), label=f"S={S}")
+
+
+def test_prefill_ungated_and_k0():
+    run_prefill_case(_problem(500, 8, 2, 128, 128, 4, seed=3), gated=False, label="ungated")
+    run_prefill_case(_problem(333, 8, 2, 128, 128, 0, seed=4), label="k=0")
+
+
+@pytest.mark.timeout(900)
+def test_prefill_full_workload_sampled_tiles():
+    p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
+    run_prefill_case(p, tiles=[0, 1, 2, 15, 16, 17, 100, 200, 254, 255], selection="random",
+                     label="qwen3_4b_prefill_16k")
