@@ -232,6 +232,145 @@ def run_decode(args, wl):
     return res, p
 
 
+# --------------------------------------------------------------------------
+# prefill (training-style forward + backward)
+# --------------------------------------------------------------------------
+def prefill_pairs(S, G_heads, idx_h):
+    """Causally visible selected (query, key) pairs summed over query heads."""
+    Hkv = idx_h.shape[1]
+    Hq_per = G_heads
+    total = 0
+    n_tiles = -(-S // 64)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            nq = min(64, S - 64 * t)
+            nsel = int((idx_h[0, r, t] >= 0).sum())
+            total += Hq_per * (nsel * 64 * nq + nq * (nq + 1) // 2)
+    return total
+
+
+def run_prefill(args, wl):
+    import torch
+    from gated_block_sparse_amd import binding as Sb
+    from gated_block_sparse_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    p = synth.make_problem(wl, seed=0)
+    B, Hq, Hkv, d, ds, k = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.sel_dim, wl.top_k
+    S = int(p.seq_lens[0])
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    Q, K, V, dO = up(p.q), up(p.K), up(p.V), up(p.dO)
+    Wq, Wk = up(p.Wq_sel), up(p.Wk_sel)
+    lens = torch.tensor([S], dtype=torch.int32, device=dev)
+    summ = Sb.sas_block_summaries(K, lens, Wk)
+    idx, lg, slse, _ = Sb.sas_select(Sb.SAS_SELECT_TILES, Q, None, Wq, summ, k, t_max=S)
+    O, lse = Sb.sas_prefill_fwd(Q, K, V, idx, lg)
+    dQ, dK, dV, dlg = Sb.sas_bwd(Q, K, V, O, dO, lse, idx, lg)
+    torch.cuda.synchronize()
+    pairs = prefill_pairs(S, Hq // Hkv, idx.cpu().numpy())
+    fwd_flop = 4.0 * d * pairs
+    bwd_flop = 10.0 * d * pairs
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    dims = Sb.make_dims(B, Hq, Hkv, d, ds, k, S, Sb.SAS_BF16)
+    ws_sel = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_SELECT_TILES, dims, S)), dtype=torch.uint8, device=dev)
+    ws_fwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_PREFILL_FWD, dims, S)), dtype=torch.uint8, device=dev)
+    ws_bwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_BWD, dims, S)), dtype=torch.uint8, device=dev)
+
+    def step(evs=None):
+        rec = (lambda i: evs[i].record(stream)) if evs else (lambda i: None)
+        rec(0)
+        Sb.sas_block_summaries(K, lens, Wk, summ=summ)
+        Sb.sas_select(Sb.SAS_SELECT_TILES, Q, None, Wq, summ, k, t_max=S, idx=idx, log_gate=lg,
+                      score_lse=slse, ws=ws_sel)
+        rec(1)
+        Sb.sas_prefill_fwd(Q, K, V, idx, lg, O=O, lse=lse, ws=ws_fwd)
+        rec(2)
+        Sb.sas_bwd(Q, K, V, O, dO, lse, idx, lg, dQ=dQ, dK=dK, dV=dV, dlog_gate=dlg, ws=ws_bwd)
+        rec(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    t0 = time.perf_counter()
+    for i in range(n):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_sel = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    t_fwd = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    t_bwd = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
+    tot = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    med = statistics.median
+    us_fwd, us_bwd, us_step = med(t_fwd), med(t_bwd), med(tot)
+    fwd_tf = fwd_flop / (us_fwd * 1e-6) / 1e12
+    bwd_tf = bwd_flop / (us_bwd * 1e-6) / 1e12
+    res = {
+        "metric": "SAS prefill fwd+bwd us/step + achieved bf16 MFMA TFLOP/s (% peak), Qwen3-4B shape, S=16384",
+        "value": round(us_step, 1),
+        "unit": "us/step",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V/dO, random selector weights)",
+        "config": {"workload": wl.name, "batch": B, "seq_len": S, "n_q_heads": Hq,
+                   "n_kv_heads": Hkv, "head_dim": d, "sel_dim": ds, "block": 64, "top_k": k,
+                   "cache": "hot" if args.no_flush else "cold (MALL+L2 flushed)"},
+        "tokens_per_s": round(B * S / (us_step * 1e-6), 1),
+        "breakdown_us": {
+            "summaries_and_select": round(med(t_sel), 2),
+            "prefill_fwd": {"median": round(us_fwd, 2), "p10": round(_pct(t_fwd, .1), 2), "p90": round(_pct(t_fwd, .9), 2)},
+            "bwd": {"median": round(us_bwd, 2), "p10": round(_pct(t_bwd, .1), 2), "p90": round(_pct(t_bwd, .9), 2)},
+        },
+        "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
+        "bwd_TFLOPs": round(bwd_tf, 1),
+        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel (sas_prefill_fwd)",
+                     "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "wall_s_timed_region": round(wall, 3),
+    }
+    return res, p
+
+
+def cpu_baseline_prefill(p, budget_s):
+    """The float64 oracle forward on a sample of tiles, scaled to one full forward."""
+    from oracle import sas_oracle as O
+    from gated_block_sparse_amd import synth
+    wl = p.wl
+    S = int(p.seq_lens[0])
+    G = wl.n_q_heads // wl.n_kv_heads
+    n_tiles = -(-S // 64)
+    Qf, Kf, Vf = (synth.to_f64(x[0], wl.dtype) for x in (p.q, p.K, p.V))
+    rng = np.random.default_rng(0)
+    idx = np.full((wl.n_kv_heads, n_tiles, wl.top_k), -1, np.int64)
+    lg = np.full(idx.shape, -np.inf)
+    for r in range(wl.n_kv_heads):
+        for t in range(n_tiles):
+            c = min(wl.top_k, t)
+            if c:
+                idx[r, t, :c] = np.sort(rng.choice(t, size=c, replace=False))
+                lg[r, t, :c] = -2.0
+    done = 0
+    t0 = time.perf_counter()
+    tiles = list(range(n_tiles - 1, -1, -1))   # full tiles first
+    while time.perf_counter() - t0 < budget_s and done < n_tiles:
+        O.prefill_attend(Qf, Kf, Vf, S, idx, lg, 1.0 / math.sqrt(wl.head_dim), G, tiles=[tiles[done]])
+        done += 1
+    el = time.perf_counter() - t0
+    return el / done * n_tiles * 1e6, done, n_tiles
+
+
 def cpu_baseline_decode(p, budget_s):
     """The float64 oracle on the same decode step, repeated for ~budget_s."""
     from oracle import sas_oracle as O
@@ -288,7 +427,17 @@ def main():
     from gated_block_sparse_amd import synth
     wl = synth.WORKLOADS[args.workload]
     if wl.mode != "decode":
-        raise SystemExit("prefill benchmark not available yet")
+        res, p = run_prefill(args, wl)
+        if not args.no_cpu_baseline:
+            us, done, n_tiles = cpu_baseline_prefill(p, args.cpu_seconds)
+            res["cpu_baseline"] = {
+                "value": round(us, 1), "unit": "us per prefill forward", "cores": blas_threads(),
+                "kind": "oracle",
+                "sample": f"oracle forward on {done} of {n_tiles} query tiles (all heads), "
+                          f"scaled to the full sequence; float64 NumPy",
+            }
+        print(json.dumps(res))
+        return
     res, p = run_decode(args, wl)
     if args.calibrate_copy:
         import torch

@@ -20,19 +20,9 @@
 //  * the log-gate is added per block; the diagonal block is masked j > i.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "sas_mfma.h"
 
 namespace sas {
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-
-constexpr float kLog2eF = 1.4426950408889634f;
-constexpr float kLn2F = 0.6931471805599453f;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
-__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 template <int D, int HPW>
 __global__ void __launch_bounds__(128 * HPW)
@@ -90,27 +80,8 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
     const int tok0 = blk * 64;
     __syncthreads();  // the previous block's LDS reads are done
-    for (int c = tid; c < 64 * (D / 8); c += NT) {
-      const int row = c / (D / 8), cc = c % (D / 8);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (tok0 + row < S) u = *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(tok0 + row) * D + cc * 8);
-      *reinterpret_cast<uint4*>(&Ks[row * KSTR + cc * 8]) = u;
-    }
-    for (int p = tid; p < 32 * (D / 8); p += NT) {
-      const int tp = p % 32, cc = p / 32;
-      const int r0 = tok0 + 2 * tp;
-      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-      if (r0 < S) u0 = *reinterpret_cast<const uint4*>(Vg + static_cast<size_t>(r0) * D + cc * 8);
-      if (r0 + 1 < S) u1 = *reinterpret_cast<const uint4*>(Vg + static_cast<size_t>(r0 + 1) * D + cc * 8);
-      const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
-      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (w0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t c1 = (w1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&Vt[(cc * 8 + e) * VSTR + 2 * tp]) = a | (c1 << 16);
-      }
-    }
+    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, nullptr, tid);
+    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, nullptr, Vt, tid);
     __syncthreads();
 
     // S^T (64 tokens x 32 queries) = K Q^T
@@ -157,38 +128,18 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
 
-    // P^T operands: k-step j covers tokens 16j..16j+15 in accumulator order
-    bf16x8_t pb[4];
+    // O^T (D channels x 32 queries) += V^T P^T, k-step j = tokens 16j..16j+15
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t pb = acc_to_bop(s, j);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[j][e] = static_cast<__bf16>(s[j >> 1][8 * (j & 1) + e]);
-    // O^T (D channels x 32 queries) += V^T P^T
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const uint16_t* vrow = &Vt[(32 * ct + l32) * VSTR + 4 * hi];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + 16 * j);
-        const uint2 up = *reinterpret_cast<const uint2*>(vrow + 16 * j + 8);
-        acc[ct] = mfma32x32x16(as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y)), pb[j], acc[ct]);
-      }
+      for (int ct = 0; ct < CT; ++ct)
+        acc[ct] = mfma32x32x16(lds_aop_perm(&Vt[(32 * ct + l32) * VSTR], j, hi), pb, acc[ct]);
     }
   }
 
   if (qvalid) {
-    const float inv = 1.f / l_run;
-    uint16_t* orow = O + ((static_cast<size_t>(b) * Hq + h) * S + qi) * D;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int c0 = 32 * ct + 8 * grp + 4 * hi;
-        uint2 pk;
-        pk.x = f32_to_bf16(acc[ct][4 * grp + 0] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[ct][4 * grp + 1] * inv)) << 16);
-        pk.y = f32_to_bf16(acc[ct][4 * grp + 2] * inv) | (static_cast<uint32_t>(f32_to_bf16(acc[ct][4 * grp + 3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(orow + c0) = pk;
-      }
+    store_acc_col<CT>(acc, 1.f / l_run, O + ((static_cast<size_t>(b) * Hq + h) * S + qi) * D, hi);
     if (hi == 0) lse[(static_cast<size_t>(b) * Hq + h) * S + qi] = (m_run + log2f(l_run)) * kLn2F;
   }
 }

@@ -14,8 +14,8 @@ import torch
 
 from gated_block_sparse_amd import synth
 from oracle import sas_oracle as O
-from tests.gpu_util import (TOL_OUT, check_selection_row, dev, host, idx_dev, lg_dev, log,
-                            needs_gpu, rel_l2)
+from tests.gpu_util import (TOL_GRAD_REL, TOL_OUT, check_selection_row, dev, host, idx_dev,
+                            lg_dev, log, needs_gpu)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 TOL_LSE = 1e-3
@@ -126,3 +126,88 @@ def test_prefill_full_workload_sampled_tiles():
     p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
     run_prefill_case(p, tiles=[0, 1, 2, 15, 16, 17, 100, 200, 254, 255], selection="random",
                      label="qwen3_4b_prefill_16k")
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def run_bwd_case(p, ctx, exact_blocks=None, label=""):
+    """sas_bwd on the forward's outputs vs prefill_backward of the oracle.
+
+    ctx: what run_prefill_case returned.  With sampled tiles, dQ and dlog_gate
+    are compared on those tiles and dK/dV on `exact_blocks` (blocks whose every
+    reader is a sampled tile); otherwise everything is compared."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hq, Hkv, d, k, G = int(p.seq_lens[0]), wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_k, wl.group
+    n_tiles = -(-S // 64)
+    idx, lg, tiles = ctx["idx"], ctx["lg"], ctx["tiles"]
+    full = len(tiles) == n_tiles
+    dO = dev(p.dO)
+    dQ, dK, dV, dlg = S_.sas_bwd(ctx["Q"], ctx["K"], ctx["V"], ctx["O"], dO, ctx["lse"],
+                                 idx_dev(idx[None]), lg_dev(lg[None]))
+    dOf = synth.to_f64(p.dO[0], "bf16")
+    scale = 1.0 / math.sqrt(d)
+    rQ, rK, rV, rlg = O.prefill_backward(ctx["Qf"], ctx["Kf"], ctx["Vf"], dOf, S, idx, lg, scale,
+                                         G, tiles=None if full else tiles)
+    gQ, gK, gV, glg = host(dQ)[0], host(dK)[0][:, :S], host(dV)[0][:, :S], host(dlg)[0]
+    rows = ctx["rows"]
+    # relative L2 per tensor; the floor keeps an exactly-zero reference (one
+    # query and one key: dQ = dK = 0) from dividing by zero
+    floor = 1e-2 * np.linalg.norm(dOf[:, rows])
+
+    def rel_l2(x, ref):
+        return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), floor))
+
+    e_q = rel_l2(gQ[:, rows], rQ[:, rows])
+    sel = np.zeros_like(idx, bool)
+    sel[:, tiles] = True
+    valid = (idx >= 0) & sel
+    e_lg = rel_l2(glg[valid], rlg[valid]) if valid.any() else 0.0
+    assert (glg[idx < 0] == 0).all()
+    if full:
+        kv_rows = np.arange(S)
+    else:
+        kv_rows = np.concatenate([np.arange(64 * m, min(64 * m + 64, S)) for m in exact_blocks])
+    e_k = rel_l2(gK[:, kv_rows], rK[:, kv_rows])
+    e_v = rel_l2(gV[:, kv_rows], rV[:, kv_rows])
+    log(f"[bwd {label}] rel dQ={e_q:.3g} dK={e_k:.3g} dV={e_v:.3g} dlog_gate={e_lg:.3g}")
+    assert max(e_q, e_k, e_v, e_lg) <= TOL_GRAD_REL
+    # identities that hold at any size: sum_j dV_j = sum over the group's rows of dO,
+    # sum_j dK_j = 0 (a shift of every key leaves each softmax row unchanged)
+    for r in range(Hkv):
+        sv = gV[r].sum(axis=0)
+        so = dOf[r * G:(r + 1) * G].sum(axis=(0, 1))
+        assert np.linalg.norm(sv - so) <= TOL_GRAD_REL * max(np.linalg.norm(so), floor)
+        assert np.linalg.norm(gK[r].sum(axis=0)) <= TOL_GRAD_REL * np.linalg.norm(gK[r]) + 1e-3
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,k", [
+    (64, 4, 1, 128, 4), (100, 4, 1, 128, 4), (1000, 8, 2, 128, 3), (2048, 8, 2, 128, 16),
+    (777, 2, 2, 64, 5), (700, 16, 2, 64, 6), (1, 4, 1, 128, 2), (333, 8, 2, 128, 0),
+])
+def test_bwd_small(S, Hq, Hkv, d, k):
+    p = _problem(S, Hq, Hkv, d, 128, k, seed=S + 7 * Hq)
+    ctx = run_prefill_case(p, label=f"S={S}")
+    run_bwd_case(p, ctx, label=f"S={S}")
+
+
+@pytest.mark.timeout(900)
+def test_bwd_full_workload_sampled_tiles():
+    p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
+    ctx = run_prefill_case(p, tiles=[0, 1, 2, 15, 16, 17, 100, 200, 253, 254, 255],
+                           selection="random", label="qwen3_4b_prefill_16k")
+    run_bwd_case(p, ctx, exact_blocks=[253, 254, 255], label="qwen3_4b_prefill_16k")
+
+
+def test_bwd_deterministic():
+    S_ = _sas()
+    p = _problem(1500, 8, 2, 128, 128, 6, seed=11)
+    ctx = run_prefill_case(p, label="det")
+    outs = []
+    for _ in range(2):
+        r = S_.sas_bwd(ctx["Q"], ctx["K"], ctx["V"], ctx["O"], dev(p.dO), ctx["lse"],
+                       idx_dev(ctx["idx"][None]), lg_dev(ctx["lg"][None]))
+        outs.append([x.clone() for x in r])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
