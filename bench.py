@@ -172,7 +172,7 @@ def run_decode(args, wl):
         s2.wait_stream(stream)
         with torch.cuda.stream(s2):
             sp2 = s2.cuda_stream
-            a2 = [tuple(sp2 if x is sp else x for x in a) for a in (a_sum, a_sel, a_dec)]
+            a2 = [a[:-1] + (sp2,) for a in (a_sum, a_sel, a_dec)]   # the stream is the last argument
             g.capture_begin()
             sts = [lib.sas_block_summaries(*a2[0]), lib.sas_select(*a2[1]),
                    lib.sas_decode_fwd(*a2[2])]

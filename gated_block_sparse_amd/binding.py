@@ -119,8 +119,7 @@ def sas_workspace_bytes(op: int, dims: SasDims, q_len: int = 0) -> int:
 def _workspace(op, dims, q_len, ws, device):
     need = sas_workspace_bytes(op, dims, q_len)
     if ws is None:
-        # zero-filled: the counters at the start of a workspace must start at 0
-        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
 
 

@@ -10,12 +10,11 @@
 // and V once (16-byte loads, every load instruction covers whole 256-byte
 // rows), applies it to all G query heads of the group (each K/V byte serves G
 // heads), and leaves an unnormalised partial softmax state (max, sum, acc) in
-// the workspace.  The last workgroup of a (sequence, group) to finish -- found
-// with one arrival counter per group -- merges the k+1 partials of each head
-// in slot order:  o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u,  so the
-// result does not depend on arrival order and is bitwise reproducible.  That
-// workgroup also resets the counter, leaving the workspace ready for the next
-// call (the counters must be zero before the first one).
+// the workspace.  A second, small kernel merges the k+1 partials of each head
+// in slot order:  o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u,  issuing
+// all of its loads at once; the kernel boundary orders the two, so no
+// device-wide fences or atomics are needed and results are bitwise
+// reproducible.
 #include "sas_device.h"
 #include "sas_internal.h"
 
@@ -32,11 +31,10 @@ template <int G, int D> struct DecPartial {
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kDecThreads)
-decode_fwd_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
+decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
                   const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
                   const float* __restrict__ log_gate, float scale2, int Hkv, int t_max, int k,
-                  unsigned* __restrict__ counters, float* __restrict__ part, T* __restrict__ o,
-                  float* __restrict__ lse) {
+                  float* __restrict__ part) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per row
   constexpr int RPI = 64 / LPR;         // rows per wave load instruction
@@ -45,10 +43,6 @@ decode_fwd_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __r
   __shared__ float red_m[4][G];
   __shared__ float red_l[4][G];
   __shared__ float red_acc[4][G][D];
-  __shared__ float mrg_w[kMaxTopK + 1][G];  // per-slot max, then merge weight
-  __shared__ float mrg_l[kMaxTopK + 1][G];
-  __shared__ float mrg_L[G];
-  __shared__ int s_last;
 
   const int u = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,7 +114,7 @@ decode_fwd_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __r
       float v = z[0][h];
 #pragma unroll
       for (int i = 1; i < NI; ++i) v = fmaxf(v, z[i][h]);
-      mh[h] = wave_max_from(v, LPR);
+      mh[h] = wave_max_from(v, LPR);  // across the row groups
     }
     if (lane == 0) {
 #pragma unroll
@@ -152,16 +146,44 @@ decode_fwd_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __r
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      lh[h] = wave_sum_from(lh[h], LPR);
+    for (int h = 0; h < G; ++h) lh[h] = wave_sum_from(lh[h], LPR);
+    // Sum acc over the RG = 64/LPR row groups of the wave with a transposed
+    // butterfly: each step halves the values a lane keeps, so lane group q
+    // ends up owning NV/RG distinct (head, element) sums.
+    constexpr int NV = G * EPL, RG = 64 / LPR;
+    float av[NV];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = wave_sum_from(acc[h][e], LPR);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) av[h * EPL + e] = acc[h][e];
+    int kept = NV;
+#pragma unroll
+    for (int sft = 32; sft >= LPR; sft >>= 1) {
+      const uint32_t up = (lane & sft) ? 0xFFFFFFFFu : 0u;
+      const int half = kept / 2;
+#pragma unroll
+      for (int j = 0; j < NV / 2; ++j) {
+        if (j < half) {
+          const uint32_t a = __float_as_uint(av[j]), bb = __float_as_uint(av[j + half]);
+          const float keep = __uint_as_float((bb & up) | (a & ~up));
+          const float send = __uint_as_float((a & up) | (bb & ~up));
+          av[j] = keep + __shfl_xor(send, sft, 64);
+        }
+      }
+      kept = half;
     }
-    if (lane < LPR) {
+    {
+      // lane's row group q = lane / LPR selects which block of NV/RG values it owns
+      const int q = lane / LPR;
+      int owner = 0;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int bit = RG / 2, sft = 32; bit >= 1; bit >>= 1, sft >>= 1)
+        if (lane & sft) owner += bit;
+      (void)q;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) red_acc[wave][h][col * EPL + e] = acc[h][e];
+      for (int j = 0; j < NV / RG; ++j) {
+        const int vi = owner * (NV / RG) + j;
+        red_acc[wave][vi / EPL][col * EPL + (vi % EPL)] = av[j];
       }
     }
     if (lane == 0) {
@@ -179,68 +201,79 @@ decode_fwd_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __r
     }
   }
 
-  // ---- arrival; the last workgroup of the row merges
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(counters + row, 1u) == static_cast<unsigned>(k);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  const float* base = part + row * (k + 1) * static_cast<size_t>(PF);
-  for (int x = tid; x < (k + 1) * G; x += kDecThreads) {  // all (max, sum) loads at once
-    const int uu = x / G, g = x % G;
-    mrg_w[uu][g] = base[uu * PF + G * D + g];
-    mrg_l[uu][g] = base[uu * PF + G * D + G + g];
-  }
-  __syncthreads();
-  if (tid < G) {
-    const int g = tid;
-    float M = -INFINITY;
-    for (int uu = 0; uu <= k; ++uu) M = fmaxf(M, mrg_w[uu][g]);
-    float L = 0.f;
-    for (int uu = 0; uu <= k; ++uu) {
-      const float w = exp2f(mrg_w[uu][g] - M);
-      mrg_w[uu][g] = w;
-      L += w * mrg_l[uu][g];
-    }
-    mrg_L[g] = L;
-    if (lse) lse[row * G + g] = M * kLn2 + logf(L);
-  }
-  __syncthreads();
-  for (int x = tid; x < G * D; x += kDecThreads) {
-    const int g = x / D;
-    float a = 0.f;
-#pragma unroll 8
-    for (int uu = 0; uu <= k; ++uu) a += mrg_w[uu][g] * base[uu * PF + x];
-    store_scalar<T>(o + (row * G) * static_cast<size_t>(D) + x, a / mrg_L[g]);
-  }
-  if (tid == 0) counters[row] = 0u;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// One workgroup per (sequence, group): thread x handles outputs x, x + 256 of
+// the group's G*D.  The partials are folded in slot order with the usual
+// online rescaling, loading BATCH slots at a time before using any of them.
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kDecThreads)
+decode_merge_kernel(int Hkv, int k, const float* __restrict__ part, T* __restrict__ o,
+                    float* __restrict__ lse) {
+  constexpr int PF = DecPartial<G, D>::kFloats;
+  constexpr int PER = (G * D + kDecThreads - 1) / kDecThreads;
+  constexpr int BATCH = 24;  // k = 16 or 23: one round trip of loads
+  const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(b) * Hkv + r;
+  const float* base = part + row * (k + 1) * static_cast<size_t>(PF);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int x = tid + e * kDecThreads;
+    if (x >= G * D) break;
+    const int g = x / D;
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int u0 = 0; u0 <= k; u0 += BATCH) {
+      float mv[BATCH], lv[BATCH], av[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int u = u0 + j;
+        mv[j] = -INFINITY;
+        lv[j] = 0.f;
+        av[j] = 0.f;
+        if (u <= k) {
+          const float* pu = base + static_cast<size_t>(u) * PF;
+          mv[j] = pu[G * D + g];
+          lv[j] = pu[G * D + G + g];
+          av[j] = pu[x];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        if (mv[j] == -INFINITY) continue;  // empty slot
+        const float mn = fmaxf(M, mv[j]);
+        const float so = exp2f(M - mn), w = exp2f(mv[j] - mn);
+        L = L * so + w * lv[j];
+        A = A * so + w * av[j];
+        M = mn;
+      }
+    }
+    store_scalar<T>(o + (row * G) * static_cast<size_t>(D) + x, A / L);
+    if (lse && (x % D) == 0) lse[row * G + g] = M * kLn2 + logf(L);
+  }
+}
 
-// workspace: counters[B*Hkv] | partials[B*Hkv*(k+1)*G*(d+2)] fp32
+// workspace: partials[B*Hkv*(k+1)*G*(d+2)] fp32
 size_t decode_ws_bytes(const sas_dims& d) {
   const int G = d.n_q_heads / d.n_kv_heads;
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
-  return align256(rows * sizeof(unsigned)) +
-         rows * (d.top_k + 1) * G * (d.head_dim + 2) * sizeof(float);
+  return rows * (d.top_k + 1) * G * (d.head_dim + 2) * sizeof(float);
 }
 
 template <typename T, int D, int G>
 static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, const void* V,
                              const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
                              float scale, void* o, float* lse, void* ws, hipStream_t st) {
-  const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
-  unsigned* counters = static_cast<unsigned*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(rows * sizeof(unsigned)));
-  hipLaunchKernelGGL((decode_fwd_kernel<T, D, G>), dim3(d.top_k + 1, d.n_kv_heads, d.batch),
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(d.top_k + 1, d.n_kv_heads, d.batch),
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx, log_gate,
-                     scale * kLog2e, d.n_kv_heads, d.t_max, d.top_k, counters, part,
-                     static_cast<T*>(o), lse);
-  return check_launch("decode_fwd");
+                     scale * kLog2e, d.n_kv_heads, d.t_max, d.top_k, part);
+  sas_status s = check_launch("decode_split");
+  if (s != SAS_OK) return s;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(d.n_kv_heads, d.batch),
+                     dim3(kDecThreads), 0, st, d.n_kv_heads, d.top_k, part, static_cast<T*>(o),
+                     lse);
+  return check_launch("decode_merge");
 }
 
 template <typename T, int D>

@@ -24,6 +24,60 @@
 
 namespace sas {
 
+// Per-thread share of staging one 64-token block: K rows (16-byte chunks)
+// and V row pairs (transposed on the way into LDS).
+template <int D, int NT>
+struct BlockStage {
+  static constexpr int KTOT = 64 * (D / 8);          // 16-byte K chunks per block
+  static constexpr int VTOT = 32 * (D / 8);          // V row pairs per block
+  static constexpr int KCH = (KTOT + NT - 1) / NT;   // per thread
+  static constexpr int VCH = (VTOT + NT - 1) / NT;
+  uint4 k[KCH];
+  uint4 v0[VCH], v1[VCH];
+
+  __device__ __forceinline__ void load(const uint16_t* Kb, const uint16_t* Vb, int valid, int tid) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
+      k[i] = (c < KTOT && row < valid)
+                 ? *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(row) * D + cc * 8)
+                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int p = tid + i * NT, tp = p % 32, cc = p / 32, r0 = 2 * tp;
+      const bool in = p < VTOT;
+      v0[i] = (in && r0 < valid)
+                  ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(r0) * D + cc * 8)
+                  : make_uint4(0, 0, 0, 0);
+      v1[i] = (in && r0 + 1 < valid)
+                  ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(r0 + 1) * D + cc * 8)
+                  : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vt, int tid) const {
+    constexpr int RSTR = D + 8, TSTR = 64 + 8;
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
+      if (c < KTOT) *reinterpret_cast<uint4*>(&Ks[row * RSTR + cc * 8]) = k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int p = tid + i * NT, tp = p % 32, cc = p / 32;
+      if (p >= VTOT) continue;
+      const uint32_t w0[4] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w};
+      const uint32_t w1[4] = {v1[i].x, v1[i].y, v1[i].z, v1[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t*>(&Vt[(cc * 8 + e) * TSTR + 2 * tp]) = lo | (hi << 16);
+      }
+    }
+  }
+};
+
 template <int D, int HPW>
 __global__ void __launch_bounds__(128 * HPW)
 prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -36,8 +90,11 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int CT = D / 32;         // channel tiles of O^T
   constexpr int KSTR = D + 8;        // K row stride in LDS (bf16), +16 bytes
   constexpr int VSTR = 64 + 8;       // V^T row stride in LDS (bf16), +16 bytes
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+  __shared__ int s_blk[kMaxTopK + 1];
+  __shared__ float s_beta[kMaxTopK + 1];
+  __shared__ int s_nblk;
 
   const int nhc = G / HPW;                       // head chunks per group
   const int t = n_tiles - 1 - static_cast<int>(blockIdx.x) / nhc;
@@ -50,6 +107,24 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int qi = t * 64 + qloc;
   const bool qvalid = qi < S;
 
+  // block list: the valid selected blocks (in slot order), then the diagonal
+  const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
+  if (wave == 0) {
+    const bool ok = lane < k && idx[srow * k + lane] >= 0;
+    const unsigned long long mask = __ballot(ok);
+    if (ok) {
+      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+      s_blk[pos] = idx[srow * k + lane];
+      s_beta[pos] = log_gate ? log_gate[srow * k + lane] * kLog2eF : 0.f;
+    }
+    if (lane == 0) {
+      const int nv = __popcll(mask);
+      s_blk[nv] = t;
+      s_beta[nv] = 0.f;
+      s_nblk = nv + 1;
+    }
+  }
+
   bf16x8_t qb[KS];  // B operand of S^T = K Q^T: Q[qi][16ks + 8hi .. +8]
   {
     const uint16_t* qrow = Q + ((static_cast<size_t>(b) * Hq + h) * S + (qvalid ? qi : 0)) * D + 8 * hi;
@@ -60,63 +135,67 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
   f32x16_t acc[CT];
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[ct][v] = 0.f;
+  for (int ct = 0; ct < CT; ++ct) zero16(acc[ct]);
   float m_run = -INFINITY, l_run = 0.f;
 
-  const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
+  __syncthreads();
+  const int nblk = s_nblk;
 
-  for (int it = 0; it <= k; ++it) {
-    const bool diag = it == k;
-    int blk = t;
-    float beta2 = 0.f;
-    if (!diag) {
-      blk = idx[srow * k + it];
-      if (blk < 0) continue;  // uniform across the workgroup
-      if (log_gate) beta2 = log_gate[srow * k + it] * kLog2eF;
+  BlockStage<D, NT> stg;
+  {
+    const int tok0 = s_blk[0] * 64;
+    stg.load(Kg + static_cast<size_t>(tok0) * D, Vg + static_cast<size_t>(tok0) * D, S - tok0, tid);
+    stg.store(Ks[0], Vt[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nblk; ++it) {
+    const int buf = it & 1;
+    const bool diag = it == nblk - 1;
+    const float beta2 = s_beta[it];
+    if (it + 1 < nblk) {  // prefetch the next block while this one computes
+      const int tok1 = s_blk[it + 1] * 64;
+      stg.load(Kg + static_cast<size_t>(tok1) * D, Vg + static_cast<size_t>(tok1) * D, S - tok1, tid);
     }
-    const int tok0 = blk * 64;
-    __syncthreads();  // the previous block's LDS reads are done
-    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, nullptr, tid);
-    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, nullptr, Vt, tid);
-    __syncthreads();
+    const uint16_t* Kc = Ks[buf];
+    const uint16_t* Vc = Vt[buf];
 
     // S^T (64 tokens x 32 queries) = K Q^T
     f32x16_t s[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[tt][v] = 0.f;
+      zero16(s[tt]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[(32 * tt + l32) * KSTR + 16 * ks + 8 * hi]));
+        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kc[(32 * tt + l32) * KSTR + 16 * ks + 8 * hi]));
         s[tt] = mfma32x32x16(a, qb[ks], s[tt]);
       }
     }
     // online softmax on the lane's query column (base-2 domain)
+    if (diag) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * tt + acc_row(v, hi) > qloc) s[tt][v] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tok = 32 * tt + 8 * (v >> 2) + 4 * hi + (v & 3);
-        float z = s[tt][v] * scale2 + beta2;
-        if (diag && tok > qloc) z = -INFINITY;
-        s[tt][v] = z;
-        mx = fmaxf(mx, z);
-      }
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[tt][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = fmaxf(m_run, mx * scale2 + beta2);
     const float alpha = exp2f(m_run - m_new);
+    const float off = beta2 - m_new;
     float ls = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(s[tt][v] - m_new);
+        const float p = exp2f(fmaf(s[tt][v], scale2, off));
         s[tt][v] = p;
         ls += p;
       }
@@ -134,8 +213,10 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const bf16x8_t pb = acc_to_bop(s, j);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        acc[ct] = mfma32x32x16(lds_aop_perm(&Vt[(32 * ct + l32) * VSTR], j, hi), pb, acc[ct]);
+        acc[ct] = mfma32x32x16(lds_aop_perm(&Vc[(32 * ct + l32) * VSTR], j, hi), pb, acc[ct]);
     }
+    if (it + 1 < nblk) stg.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+    __syncthreads();
   }
 
   if (qvalid) {

@@ -59,10 +59,57 @@ __device__ __forceinline__ float wave_max_from(float v, int lo) {
   for (int m = lo; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
   return v;
 }
-// Reductions across the lanes [0, n) of each aligned group of n lanes.
+// DPP lane moves inside a row of 16 lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i inside each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i inside each row
+
+// Sum over each aligned group of n lanes (n a power of two, <= 64); every
+// lane of the group receives the sum.  Within a row the partner lanes come
+// from DPP moves: after the xor-1 and xor-2 steps each quad holds its sum,
+// so the half-row and row mirrors pair whole quads and half rows.
 __device__ __forceinline__ float group_sum(float v, int n) {
-  for (int m = 1; m < n; m <<= 1) v += __shfl_xor(v, m, 64);
+  if (n >= 2) v += dpp_mov<kDppXor1>(v);
+  if (n >= 4) v += dpp_mov<kDppXor2>(v);
+  if (n >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if (n >= 16) v += dpp_mov<kDppMirror>(v);
+  if (n >= 32) v += __shfl_xor(v, 16, 64);
+  if (n >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+__device__ __forceinline__ float group_max(float v, int n) {
+  if (n >= 2) v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  if (n >= 4) v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  if (n >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  if (n >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  if (n >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if (n >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+// Transposed butterfly over the 32 lanes of each half wave: lane l32 starts
+// with 32 partial values v[0..31] and ends with v[0] = the sum over the half
+// wave of v[l32].  31 shuffles in all.  The keep/send choice is an integer
+// blend so the compiler cannot turn it into dynamic register indexing.
+__device__ __forceinline__ float transpose_sum32(float* v, int l32) {
+#pragma unroll
+  for (int sft = 16; sft >= 1; sft >>= 1) {
+    const uint32_t up = (l32 & sft) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < sft; ++j) {
+      const uint32_t a = __float_as_uint(v[j]), b = __float_as_uint(v[j + sft]);
+      const float keep = __uint_as_float((b & up) | (a & ~up));
+      const float send = __uint_as_float((a & up) | (b & ~up));
+      v[j] = keep + __shfl_xor(send, sft, 64);
+    }
+  }
+  return v[0];
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger float -> larger
@@ -108,6 +155,42 @@ __device__ inline void bitonic_sort_desc(uint64_t* keys, int n) {
     }
   }
   __syncthreads();
+}
+
+// 64-bit xor shuffle inside a wave.
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m, 64);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m, 64);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Bitonic sort of one key per lane across a wave into DESCENDING lane order
+// (lane 0 holds the largest).  Wave-synchronous: no LDS, no barrier.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t key) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint64_t other = shfl_xor_u64(key, stride);
+      const bool desc = (lane & size) == 0;
+      const bool lower = (lane & stride) == 0;
+      const bool keep_max = (lower == desc);
+      key = keep_max ? (key > other ? key : other) : (key < other ? key : other);
+    }
+  }
+  return key;
+}
+
+// Number of entries greater than x in a DESCENDING sorted list of n keys.
+__device__ __forceinline__ int count_greater_desc(const uint64_t* list, int n, uint64_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (list[mid] > x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
 }
 
 }  // namespace sas

@@ -24,7 +24,7 @@ namespace sas {
 constexpr int kSelThreads = 256;
 
 __device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max_from(v, 1);
+  v = group_max(v, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
@@ -34,7 +34,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 __device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum_from(v, 1);
+  v = group_sum(v, 64);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
@@ -99,16 +99,7 @@ __device__ __forceinline__ void score_rows(const float* __restrict__ summ_row0, 
 #pragma unroll
       for (int j = 0; j < 32; ++j) v[j] = x[j].x * qv[0] + x[j].y * qv[1];
     }
-#pragma unroll
-    for (int sft = 16; sft >= 1; sft >>= 1) {
-      const bool up = (l32 & sft) != 0;
-#pragma unroll
-      for (int j = 0; j < sft; ++j) {
-        const float keep = up ? v[j + sft] : v[j];
-        const float send = up ? v[j] : v[j + sft];
-        v[j] = keep + __shfl_xor(send, sft, 64);
-      }
-    }
+    transpose_sum32(v, l32);
     const int i = base + hw + 8 * l32;
     if (i < n) sc[i] = v[0];
   }
@@ -132,112 +123,200 @@ __device__ __forceinline__ void write_selection(const uint64_t* keys, int kk, in
 }
 
 // ------------------------------------------------------------- decode ---
-// One launch per step: grid (chunk, group, sequence).  Every workgroup scores
-// its chunk, keeps the chunk's LSE state and its top-k keys in the workspace,
-// then bumps the row's arrival counter; the last workgroup of the row merges
-// the states and candidates in chunk order (so the result does not depend on
-// arrival order) and resets the counter to zero for the next call.
+// Chunk kernel: grid (chunk, group, sequence), kSelChunk blocks per chunk.
+// Every load the workgroup needs (q, one Wq_sel row per thread, 32 summary
+// slices per lane) is issued before any arithmetic, so the kernel pays about
+// one memory round trip.  Each wave then sorts its 64 scores with a shuffle
+// bitonic network, the four sorted lists are merged by rank (a key's rank is
+// its position in its own list plus the number of larger keys in the others,
+// found by binary search), and the chunk's top-k keys plus its (max, sum-exp)
+// go to the workspace.  A row that fits one chunk is finished right here.
 template <typename T, int D, int DS, int G>
 __global__ void __launch_bounds__(kSelThreads)
-select_decode_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
-                     const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
-                     int t_max, int c_max, int k, int kc, int nchunk, int npow,
-                     float* __restrict__ scores, unsigned* __restrict__ counters,
-                     float2* __restrict__ part, uint64_t* __restrict__ cand,
-                     int32_t* __restrict__ idx, float* __restrict__ log_gate,
-                     float* __restrict__ score_lse) {
+select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                           const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
+                           int t_max, int c_max, int k, int kc, int nchunk,
+                           float* __restrict__ scores, float2* __restrict__ part,
+                           uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
+                           float* __restrict__ log_gate, float* __restrict__ score_lse) {
+  constexpr int PL = DS / 32;                 // summary floats per lane
+  constexpr int NW = kSelThreads / 64;
   __shared__ float qm[D];
   __shared__ float qs[DS];
-  __shared__ float sc[kSelChunk];
-  __shared__ uint64_t keys[kSelChunk];
-  __shared__ float red[kSelThreads / 64];
-  __shared__ int s_last;
-  extern __shared__ uint64_t mkeys[];
+  __shared__ uint64_t lists[NW][64];
+  __shared__ uint64_t best[kMaxTopK];
+  __shared__ float red[2][NW];
 
   const int b = blockIdx.z, r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hw = tid >> 5, l32 = tid & 31;
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
   const int m0 = chunk * kSelChunk;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const size_t p = row * nchunk + chunk;
-  float M = -INFINITY, S = 0.f;
-  if (m0 < C) {
-    const int n = min(kSelChunk, C - m0);
-    if (tid < D) {
-      const T* qb = q + (row * G) * static_cast<size_t>(D) + tid;
+  const int n = max(0, min(kSelChunk, C - m0));
+
+  // ---- all loads up front
+  float qraw[G];
+  if (tid < D) {
+    const T* qb = q + (row * G) * static_cast<size_t>(D) + tid;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qraw[h] = load_scalar<T>(qb + h * D);
+  }
+  float4 wrow[D / 4];
+  if (tid < DS) {
+    const float4* w = reinterpret_cast<const float4*>(Wq + static_cast<size_t>(tid) * D);
+#pragma unroll
+    for (int c4 = 0; c4 < D / 4; ++c4) wrow[c4] = w[c4];
+  }
+  const float* srow = summ + (row * c_max + m0) * static_cast<size_t>(DS) + l32 * PL;
+  float xs[32][PL];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int i = hw + 8 * j;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) xs[j][e] = 0.f;
+    if (i < n) {
+      if constexpr (PL == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(srow + static_cast<size_t>(i) * DS);
+        xs[j][0] = x.x; xs[j][1] = x.y; xs[j][2] = x.z; xs[j][3] = x.w;
+      } else {
+        const float2 x = *reinterpret_cast<const float2*>(srow + static_cast<size_t>(i) * DS);
+        xs[j][0] = x.x; xs[j][1] = x.y;
+      }
+    }
+  }
+  // ---- pooled query, projected
+  if (tid < D) {
+    float a = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) a += qraw[h];
+    qm[tid] = a / G;
+  }
+  __syncthreads();
+  if (tid < DS) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < D / 4; ++c4) {
+      a0 += wrow[c4].x * qm[4 * c4];
+      a1 += wrow[c4].y * qm[4 * c4 + 1];
+      a2 += wrow[c4].z * qm[4 * c4 + 2];
+      a3 += wrow[c4].w * qm[4 * c4 + 3];
+    }
+    qs[tid] = ((a0 + a1) + (a2 + a3)) * (1.0f / sqrtf(static_cast<float>(DS)));
+  }
+  __syncthreads();
+  // ---- scores: half wave hw owns rows hw + 8j; the transposed butterfly
+  // leaves row hw + 8*l32 in lane l32
+  float v[32];
+  {
+    float qv[PL];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) qv[e] = qs[l32 * PL + e];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
       float a = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) a += load_scalar<T>(qb + h * D);
-      qm[tid] = a / G;
+      for (int e = 0; e < PL; ++e) a += xs[j][e] * qv[e];
+      v[j] = a;
     }
-    __syncthreads();
-    project_query<D, DS>(Wq, qm, qs);
-    __syncthreads();
-    const float* srow = summ + row * static_cast<size_t>(c_max) * DS;
-    score_rows<DS>(srow + static_cast<size_t>(m0) * DS, qs, n, sc);
-    __syncthreads();
-    const bool valid = tid < n;
-    const float s = valid ? sc[tid] : -INFINITY;
-    if (scores && valid) scores[row * c_max + m0 + tid] = s;
-    M = block_max(s, red);
-    S = block_sum(valid ? expf(s - M) : 0.f, red);
-    keys[tid] = valid ? topk_key(s, m0 + tid) : 0ull;
-    bitonic_sort_desc(keys, kSelChunk);
   }
-  const int kk = min(k, C);
-  if (nchunk == 1) {  // the row fits one chunk: finish here
-    const float lse = C > 0 ? M + logf(S) : -INFINITY;
-    write_selection(keys, kk, k, lse, idx + row * k, log_gate + row * k);
+  transpose_sum32(v, l32);
+  const int i_row = hw + 8 * l32;
+  const bool valid = i_row < n;
+  const float sc = valid ? v[0] : -INFINITY;
+  if (scores && valid) scores[row * c_max + m0 + i_row] = sc;
+
+  // ---- chunk (max, sum exp)
+  float mx = group_max(sc, 64);
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
+  float M = red[0][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[0][w]);
+  float se = group_sum(valid ? expf(sc - M) : 0.f, 64);
+  if (lane == 0) red[1][wave] = se;
+
+  // ---- chunk top-k
+  const uint64_t key = wave_sort_desc(valid ? topk_key(sc, m0 + i_row) : 0ull);
+  lists[wave][lane] = key;
+  __syncthreads();
+  float Ssum = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) Ssum += red[1][w];
+  {
+    int rank = lane;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w != wave) rank += count_greater_desc(lists[w], 64, key);
+    if (rank < kc && key != 0ull) best[rank] = key;
+  }
+  __syncthreads();
+  const int nk = min(kc, n);  // valid keys among the chunk's best
+  if (nchunk == 1) {
+    const float lse = C > 0 ? M + logf(Ssum) : -INFINITY;
+    write_selection(best, min(k, C), k, lse, idx + row * k, log_gate + row * k);
     if (tid == 0) score_lse[row] = lse;
     return;
   }
-  if (tid < kc) cand[p * kc + tid] = (m0 < C) ? keys[tid] : 0ull;
-  if (tid == 0) part[p] = make_float2(M, S);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(counters + row, 1u) == static_cast<unsigned>(nchunk - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (tid < kc) cand[p * kc + tid] = tid < nk ? best[tid] : 0ull;
+  if (tid == 0) part[p] = n > 0 ? make_float2(M, Ssum) : make_float2(-INFINITY, 0.f);
+}
 
+// Merge kernel: one workgroup per (group, sequence) combines the chunk
+// (max, sum-exp) pairs into LSE(s) and ranks the chunks' sorted candidate
+// lists (the same binary-search ranking) into the row's top-k.
+__global__ void __launch_bounds__(kSelThreads)
+select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_max, int k,
+                           int kc, int nchunk, const float2* __restrict__ part,
+                           const uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
+                           float* __restrict__ log_gate, float* __restrict__ score_lse) {
+  extern __shared__ uint64_t lists[];        // nchunk * kc keys
+  __shared__ uint64_t best[kMaxTopK];
+  __shared__ float red[kSelThreads / 64];
+  const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int len = clamp_len(seq_lens[b], t_max);
+  const int C = (len - 1) / kBlock;
+  const size_t row = static_cast<size_t>(b) * Hkv + r;
+  const int ncand = nchunk * kc;
+  const uint64_t* cr = cand + row * static_cast<size_t>(ncand);
+  for (int i = tid; i < ncand; i += kSelThreads) lists[i] = cr[i];
   const float2* pr = part + row * nchunk;
   float mloc = -INFINITY;
   for (int i = tid; i < nchunk; i += kSelThreads) mloc = fmaxf(mloc, pr[i].x);
-  const float Mr = block_max(mloc, red);
+  const float M = block_max(mloc, red);
   float sloc = 0.f;
   for (int i = tid; i < nchunk; i += kSelThreads) {
     const float2 v = pr[i];
-    if (v.x != -INFINITY) sloc += v.y * expf(v.x - Mr);
+    if (v.x != -INFINITY) sloc += v.y * expf(v.x - M);
   }
-  const float L = block_sum(sloc, red);
-  const float lse = C > 0 ? Mr + logf(L) : -INFINITY;
-  const int ncand = nchunk * kc;
-  const uint64_t* cr = cand + row * static_cast<size_t>(nchunk) * kc;
-  for (int i = tid; i < npow; i += kSelThreads) mkeys[i] = i < ncand ? cr[i] : 0ull;
-  bitonic_sort_desc(mkeys, npow);
-  write_selection(mkeys, kk, k, lse, idx + row * k, log_gate + row * k);
-  if (tid == 0) {
-    score_lse[row] = lse;
-    counters[row] = 0u;
+  const float L = block_sum(sloc, red);  // ends with a barrier: lists are complete
+  const float lse = C > 0 ? M + logf(L) : -INFINITY;
+  for (int i = tid; i < ncand; i += kSelThreads) {
+    const int c = i / kc, pos = i % kc;
+    const uint64_t key = lists[i];
+    if (key == 0ull) continue;
+    int rank = pos;
+    for (int c2 = 0; c2 < nchunk && rank < kc; ++c2)
+      if (c2 != c) rank += count_greater_desc(lists + c2 * kc, kc, key);
+    if (rank < kc) best[rank] = key;
   }
+  __syncthreads();
+  write_selection(best, min(k, C), k, lse, idx + row * k, log_gate + row * k);
+  if (tid == 0) score_lse[row] = lse;
 }
 
 static int decode_nchunk(const sas_dims& d) {
   const int n = cdiv(d.t_max / kBlock, kSelChunk);
   return n > 0 ? n : 1;
 }
-static int next_pow2(int n) {
-  int p = 2;
-  while (p < n) p <<= 1;
-  return p;
-}
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// workspace: counters[rows] | part[rows*nchunk] | cand[rows*nchunk*max(k,1)]
+// workspace: part[rows*nchunk] | cand[rows*nchunk*max(k,1)]
 size_t select_decode_ws_bytes(const sas_dims& d) {
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
   const size_t nc = decode_nchunk(d);
-  return align256(rows * sizeof(unsigned)) + align256(rows * nc * sizeof(float2)) +
+  return align256(rows * nc * sizeof(float2)) +
          rows * nc * static_cast<size_t>(d.top_k > 0 ? d.top_k : 1) * sizeof(uint64_t);
 }
 
@@ -248,21 +327,24 @@ static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq
   const int nchunk = decode_nchunk(d);
   const int k = d.top_k;
   const int kc = k > 0 ? k : 1;
-  const int npow = nchunk > 1 ? next_pow2(nchunk * kc) : 0;
-  if (npow > 8192)
-    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge sort",
+  if (nchunk * kc > 8192)
+    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
                 nchunk * kc);
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
   char* w = static_cast<char*>(ws);
-  unsigned* counters = reinterpret_cast<unsigned*>(w);
-  float2* part = reinterpret_cast<float2*>(w + align256(rows * sizeof(unsigned)));
-  uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(rows * sizeof(unsigned)) +
-                                               align256(rows * nchunk * sizeof(float2)));
-  hipLaunchKernelGGL((select_decode_kernel<T, D, DS, G>), dim3(nchunk, d.n_kv_heads, d.batch),
-                     dim3(kSelThreads), npow * sizeof(uint64_t), st, static_cast<const T*>(q),
-                     seq_lens, Wq, summ, d.n_kv_heads, d.t_max, d.t_max / kBlock, k, kc, nchunk,
-                     npow, scores, counters, part, cand, idx, log_gate, score_lse);
-  return check_launch("select_decode");
+  float2* part = reinterpret_cast<float2*>(w);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(rows * nchunk * sizeof(float2)));
+  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G>),
+                     dim3(nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,
+                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,
+                     d.t_max / kBlock, k, kc, nchunk, scores, part, cand, idx, log_gate,
+                     score_lse);
+  sas_status s = check_launch("select_decode_chunk");
+  if (s != SAS_OK || nchunk == 1) return s;
+  hipLaunchKernelGGL(select_decode_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kSelThreads),
+                     nchunk * kc * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max, k, kc,
+                     nchunk, part, cand, idx, log_gate, score_lse);
+  return check_launch("select_decode_merge");
 }
 
 // -------------------------------------------------------------- tiles ---

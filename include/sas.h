@@ -33,11 +33,9 @@
  *  - Ownership: the caller allocates and owns every buffer, including the
  *    workspace sized by sas_workspace_bytes().  The library allocates and
  *    frees nothing and keeps no pointer after a call returns.
- *  - Workspaces of sas_select (DECODE mode) and sas_decode_fwd begin with one
- *    32-bit arrival counter per (sequence, group): they must be zero before
- *    the first call that uses the workspace, and every call leaves them zero
- *    again (so zero-fill a new workspace once).  Calls that share one
- *    workspace must not run concurrently.
+ *  - A workspace holds intermediate results of one call only (no state is
+ *    carried between calls; its initial contents do not matter).  Calls that
+ *    share one workspace must not run concurrently.
  *  - Execution: each call validates its arguments on the host, then enqueues
  *    kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
  *    The caller synchronises.  Results are bitwise deterministic.

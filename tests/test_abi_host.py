@@ -125,9 +125,8 @@ def test_select_and_summaries_validation(lib):
 def test_workspace_sizes(lib):
     d = _dims()
     assert B.sas_workspace_bytes(B.SAS_OP_SELECT_TILES, d, 16384) == 0
-    # decode: 256-byte-aligned arrival counters, then one partial
-    # (acc[d] + max + sum) per head and per unit (k slots + B0)
-    assert B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d) == 256 + 1 * 8 * 17 * 4 * 130 * 4
+    # decode: one partial (acc[d] + max + sum) per head and per unit (k slots + B0)
+    assert B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d) == 1 * 8 * 17 * 4 * 130 * 4
     with pytest.raises(B.SasError):
         B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, _dims(head_dim=96))
     with pytest.raises(B.SasError):
