@@ -15,9 +15,10 @@
 //     tiles that selected its block (binary search in each later tile's
 //     ascending idx row) plus the diagonal tile, then for every such tile and
 //     head recomputes S = Q K^T (a lane owns one token column), dP = dO V^T,
-//     dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS in registers.  It
-//     is the only writer of dK/dV for its block and of the dlog_gate entries
-//     that point at it, which it sums over heads in a fixed order.
+//     dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS in registers, one
+//     wave per head.  It is the only writer of dK/dV for its block and of the
+//     dlog_gate entries that point at it, which it sums over heads in a fixed
+//     order.
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_mfma.h"
@@ -141,28 +142,38 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 }
 
 // --------------------------------------------------------- dK/dV pass ---
-template <int D>
-__global__ void __launch_bounds__(128)
+// One workgroup per (key block m, group r, sequence) with up to 4 waves; wave
+// w handles heads w, w + 4, ... of the group and all 64 tokens of the block,
+// keeping dK^T and dV^T (channels x tokens) in accumulator registers.  K and
+// V rows of the block are staged once in shared LDS (B operands of S = Q K^T
+// and dP = dO V^T).  For every tile that reads the block and every head, the
+// wave loads the tile's Q and dO rows straight into registers as A operands,
+// then writes them transposed into its own LDS region (the A operands of
+// dK^T += Q^T dS and dV^T += dO^T P), so the waves never wait for each other
+// between tiles.  dlog_gate partials are summed over waves at the end.
+template <int D, int NWV>
+__global__ void __launch_bounds__(64 * NWV)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv,
                 int G, int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
                 const float* __restrict__ log_gate, float scale2, float scale,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
-  constexpr int NT = 128;
+  constexpr int NT = 64 * NWV;
   constexpr int KS = D / 16, CT = D / 32;
-  constexpr int RSTR = D + 8, TSTR = 64 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[D * TSTR];
-  __shared__ float lse_s[64];
-  __shared__ float D_s[64];
+  constexpr int RSTR = D + 8;       // K/V row stride (bf16)
+  constexpr int TSTR = 32 + 8;      // transposed Q/dO row stride (32 queries)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * RSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * RSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Qt[NWV][D * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t dOt[NWV][D * TSTR];
   __shared__ int list_t[kMaxTileRows];
   __shared__ int list_slot[kMaxTileRows];
+  __shared__ float dsum_s[NWV][kMaxTileRows];
+  __shared__ float lse_w[NWV][64];   // per wave: lse (base 2) and D of the tile's queries
+  __shared__ float dq_w[NWV][64];
   __shared__ int s_count;
-  __shared__ int s_wcount[2];
-  __shared__ float s_red[2];
+  __shared__ int s_wcount[NWV];
 
   const int m = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -196,35 +207,38 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int before = __popcll(mask & ((1ull << lane) - 1ull));
     if (lane == 0) s_wcount[wave] = __popcll(mask);
     __syncthreads();
-    const int off = s_count + (wave == 1 ? s_wcount[0] : 0);
+    int off = s_count;
+    for (int w = 0; w < wave; ++w) off += s_wcount[w];
     if (slot >= 0) {
       list_t[off + before] = t;
       list_slot[off + before] = slot;
     }
     __syncthreads();
-    if (tid == 0) s_count += s_wcount[0] + s_wcount[1];
+    if (tid == 0) {
+      int add = 0;
+      for (int w = 0; w < NWV; ++w) add += s_wcount[w];
+      s_count += add;
+    }
     __syncthreads();
   }
   const int n_list = s_count;
 
-  // ---- this lane's token column: K/V rows as B operands
-  const int tokloc = 32 * wave + l32;
-  const int tok = 64 * m + tokloc;
-  const bool tvalid = tok < S;
-  const uint16_t* Krow = K + (grow * t_max + (tvalid ? tok : 0)) * D;
-  const uint16_t* Vrow = V + (grow * t_max + (tvalid ? tok : 0)) * D;
-  bf16x8_t kb[KS], vb[KS];
+  // ---- stage the block's K and V rows (B operands, shared by the waves)
+  const int tok0 = 64 * m;
+  stage_rows<D, NT>(K + (grow * t_max + tok0) * D, S - tok0, Ks, nullptr, tid);
+  stage_rows<D, NT>(V + (grow * t_max + tok0) * D, S - tok0, Vs, nullptr, tid);
+  __syncthreads();
+
+  f32x16_t dk[2][CT], dv[2][CT];  // [token tile][channel tile]
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kb[ks] = as_bf16x8(tvalid ? *reinterpret_cast<const uint4*>(Krow + 16 * ks + 8 * hi) : make_uint4(0, 0, 0, 0));
-    vb[ks] = as_bf16x8(tvalid ? *reinterpret_cast<const uint4*>(Vrow + 16 * ks + 8 * hi) : make_uint4(0, 0, 0, 0));
-  }
-  f32x16_t dk[CT], dv[CT];
+  for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    zero16(dk[ct]);
-    zero16(dv[ct]);
-  }
+    for (int ct = 0; ct < CT; ++ct) {
+      zero16(dk[tt][ct]);
+      zero16(dv[tt][ct]);
+    }
+  uint16_t* qt_s = Qt[wave];
+  uint16_t* dot_s = dOt[wave];
 
   for (int e = 0; e < n_list; ++e) {
     const int t = list_t[e], slot = list_slot[e];
@@ -233,64 +247,137 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int q0 = 64 * t;
     const int nq = min(64, S - q0);
     float dsum = 0.f;
-    for (int g = 0; g < G; ++g) {
+    for (int g = wave; g < G; g += NWV) {
       const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g) * S + q0;
-      __syncthreads();
-      stage_rows<D, NT>(Q + hrow * D, nq, Qs, Qt, tid);
-      stage_rows<D, NT>(dO + hrow * D, nq, dOs, dOt, tid);
-      if (tid < 64) {
-        lse_s[tid] = tid < nq ? lse[hrow + tid] * kLog2eF : 0.f;
-        D_s[tid] = tid < nq ? Dq[hrow + tid] : 0.f;
-      }
-      __syncthreads();
-
-      // S and dP (64 queries x this wave's 32 tokens)
-      f32x16_t s[2], dp[2];
-#pragma unroll
+      lse_w[wave][lane] = lane < nq ? lse[hrow + lane] * kLog2eF : 0.f;
+      dq_w[wave][lane] = lane < nq ? Dq[hrow + lane] : 0.f;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
       for (int qt = 0; qt < 2; ++qt) {
-        zero16(s[qt]);
-        zero16(dp[qt]);
+        // A operands: Q and dO rows of queries 32qt + l32
+        const int qa_row = 32 * qt + l32;
+        const bool qok = qa_row < nq;
+        bf16x8_t qa[KS], da[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int off = (32 * qt + l32) * RSTR + 16 * ks + 8 * hi;
-          s[qt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(&Qs[off])), kb[ks], s[qt]);
-          dp[qt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(&dOs[off])), vb[ks], dp[qt]);
+          qa[ks] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(Q + (hrow + qa_row) * D + 16 * ks + 8 * hi)
+                                 : make_uint4(0, 0, 0, 0));
+          da[ks] = as_bf16x8(qok ? *reinterpret_cast<const uint4*>(dO + (hrow + qa_row) * D + 16 * ks + 8 * hi)
+                                 : make_uint4(0, 0, 0, 0));
         }
-      }
+        // S = Q K^T and dP = dO V^T (32 queries x 64 tokens)
+        f32x16_t s[2], dp[2];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+        for (int tt = 0; tt < 2; ++tt) {
+          zero16(s[tt]);
+          zero16(dp[tt]);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int q = 32 * qt + acc_row(v, hi);
-          const bool ok = tvalid && q < nq && !(diag && tokloc > q);
-          const float p = ok ? exp2f(s[qt][v] * scale2 + beta2 - lse_s[q]) : 0.f;
-          const float ds = p * (dp[qt][v] - D_s[q]);
-          s[qt][v] = p;
-          dp[qt][v] = ds;
-          dsum += ds;
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = (32 * tt + l32) * RSTR + 16 * ks + 8 * hi;
+            s[tt] = mfma32x32x16(qa[ks], as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[off])), s[tt]);
+            dp[tt] = mfma32x32x16(da[ks], as_bf16x8(*reinterpret_cast<const uint4*>(&Vs[off])), dp[tt]);
+          }
         }
-      // dV^T += dO^T P and dK^T += Q^T dS; k-step j = queries 16j..16j+15
+        // transposed copies of this half tile's Q and dO into the wave's LDS
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8_t pb = acc_to_bop(s, j);
-        const bf16x8_t sb = acc_to_bop(dp, j);
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 uq = __builtin_bit_cast(uint4, qa[ks]);
+          const uint4 ud = __builtin_bit_cast(uint4, da[ks]);
+          const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w};
+          const uint32_t wd[4] = {ud.x, ud.y, ud.z, ud.w};
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          dv[ct] = mfma32x32x16(lds_aop_perm(&dOt[(32 * ct + l32) * TSTR], j, hi), pb, dv[ct]);
-          dk[ct] = mfma32x32x16(lds_aop_perm(&Qt[(32 * ct + l32) * TSTR], j, hi), sb, dk[ct]);
+          for (int e8 = 0; e8 < 8; ++e8) {
+            const int c = 16 * ks + 8 * hi + e8;
+            qt_s[c * TSTR + l32] = static_cast<uint16_t>(wq[e8 >> 1] >> (16 * (e8 & 1)));
+            dot_s[c * TSTR + l32] = static_cast<uint16_t>(wd[e8 >> 1] >> (16 * (e8 & 1)));
+          }
         }
+        // P and dS (rows: queries, columns: this lane's token)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int tok = 32 * tt + l32;
+          const bool tok_ok = tok0 + tok < S;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int q = 32 * qt + acc_row(v, hi);
+            const bool ok = tok_ok && q < nq && !(diag && tok > q);
+            const float p = ok ? exp2f(fmaf(s[tt][v], scale2, beta2 - lse_w[wave][q])) : 0.f;
+            const float ds = p * (dp[tt][v] - dq_w[wave][q]);
+            s[tt][v] = p;
+            dp[tt][v] = ds;
+            dsum += ds;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // dV^T += dO^T P and dK^T += Q^T dS; k-step j = queries 32qt + 16j..
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            const bf16x8_t pb = acc_to_bop(&s[tt], j);
+            const bf16x8_t sb = acc_to_bop(&dp[tt], j);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              const int c = 32 * ct + l32;
+              dv[tt][ct] = mfma32x32x16(lds_aop_perm(&dot_s[c * TSTR], j, hi), pb, dv[tt][ct]);
+              dk[tt][ct] = mfma32x32x16(lds_aop_perm(&qt_s[c * TSTR], j, hi), sb, dk[tt][ct]);
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();  // transposed buffers are free again
       }
     }
-    if (!diag) {  // dlog_gate entry (t, slot): sum over both token halves
-      dsum = wave_sum_from(dsum, 1);
-      if (lane == 0) s_red[wave] = dsum;
-      __syncthreads();
-      if (tid == 0) dlg[(grow * n_tiles + t) * k + slot] = s_red[0] + s_red[1];
-    }
+    dsum = wave_sum_from(dsum, 1);
+    if (lane == 0) dsum_s[wave][e] = dsum;
   }
-  if (tvalid) {
-    store_acc_col<CT>(dk, scale, dK + (grow * t_max + tok) * D, hi);
-    store_acc_col<CT>(dv, 1.f, dV + (grow * t_max + tok) * D, hi);
+  __syncthreads();
+  // dlog_gate: one writer per (tile, slot) entry, heads summed in wave order
+  for (int e = 1 + tid; e < n_list; e += NT) {
+    float tot = 0.f;
+    for (int w = 0; w < NWV; ++w) tot += dsum_s[w][e];
+    dlg[(grow * n_tiles + list_t[e]) * k + list_slot[e]] = tot;
+  }
+  // ---- sum dK^T / dV^T over the waves (through LDS, wave by wave), store
+  float* red = reinterpret_cast<float*>(&Qt[0][0]);  // reuse: needs 64*D floats
+  for (int which = 0; which < 2; ++which) {
+    for (int w = 0; w < NWV; ++w) {
+      __syncthreads();
+      if (wave == w) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int tok = 32 * tt + l32, c = 32 * ct + acc_row(v, hi);
+              const float x = which ? dv[tt][ct][v] : dk[tt][ct][v];
+              float* slotp = &red[tok * D + c];
+              *slotp = (w == 0) ? x : *slotp + x;
+            }
+      }
+    }
+    __syncthreads();
+    uint16_t* dst = which ? dV : dK;
+    const float mul = which ? 1.f : scale;
+    for (int i = tid; i < 64 * (D / 4); i += NT) {
+      const int tok = i / (D / 4), c4 = (i % (D / 4)) * 4;
+      if (tok0 + tok < S) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          uint32_t u = __float_as_uint(red[tok * D + c4 + e4] * mul);
+          u += 0x7FFFu + ((u >> 16) & 1u);
+          wv[e4] = u >> 16;
+        }
+        uint2 pk;
+        pk.x = wv[0] | (wv[1] << 16);
+        pk.y = wv[2] | (wv[3] << 16);
+        *reinterpret_cast<uint2*>(dst + (grow * t_max + tok0 + tok) * D + c4) = pk;
+      }
+    }
   }
 }
 
@@ -334,10 +421,17 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
 #undef SAS_DQ_CASE
   s = check_launch("bwd_dq");
   if (s != SAS_OK) return s;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(n_tiles, d.n_kv_heads, d.batch), dim3(128), 0, st,
-                     q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, n_tiles, d.top_k, idx,
-                     log_gate, scale2, scale, static_cast<uint16_t*>(dK),
-                     static_cast<uint16_t*>(dV), dlg);
+#define SAS_DKDV_CASE(NWV)                                                                     \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles, d.n_kv_heads, d.batch),         \
+                     dim3(64 * NWV), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, \
+                     n_tiles, d.top_k, idx, log_gate, scale2, scale,                              \
+                     static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
+  switch (G) {
+    case 1: SAS_DKDV_CASE(1); break;
+    case 2: SAS_DKDV_CASE(2); break;
+    default: SAS_DKDV_CASE(4); break;
+  }
+#undef SAS_DKDV_CASE
   return check_launch("bwd_dkdv");
 }
 

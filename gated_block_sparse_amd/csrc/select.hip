@@ -264,23 +264,26 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
 }
 
 // Merge kernel: one workgroup per (group, sequence) combines the chunk
-// (max, sum-exp) pairs into LSE(s) and ranks the chunks' sorted candidate
-// lists (the same binary-search ranking) into the row's top-k.
+// (max, sum-exp) pairs into LSE(s) and merges the chunks' sorted candidate
+// lists pairwise, log2(#chunks) levels: an element's place in the merged list
+// is its own position plus the number of larger keys in the partner list
+// (binary search), and each merged list keeps its top kc.
 __global__ void __launch_bounds__(kSelThreads)
 select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_max, int k,
-                           int kc, int nchunk, const float2* __restrict__ part,
+                           int kc, int nchunk, int nlist, const float2* __restrict__ part,
                            const uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse) {
-  extern __shared__ uint64_t lists[];        // nchunk * kc keys
-  __shared__ uint64_t best[kMaxTopK];
+  extern __shared__ uint64_t lds[];          // two buffers of nlist * kc keys
   __shared__ float red[kSelThreads / 64];
   const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
-  const int ncand = nchunk * kc;
+  const int ncand = nchunk * kc, ntot = nlist * kc;
+  uint64_t* src = lds;
+  uint64_t* dst = lds + ntot;
   const uint64_t* cr = cand + row * static_cast<size_t>(ncand);
-  for (int i = tid; i < ncand; i += kSelThreads) lists[i] = cr[i];
+  for (int i = tid; i < ntot; i += kSelThreads) src[i] = i < ncand ? cr[i] : 0ull;
   const float2* pr = part + row * nchunk;
   float mloc = -INFINITY;
   for (int i = tid; i < nchunk; i += kSelThreads) mloc = fmaxf(mloc, pr[i].x);
@@ -290,19 +293,26 @@ select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_
     const float2 v = pr[i];
     if (v.x != -INFINITY) sloc += v.y * expf(v.x - M);
   }
-  const float L = block_sum(sloc, red);  // ends with a barrier: lists are complete
+  const float L = block_sum(sloc, red);  // ends with a barrier: src is complete
   const float lse = C > 0 ? M + logf(L) : -INFINITY;
-  for (int i = tid; i < ncand; i += kSelThreads) {
-    const int c = i / kc, pos = i % kc;
-    const uint64_t key = lists[i];
-    if (key == 0ull) continue;
-    int rank = pos;
-    for (int c2 = 0; c2 < nchunk && rank < kc; ++c2)
-      if (c2 != c) rank += count_greater_desc(lists + c2 * kc, kc, key);
-    if (rank < kc) best[rank] = key;
+  for (int nl = nlist; nl > 1; nl >>= 1) {
+    const int half = nl >> 1;
+    for (int i = tid; i < half * kc; i += kSelThreads) dst[i] = 0ull;
+    __syncthreads();
+    for (int i = tid; i < nl * kc; i += kSelThreads) {
+      const int li = i / kc, pos = i % kc;
+      const uint64_t key = src[i];
+      if (key == 0ull) continue;
+      const int partner = li ^ 1;
+      const int rank = pos + count_greater_desc(src + partner * kc, kc, key);
+      if (rank < kc) dst[(li >> 1) * kc + rank] = key;
+    }
+    __syncthreads();
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
   }
-  __syncthreads();
-  write_selection(best, min(k, C), k, lse, idx + row * k, log_gate + row * k);
+  write_selection(src, min(k, C), k, lse, idx + row * k, log_gate + row * k);
   if (tid == 0) score_lse[row] = lse;
 }
 
@@ -327,9 +337,11 @@ static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq
   const int nchunk = decode_nchunk(d);
   const int k = d.top_k;
   const int kc = k > 0 ? k : 1;
-  if (nchunk * kc > 8192)
+  int nlist = 1;
+  while (nlist < nchunk) nlist <<= 1;
+  if (nlist * kc > 2048)
     return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
-                nchunk * kc);
+                nlist * kc);
   const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
   char* w = static_cast<char*>(ws);
   float2* part = reinterpret_cast<float2*>(w);
@@ -342,8 +354,8 @@ static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq
   sas_status s = check_launch("select_decode_chunk");
   if (s != SAS_OK || nchunk == 1) return s;
   hipLaunchKernelGGL(select_decode_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kSelThreads),
-                     nchunk * kc * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max, k, kc,
-                     nchunk, part, cand, idx, log_gate, score_lse);
+                     2 * nlist * kc * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max, k, kc,
+                     nchunk, nlist, part, cand, idx, log_gate, score_lse);
   return check_launch("select_decode_merge");
 }
 

@@ -186,9 +186,10 @@ def test_decode_varlen_batch_and_ragged_tmax():
     run_decode_case(p, label="varlen")
 
 
-def test_decode_max_k():
-    run_decode_case(_edge_problem(64 * 200 + 3, 64, dtype="bf16", Hq=8, Hkv=2, d=128, ds=128),
-                    label="k=64")
+@pytest.mark.parametrize("T,k", [(64 * 200 + 3, 64), (64 * 3000 + 17, 64), (64 * 9000 + 1, 32)])
+def test_decode_large_k_and_many_chunks(T, k):
+    run_decode_case(_edge_problem(T, k, dtype="bf16", Hq=8, Hkv=2, d=128, ds=128, seed=T),
+                    label=f"T={T} k={k}")
 
 
 def test_decode_deterministic():
