@@ -10,7 +10,8 @@
 // Three kernels, no atomics (bitwise reproducible):
 //  1. pre-pass: D per query row; zero dlog_gate.
 //  2. Q-outer (one workgroup per tile x group, heads packed like the
-//     forward): recompute S^T = K Q^T, dP^T = V dO^T, dS^T; dQ^T += K^T dS^T.
+//     forward): recompute S^T = K Q^T, dP^T = V dO^T, dS^T; dQ^T += K^T dS^T
+//     (K^T read from the row-major K tile with the LDS transpose read).
 //  3. KV-outer (one workgroup per key block x group): the workgroup finds the
 //     tiles that selected its block (binary search in each later tile's
 //     ascending idx row) plus the diagonal tile, then for every such tile and
@@ -58,10 +59,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               uint16_t* __restrict__ dQ) {
   constexpr int NT = 128 * HPW;
   constexpr int KS = D / 16, CT = D / 32;
-  constexpr int RSTR = D + 8, TSTR = 64 + 8;
+  constexpr int RSTR = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * RSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[D * TSTR];
 
   const int nhc = G / HPW;
   const int t = n_tiles - 1 - static_cast<int>(blockIdx.x) / nhc;
@@ -104,8 +104,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     const int tok0 = blk * 64;
     __syncthreads();
-    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, Kt, tid);
-    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, Vs, nullptr, tid);
+    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, tid);
+    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, Vs, tid);
     __syncthreads();
 
     f32x16_t s[2], dp[2];
@@ -120,22 +120,31 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dp[tt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(&Vs[off])), db[ks], dp[tt]);
       }
     }
+    const float off = beta2 - lse2;
+    if (diag || !qvalid) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tok = 32 * tt + acc_row(v, hi);
-        const bool ok = qvalid && !(diag && tok > qloc);
-        const float p = ok ? exp2f(s[tt][v] * scale2 + beta2 - lse2) : 0.f;
-        s[tt][v] = p * (dp[tt][v] - Dv);  // dS^T
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int tok = 32 * tt + acc_row(v, hi);
+          const bool ok = qvalid && !(diag && tok > qloc);
+          const float p = ok ? fast_exp2(fmaf(s[tt][v], scale2, off)) : 0.f;
+          s[tt][v] = p * (dp[tt][v] - Dv);  // dS^T
+        }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          s[tt][v] = fast_exp2(fmaf(s[tt][v], scale2, off)) * (dp[tt][v] - Dv);
+    }
     // dQ^T (D x 32 queries) += K^T dS^T, k-step j = tokens 16j..16j+15
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const bf16x8_t bop = acc_to_bop(s, j);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        dq[ct] = mfma32x32x16(lds_aop_perm(&Kt[(32 * ct + l32) * TSTR], j, hi), bop, dq[ct]);
+        dq[ct] = mfma32x32x16(lds_aop_tr_perm(Ks, RSTR, 32 * ct, j, hi), bop, dq[ct]);
     }
   }
   if (qvalid) store_acc_col<CT>(dq, scale, dQ + qrow_i * D, hi);
@@ -148,9 +157,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 // V rows of the block are staged once in shared LDS (B operands of S = Q K^T
 // and dP = dO V^T).  For every tile that reads the block and every head, the
 // wave loads the tile's Q and dO rows straight into registers as A operands,
-// then writes them transposed into its own LDS region (the A operands of
-// dK^T += Q^T dS and dV^T += dO^T P), so the waves never wait for each other
-// between tiles.  dlog_gate partials are summed over waves at the end.
+// then copies them into its own LDS region, from which the LDS transpose read
+// yields the A operands of dK^T += Q^T dS and dV^T += dO^T P; the waves never
+// wait for each other between tiles.  dlog_gate partials are summed over
+// waves at the end.
 template <int D, int NWV>
 __global__ void __launch_bounds__(64 * NWV)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -162,11 +172,13 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NT = 64 * NWV;
   constexpr int KS = D / 16, CT = D / 32;
   constexpr int RSTR = D + 8;       // K/V row stride (bf16)
-  constexpr int TSTR = 32 + 8;      // transposed Q/dO row stride (32 queries)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[NWV][D * TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOt[NWV][D * TSTR];
+  // K rows then V rows; reused at the end for the cross-wave dK/dV sum
+  // (64 x D floats fit in 2 x 64 x (D + 8) bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * 64 * RSTR];
+  uint16_t* const Ks = KVs;
+  uint16_t* const Vs = KVs + 64 * RSTR;
+  __shared__ __attribute__((aligned(16))) uint16_t Qw[NWV][32 * RSTR];   // per wave: 32 query rows
+  __shared__ __attribute__((aligned(16))) uint16_t dOw[NWV][32 * RSTR];
   __shared__ int list_t[kMaxTileRows];
   __shared__ int list_slot[kMaxTileRows];
   __shared__ float dsum_s[NWV][kMaxTileRows];
@@ -225,8 +237,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- stage the block's K and V rows (B operands, shared by the waves)
   const int tok0 = 64 * m;
-  stage_rows<D, NT>(K + (grow * t_max + tok0) * D, S - tok0, Ks, nullptr, tid);
-  stage_rows<D, NT>(V + (grow * t_max + tok0) * D, S - tok0, Vs, nullptr, tid);
+  stage_rows<D, NT>(K + (grow * t_max + tok0) * D, S - tok0, Ks, tid);
+  stage_rows<D, NT>(V + (grow * t_max + tok0) * D, S - tok0, Vs, tid);
   __syncthreads();
 
   f32x16_t dk[2][CT], dv[2][CT];  // [token tile][channel tile]
@@ -237,8 +249,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       zero16(dk[tt][ct]);
       zero16(dv[tt][ct]);
     }
-  uint16_t* qt_s = Qt[wave];
-  uint16_t* dot_s = dOt[wave];
+  uint16_t* qt_s = Qw[wave];
+  uint16_t* dot_s = dOw[wave];
 
   for (int e = 0; e < n_list; ++e) {
     const int t = list_t[e], slot = list_slot[e];
@@ -279,35 +291,48 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             dp[tt] = mfma32x32x16(da[ks], as_bf16x8(*reinterpret_cast<const uint4*>(&Vs[off])), dp[tt]);
           }
         }
-        // transposed copies of this half tile's Q and dO into the wave's LDS
+        // this half tile's Q and dO rows into the wave's LDS (row-major; the
+        // dK/dV A operands read them back transposed)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 uq = __builtin_bit_cast(uint4, qa[ks]);
-          const uint4 ud = __builtin_bit_cast(uint4, da[ks]);
-          const uint32_t wq[4] = {uq.x, uq.y, uq.z, uq.w};
-          const uint32_t wd[4] = {ud.x, ud.y, ud.z, ud.w};
-#pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) {
-            const int c = 16 * ks + 8 * hi + e8;
-            qt_s[c * TSTR + l32] = static_cast<uint16_t>(wq[e8 >> 1] >> (16 * (e8 & 1)));
-            dot_s[c * TSTR + l32] = static_cast<uint16_t>(wd[e8 >> 1] >> (16 * (e8 & 1)));
-          }
+          *reinterpret_cast<uint4*>(&qt_s[l32 * RSTR + 16 * ks + 8 * hi]) = __builtin_bit_cast(uint4, qa[ks]);
+          *reinterpret_cast<uint4*>(&dot_s[l32 * RSTR + 16 * ks + 8 * hi]) = __builtin_bit_cast(uint4, da[ks]);
         }
         // P and dS (rows: queries, columns: this lane's token)
+        if (diag || nq < 64 || tok0 + 64 > S) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int tok = 32 * tt + l32;
-          const bool tok_ok = tok0 + tok < S;
+          for (int tt = 0; tt < 2; ++tt) {
+            const int tok = 32 * tt + l32;
+            const bool tok_ok = tok0 + tok < S;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int q = 32 * qt + acc_row(v, hi);
+              const bool ok = tok_ok && q < nq && !(diag && tok > q);
+              const float p = ok ? fast_exp2(fmaf(s[tt][v], scale2, beta2 - lse_w[wave][q])) : 0.f;
+              const float ds = p * (dp[tt][v] - dq_w[wave][q]);
+              s[tt][v] = p;
+              dp[tt][v] = ds;
+              dsum += ds;
+            }
+          }
+        } else {
+          float lo[16], dd[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int q = 32 * qt + acc_row(v, hi);
-            const bool ok = tok_ok && q < nq && !(diag && tok > q);
-            const float p = ok ? exp2f(fmaf(s[tt][v], scale2, beta2 - lse_w[wave][q])) : 0.f;
-            const float ds = p * (dp[tt][v] - dq_w[wave][q]);
-            s[tt][v] = p;
-            dp[tt][v] = ds;
-            dsum += ds;
+            lo[v] = beta2 - lse_w[wave][q];
+            dd[v] = dq_w[wave][q];
           }
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const float p = fast_exp2(fmaf(s[tt][v], scale2, lo[v]));
+              const float ds = p * (dp[tt][v] - dd[v]);
+              s[tt][v] = p;
+              dp[tt][v] = ds;
+              dsum += ds;
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
@@ -320,9 +345,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const bf16x8_t sb = acc_to_bop(&dp[tt], j);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-              const int c = 32 * ct + l32;
-              dv[tt][ct] = mfma32x32x16(lds_aop_perm(&dot_s[c * TSTR], j, hi), pb, dv[tt][ct]);
-              dk[tt][ct] = mfma32x32x16(lds_aop_perm(&qt_s[c * TSTR], j, hi), sb, dk[tt][ct]);
+              dv[tt][ct] = mfma32x32x16(lds_aop_tr_perm(dot_s, RSTR, 32 * ct, j, hi), pb, dv[tt][ct]);
+              dk[tt][ct] = mfma32x32x16(lds_aop_tr_perm(qt_s, RSTR, 32 * ct, j, hi), sb, dk[tt][ct]);
             }
           }
         }
@@ -341,7 +365,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dlg[(grow * n_tiles + list_t[e]) * k + list_slot[e]] = tot;
   }
   // ---- sum dK^T / dV^T over the waves (through LDS, wave by wave), store
-  float* red = reinterpret_cast<float*>(&Qt[0][0]);  // reuse: needs 64*D floats
+  float* red = reinterpret_cast<float*>(KVs);
   for (int which = 0; which < 2; ++which) {
     for (int w = 0; w < NWV; ++w) {
       __syncthreads();

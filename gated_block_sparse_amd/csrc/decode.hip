@@ -139,7 +139,7 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* _
       Vec16<T>::unpack(vr[i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = exp2f(z[i][h] - mh[h]);  // 0 for masked rows
+        const float p = fast_exp2(z[i][h] - mh[h]);  // 0 for masked rows
         lh[h] += p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];

@@ -15,8 +15,8 @@
 //    is one multiply per lane;
 //  * O^T += V^T P^T: P^T comes straight from the S^T accumulators of the lane
 //    (the 16 tokens of a k-step are taken in the order the accumulator layout
-//    holds them, and V^T is read in that same order), V is transposed while
-//    it is staged into LDS;
+//    holds them), and V^T is read in that same order from the row-major V
+//    tile with the LDS transpose read;
 //  * the log-gate is added per block; the diagonal block is masked j > i.
 #include "sas_device.h"
 #include "sas_internal.h"
@@ -24,55 +24,34 @@
 
 namespace sas {
 
-// Per-thread share of staging one 64-token block: K rows (16-byte chunks)
-// and V row pairs (transposed on the way into LDS).
+// Per-thread share of staging one 64-token block: K and V rows, as 16-byte
+// chunks copied row-major into LDS (V is read back transposed by the LDS
+// transpose read, so no shuffling is needed on the way in).
 template <int D, int NT>
 struct BlockStage {
-  static constexpr int KTOT = 64 * (D / 8);          // 16-byte K chunks per block
-  static constexpr int VTOT = 32 * (D / 8);          // V row pairs per block
-  static constexpr int KCH = (KTOT + NT - 1) / NT;   // per thread
-  static constexpr int VCH = (VTOT + NT - 1) / NT;
-  uint4 k[KCH];
-  uint4 v0[VCH], v1[VCH];
+  static constexpr int TOT = 64 * (D / 8);           // 16-byte chunks per tensor
+  static constexpr int CH = (TOT + NT - 1) / NT;     // per thread
+  uint4 k[CH], v[CH];
 
   __device__ __forceinline__ void load(const uint16_t* Kb, const uint16_t* Vb, int valid, int tid) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
-      k[i] = (c < KTOT && row < valid)
-                 ? *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(row) * D + cc * 8)
-                 : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int p = tid + i * NT, tp = p % 32, cc = p / 32, r0 = 2 * tp;
-      const bool in = p < VTOT;
-      v0[i] = (in && r0 < valid)
-                  ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(r0) * D + cc * 8)
-                  : make_uint4(0, 0, 0, 0);
-      v1[i] = (in && r0 + 1 < valid)
-                  ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(r0 + 1) * D + cc * 8)
-                  : make_uint4(0, 0, 0, 0);
+      const bool ok = c < TOT && row < valid;
+      k[i] = ok ? *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(row) * D + cc * 8)
+                : make_uint4(0, 0, 0, 0);
+      v[i] = ok ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(row) * D + cc * 8)
+                : make_uint4(0, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vt, int tid) const {
-    constexpr int RSTR = D + 8, TSTR = 64 + 8;
+  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vs, int tid) const {
+    constexpr int RSTR = D + 8;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
-      if (c < KTOT) *reinterpret_cast<uint4*>(&Ks[row * RSTR + cc * 8]) = k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int p = tid + i * NT, tp = p % 32, cc = p / 32;
-      if (p >= VTOT) continue;
-      const uint32_t w0[4] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w};
-      const uint32_t w1[4] = {v1[i].x, v1[i].y, v1[i].z, v1[i].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (w0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t hi = (w1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&Vt[(cc * 8 + e) * TSTR + 2 * tp]) = lo | (hi << 16);
+      if (c < TOT) {
+        *reinterpret_cast<uint4*>(&Ks[row * RSTR + cc * 8]) = k[i];
+        *reinterpret_cast<uint4*>(&Vs[row * RSTR + cc * 8]) = v[i];
       }
     }
   }
@@ -89,9 +68,8 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
   constexpr int CT = D / 32;         // channel tiles of O^T
   constexpr int KSTR = D + 8;        // K row stride in LDS (bf16), +16 bytes
-  constexpr int VSTR = 64 + 8;       // V^T row stride in LDS (bf16), +16 bytes
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * KSTR];
   __shared__ int s_blk[kMaxTopK + 1];
   __shared__ float s_beta[kMaxTopK + 1];
   __shared__ int s_nblk;
@@ -147,7 +125,7 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   {
     const int tok0 = s_blk[0] * 64;
     stg.load(Kg + static_cast<size_t>(tok0) * D, Vg + static_cast<size_t>(tok0) * D, S - tok0, tid);
-    stg.store(Ks[0], Vt[0], tid);
+    stg.store(Ks[0], Vs[0], tid);
   }
   __syncthreads();
 
@@ -160,7 +138,7 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       stg.load(Kg + static_cast<size_t>(tok1) * D, Vg + static_cast<size_t>(tok1) * D, S - tok1, tid);
     }
     const uint16_t* Kc = Ks[buf];
-    const uint16_t* Vc = Vt[buf];
+    const uint16_t* Vc = Vs[buf];
 
     // S^T (64 tokens x 32 queries) = K Q^T
     f32x16_t s[2];
@@ -187,25 +165,31 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[tt][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale2 + beta2);
-    const float alpha = exp2f(m_run - m_new);
-    const float off = beta2 - m_new;
+    // Lazy rescaling: the running max only moves (and the accumulators are
+    // only rescaled) when some lane's max grew by more than 2^8; otherwise the
+    // probabilities are taken against the stale max, which bounds them by 256.
+    const float m_cand = fmaxf(m_run, mx * scale2 + beta2);
+    if (__any(!(m_cand - m_run <= 8.f))) {
+      const float alpha = exp2f(m_run - m_cand);
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
+      m_run = m_cand;
+    }
+    const float off = beta2 - m_run;
     float ls = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(fmaf(s[tt][v], scale2, off));
+        const float p = fast_exp2(fmaf(s[tt][v], scale2, off));
         s[tt][v] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
+    l_run += ls;
 
     // O^T (D channels x 32 queries) += V^T P^T, k-step j = tokens 16j..16j+15
 #pragma unroll
@@ -213,9 +197,9 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const bf16x8_t pb = acc_to_bop(s, j);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        acc[ct] = mfma32x32x16(lds_aop_perm(&Vc[(32 * ct + l32) * VSTR], j, hi), pb, acc[ct]);
+        acc[ct] = mfma32x32x16(lds_aop_tr_perm(Vc, KSTR, 32 * ct, j, hi), pb, acc[ct]);
     }
-    if (it + 1 < nblk) stg.store(Ks[buf ^ 1], Vt[buf ^ 1], tid);
+    if (it + 1 < nblk) stg.store(Ks[buf ^ 1], Vs[buf ^ 1], tid);
     __syncthreads();
   }
 

@@ -45,6 +45,10 @@ template <> __device__ __forceinline__ void store_scalar<uint16_t>(uint16_t* p, 
   *p = static_cast<uint16_t>(u >> 16);
 }
 
+// 2^x with the hardware transcendental (v_exp_f32, about 1 ulp; results below
+// the normal range flush to 0, which is what a softmax wants).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ int clamp_len(int T, int t_max) {
   return T < 1 ? 1 : (T > t_max ? t_max : T);
 }

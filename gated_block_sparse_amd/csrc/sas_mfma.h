@@ -34,52 +34,55 @@ __device__ __forceinline__ int acc_row(int v, int hi) { return 8 * (v >> 2) + 4 
 // B operand for a contraction over the 32 rows of two accumulator tiles:
 // k-step j (0..3) takes the 16 rows 16j..16j+15 in the order the lane holds
 // them (elements 8*(j%2) .. +8 of tile j/2).  The matching A operand reads
-// rows 16j + 4*hi + {0..3} and 16j + 8 + 4*hi + {0..3}.
+// rows 16j + 4*hi + {0..3} and 16j + 8 + 4*hi + {0..3} (lds_aop_tr_perm).
 __device__ __forceinline__ bf16x8_t acc_to_bop(const f32x16_t* tiles, int j) {
   bf16x8_t r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = static_cast<__bf16>(tiles[j >> 1][8 * (j & 1) + e]);
   return r;
 }
-// The matching A operand from a [M][stride] bf16 LDS matrix whose columns are
-// the contraction rows: row = M index of this lane, k-step j.
-__device__ __forceinline__ bf16x8_t lds_aop_perm(const uint16_t* row, int j, int hi) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(row + 16 * j + 4 * hi);
-  const uint2 up = *reinterpret_cast<const uint2*>(row + 16 * j + 8 + 4 * hi);
-  return as_bf16x8(make_uint4(lo.x, lo.y, up.x, up.y));
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
+// lanes, lane j supplies an 8-byte chunk C_j; lane 4a+b receives element b of
+// C_a, C_{a+4}, C_{a+8}, C_{a+12} (layout checked on the GPU).  So if lane j
+// points at row k0 + j/4, columns c0 + 4*(j%4) of a row-major matrix, lane t
+// of the group receives rows k0..k0+3 of column c0 + t.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_t*)((__attribute__((address_space(3))) uint16_t*)p));
+  return __builtin_bit_cast(uint2, v);
+}
+// A operand of v_mfma_f32_32x32x16_bf16 whose M index is a COLUMN of a
+// row-major LDS matrix X (row stride rs, K along the rows): lane (l32, hi)
+// gets column i0 + l32, K elements 0-3 from rows k0..k0+3 and 4-7 from rows
+// k1..k1+3 (callers pass per-lane k0/k1 that depend on hi).
+__device__ __forceinline__ bf16x8_t lds_aop_tr(const uint16_t* X, int rs, int i0, int k0, int k1) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, jj = lane & 15;
+  const int col = i0 + 16 * (g & 1) + 4 * (jj & 3);
+  const int ro = jj >> 2;
+  const uint2 a = lds_read_tr16(X + (k0 + ro) * rs + col);
+  const uint2 b = lds_read_tr16(X + (k1 + ro) * rs + col);
+  return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
+}
+// The A operand matching acc_to_bop(tiles, j): rows 16j + 4hi + {0..3} and
+// 16j + 8 + 4hi + {0..3} of a row-major LDS matrix, column i0 + l32.
+__device__ __forceinline__ bf16x8_t lds_aop_tr_perm(const uint16_t* X, int rs, int i0, int j, int hi) {
+  return lds_aop_tr(X, rs, i0, 16 * j + 4 * hi, 16 * j + 8 + 4 * hi);
 }
 
-// Stage a 64-row block of a row-major [rows][D] bf16 matrix into LDS twice:
-// row-major (stride D+8) and transposed (stride 64+8).  Rows at or beyond
-// `valid` read as zero.  Every thread of the block participates.
+// Stage a 64-row block of a row-major [rows][D] bf16 matrix into LDS
+// (row stride D+8).  Rows at or beyond `valid` read as zero.  Every thread of
+// the block participates.
 template <int D, int NT>
 __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int valid,
-                                           uint16_t* rm, uint16_t* tr, int tid) {
-  constexpr int RSTR = D + 8, TSTR = 64 + 8;
-  if (rm) {
-    for (int c = tid; c < 64 * (D / 8); c += NT) {
-      const int row = c / (D / 8), cc = c % (D / 8);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (row < valid) u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D + cc * 8);
-      *reinterpret_cast<uint4*>(&rm[row * RSTR + cc * 8]) = u;
-    }
-  }
-  if (tr) {
-    for (int p = tid; p < 32 * (D / 8); p += NT) {
-      const int tp = p % 32, cc = p / 32;
-      const int r0 = 2 * tp;
-      uint4 u0 = make_uint4(0, 0, 0, 0), u1 = make_uint4(0, 0, 0, 0);
-      if (r0 < valid) u0 = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0) * D + cc * 8);
-      if (r0 + 1 < valid) u1 = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0 + 1) * D + cc * 8);
-      const uint32_t w0[4] = {u0.x, u0.y, u0.z, u0.w};
-      const uint32_t w1[4] = {u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = (w0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t b = (w1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        *reinterpret_cast<uint32_t*>(&tr[(cc * 8 + e) * TSTR + r0]) = a | (b << 16);
-      }
-    }
+                                           uint16_t* rm, int tid) {
+  constexpr int RSTR = D + 8;
+  for (int c = tid; c < 64 * (D / 8); c += NT) {
+    const int row = c / (D / 8), cc = c % (D / 8);
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (row < valid) u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D + cc * 8);
+    *reinterpret_cast<uint4*>(&rm[row * RSTR + cc * 8]) = u;
   }
 }
 
