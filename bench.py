@@ -8,16 +8,21 @@ dim 128, synthetic seeded inputs.  A step is the whole decode-time path:
 
   1. sas_block_summaries on the newest complete block (the steady-state
      refresh; it is due once every 64 steps, run here every step),
-  2. sas_select (selector score over every history-block summary, softmax-gate
-     LSE, Top-K),
-  3. sas_decode_fwd (split-KV gated attention over the selected blocks + B0,
-     then the LSE merge).
+  2. sas_decode_step: selector score over every history-block summary,
+     softmax-gate LSE, Top-K, then split-KV gated attention over the selected
+     blocks + B0 and the LSE merge (the selection's final merge runs inside
+     the attention's split kernel).
+
+The same step is also timed through the separate entry points (sas_select,
+then sas_decode_fwd) for the per-op breakdown; the two give identical
+outputs (checked before timing).  The roofline figure is sas_decode_fwd's.
 
 Inputs are resident in HBM before timing starts.  Each timed step is
 bracketed by HIP events on the stream the library launches on; between steps
-(outside the events) a 512 MiB write evicts the 256 MB Infinity Cache and the
-L2, so every step reads its bytes from HBM.  ``--workload qwen3_4b_prefill_16k``
-times the training-style prefill forward + backward instead.
+(outside the events) a 512 MiB write and a 1 GiB read sweep evict the L2s and
+the 256 MB Infinity Cache, so every step reads its bytes from HBM.
+``--workload qwen3_4b_prefill_16k`` times the training-style prefill forward +
+backward instead.
 
 Extra fields beside the contract keys: ``breakdown_us`` (per-op medians),
 ``roofline`` for the dominant kernel, ``cpu_baseline`` (the float64 CPU
@@ -52,9 +57,67 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample")
     ap.add_argument("--no-flush", action="store_true", help="hot-cache timing only")
+    ap.add_argument("--no-hot", action="store_true",
+                    help="skip the hot-cache HIP-graph figure (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for PMC byte calibration)")
     return ap.parse_args()
+
+
+DECODE_KERNELS = ("sas::decode_split_kernel", "sas::decode_merge_kernel")
+PREFILL_KERNELS = ("sas::prefill_fwd_kernel",)
+
+
+def measured_traffic(workload, prefixes):
+    """HBM bytes per launch of the roofline kernel(s), from the committed
+    PMC summary of this workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
+    None when there is none or a kernel source changed since it was taken."""
+    from gated_block_sparse_amd import profsum
+    blob = profsum.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"))
+    if blob is None:
+        return None
+    tot, hit = 0, False
+    for name, v in blob["kernels"].items():
+        if name.startswith(prefixes):
+            tot += v["fetch_bytes"] + v["write_bytes"]
+            hit = True
+    return tot if hit else None
+
+
+class CacheFlush:
+    """Evicts the L2s and the 256 MB Infinity Cache between timed steps: a
+    512 MiB scratch write, then a 1 GiB read sweep.  The read sweep matters:
+    after the write alone the Infinity Cache holds ~256 MB of dirty lines,
+    whose write-back then competes with the next timed kernel's reads (a
+    64 MB cold streaming read measured 26 us after a write flush against
+    15 us after a read sweep and 13 us hot).  A decode step in a model never
+    follows such a write burst, so the sweep is what makes the figure cold
+    without that artefact."""
+    LABEL = "cold (L2 + Infinity Cache evicted: 512 MiB write, then 1 GiB read sweep)"
+
+    def __init__(self, dev):
+        import torch
+        self.w = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        self.r = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self, i):
+        import torch
+        self.w.fill_(float(i))
+        torch.amax(self.r, dim=0, out=self.out)
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy: the known-size reference that the
+    PMC byte counters are scaled by."""
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    bb = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    bb.copy_(a)
+    torch.cuda.synchronize()
+    return {"read": a.numel() * 4, "write": bb.numel() * 4}
 
 
 def _pct(xs, q):
@@ -129,7 +192,28 @@ def run_decode(args, wl):
              lg.data_ptr(), scale, o.data_ptr(), lse.data_ptr(), ws_dec.data_ptr(),
              ws_dec.numel(), sp)
 
+    ws_step = torch.empty(max(1, S.sas_workspace_bytes(S.SAS_OP_DECODE_STEP, dims)), dtype=torch.uint8, device=dev)
+    idx2, lg2, slse2 = torch.empty_like(idx), torch.empty_like(lg), torch.empty_like(slse)
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    a_step = (pd, q.data_ptr(), K.data_ptr(), V.data_ptr(), lens.data_ptr(), Wq.data_ptr(),
+              summ.data_ptr(), 1, scale, idx2.data_ptr(), lg2.data_ptr(), slse2.data_ptr(),
+              o2.data_ptr(), lse2.data_ptr(), ws_step.data_ptr(), ws_step.numel(), sp)
+
+    def step_fused(evs=None):
+        """The production step: refresh + the fused selection/attention."""
+        if evs:
+            evs[0].record(stream)
+        st = lib.sas_block_summaries(*a_sum)
+        if evs:
+            evs[1].record(stream)
+        st |= lib.sas_decode_step(*a_step)
+        if evs:
+            evs[2].record(stream)
+        if st:
+            raise S.SasError(st, lib.sas_last_error().decode())
+
     def step(evs=None):
+        """The same step through the separate entry points (per-op timing)."""
         if evs:
             evs[0].record(stream)
         st = lib.sas_block_summaries(*a_sum)
@@ -144,10 +228,13 @@ def run_decode(args, wl):
         if st:
             raise S.SasError(st, lib.sas_last_error().decode())
 
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = CacheFlush(dev)
     for _ in range(args.warmup):
         step()
+        step_fused()
     torch.cuda.synchronize()
+    if not (torch.equal(o, o2) and torch.equal(idx, idx2) and torch.equal(lse, lse2)):
+        raise RuntimeError("fused decode step differs from select + decode_fwd")
 
     K_steps = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
@@ -155,7 +242,7 @@ def run_decode(args, wl):
     t0 = time.perf_counter()
     for i in range(K_steps):
         if not args.no_flush:
-            flush.fill_(float(i))          # evict MALL/L2; also covers host launch latency
+            flush(i)          # evict MALL/L2; also covers host launch latency
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -164,18 +251,41 @@ def run_decode(args, wl):
     t_sel = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
     t_dec = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
 
+    # the fused production step, cold the same way
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    for i in range(K_steps):
+        if not args.no_flush:
+            flush(i)
+        step_fused(evf[i])
+    torch.cuda.synchronize()
+    tot_f = [e[0].elapsed_time(e[2]) * 1e3 for e in evf]
+    t_fused = [e[1].elapsed_time(e[2]) * 1e3 for e in evf]
+
+    # hot-cache figures: the same steps with no eviction in between
+    evh = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
+    for i in range(K_steps):
+        step(evh[i])
+    evhf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    for i in range(K_steps):
+        step_fused(evhf[i])
+    torch.cuda.synchronize()
+    hot_step = statistics.median([e[0].elapsed_time(e[2]) * 1e3 for e in evhf])
+    hot_step_unfused = statistics.median([e[0].elapsed_time(e[3]) * 1e3 for e in evh])
+    hot_dec = statistics.median([e[2].elapsed_time(e[3]) * 1e3 for e in evh])
+
     # hot-cache figure: the same step replayed back to back from a HIP graph
     hot_us = None
     try:
+        if args.no_hot:
+            raise RuntimeError("--no-hot")
         g = torch.cuda.CUDAGraph()
         s2 = torch.cuda.Stream()
         s2.wait_stream(stream)
         with torch.cuda.stream(s2):
             sp2 = s2.cuda_stream
-            a2 = [a[:-1] + (sp2,) for a in (a_sum, a_sel, a_dec)]   # the stream is the last argument
+            a2 = [a[:-1] + (sp2,) for a in (a_sum, a_step)]   # the stream is the last argument
             g.capture_begin()
-            sts = [lib.sas_block_summaries(*a2[0]), lib.sas_select(*a2[1]),
-                   lib.sas_decode_fwd(*a2[2])]
+            sts = [lib.sas_block_summaries(*a2[0]), lib.sas_decode_step(*a2[1])]
             g.capture_end()
         if any(sts):
             raise S.SasError(max(sts), lib.sas_last_error().decode())
@@ -192,11 +302,12 @@ def run_decode(args, wl):
         torch.cuda.synchronize()
         hot_us = e0.elapsed_time(e1) * 1e3 / n_hot
     except Exception as exc:  # graph capture is a reported extra, never the headline
-        print(f"# hot-cache graph timing skipped: {exc}", file=sys.stderr)
+        if not args.no_hot:
+            print(f"# hot-cache graph timing skipped: {exc}", file=sys.stderr)
 
     by = decode_bytes(wl, p.seq_lens)
     med = statistics.median
-    us_step, us_dec = med(tot), med(t_dec)
+    us_step, us_dec = med(tot_f), med(t_dec)
     achieved = by["attention"] / (us_dec * 1e-6) / 1e9
     res = {
         "metric": "SAS decode attn us/step + achieved HBM GB/s (% peak), Qwen3-4B shape @64K",
@@ -213,20 +324,27 @@ def run_decode(args, wl):
         "data": "synthetic (seeded N(0,1) q/K/V, K x U(0.5,2) per channel; random selector weights)",
         "config": {"workload": wl.name, "batch": B, "context": [int(x) for x in p.seq_lens][:8],
                    "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": d, "sel_dim": ds,
-                   "block": 64, "top_k": k, "cache": "hot" if args.no_flush else "cold (MALL+L2 flushed)"},
+                   "block": 64, "top_k": k, "cache": "hot" if args.no_flush else CacheFlush.LABEL},
         "tokens_per_s": round(B / (us_step * 1e-6), 1),
         "breakdown_us": {
             "summary_refresh": {"median": round(med(t_sum), 3)},
             "select": {"median": round(med(t_sel), 3), "p10": round(_pct(t_sel, .1), 3), "p90": round(_pct(t_sel, .9), 3)},
             "decode_attention": {"median": round(us_dec, 3), "p10": round(_pct(t_dec, .1), 3), "p90": round(_pct(t_dec, .9), 3)},
-            "step": {"median": round(us_step, 3), "p10": round(_pct(tot, .1), 3), "p90": round(_pct(tot, .9), 3)},
+            "select_and_attention_fused": {"median": round(med(t_fused), 3), "p10": round(_pct(t_fused, .1), 3), "p90": round(_pct(t_fused, .9), 3)},
+            "step": {"median": round(us_step, 3), "p10": round(_pct(tot_f, .1), 3), "p90": round(_pct(tot_f, .9), 3)},
+            "step_unfused": {"median": round(med(tot), 3), "p10": round(_pct(tot, .1), 3), "p90": round(_pct(tot, .9), 3)},
+            "step_hot": round(hot_step, 3),
+            "step_unfused_hot": round(hot_step_unfused, 3),
+            "decode_attention_hot": round(hot_dec, 3),
             "step_hot_graph": None if hot_us is None else round(hot_us, 3),
         },
         "bytes": by,
         "step_GBps": round(by["step"] / (us_step * 1e-6) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "sas_decode_fwd (split-KV + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name, DECODE_KERNELS),
+                     "algorithmic_bytes": by["attention"]},
         "wall_s_timed_region": round(wall, 3),
     }
     return res, p
@@ -278,7 +396,7 @@ def run_prefill(args, wl):
     bwd_flop = 10.0 * d * pairs
 
     stream = torch.cuda.current_stream()
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = CacheFlush(dev)
     dims = Sb.make_dims(B, Hq, Hkv, d, ds, k, S, Sb.SAS_BF16)
     ws_sel = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_SELECT_TILES, dims, S)), dtype=torch.uint8, device=dev)
     ws_fwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_PREFILL_FWD, dims, S)), dtype=torch.uint8, device=dev)
@@ -304,7 +422,7 @@ def run_prefill(args, wl):
     t0 = time.perf_counter()
     for i in range(n):
         if not args.no_flush:
-            flush.fill_(float(i))
+            flush(i)
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -326,7 +444,7 @@ def run_prefill(args, wl):
         "data": "synthetic (seeded N(0,1) Q/K/V/dO, random selector weights)",
         "config": {"workload": wl.name, "batch": B, "seq_len": S, "n_q_heads": Hq,
                    "n_kv_heads": Hkv, "head_dim": d, "sel_dim": ds, "block": 64, "top_k": k,
-                   "cache": "hot" if args.no_flush else "cold (MALL+L2 flushed)"},
+                   "cache": "hot" if args.no_flush else CacheFlush.LABEL},
         "tokens_per_s": round(B * S / (us_step * 1e-6), 1),
         "breakdown_us": {
             "summaries_and_select": round(med(t_sel), 2),
@@ -337,7 +455,11 @@ def run_prefill(args, wl):
         "bwd_TFLOPs": round(bwd_tf, 1),
         "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel (sas_prefill_fwd)",
                      "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name, PREFILL_KERNELS)},
+        "roofline_bwd": {"bound": "mfma", "kernel": "sas_bwd (pre-pass, dQ, dK/dV kernels)",
+                         "achieved": round(bwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4)},
         "wall_s_timed_region": round(wall, 3),
     }
     return res, p
@@ -428,6 +550,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if wl.mode != "decode":
         res, p = run_prefill(args, wl)
+        if args.calibrate_copy:
+            res["copy_calibration_bytes"] = calibrate_copy()
         if not args.no_cpu_baseline:
             us, done, n_tiles = cpu_baseline_prefill(p, args.cpu_seconds)
             res["cpu_baseline"] = {
@@ -440,14 +564,7 @@ def main():
         return
     res, p = run_decode(args, wl)
     if args.calibrate_copy:
-        import torch
-        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
-        bb = torch.empty_like(a)
-        a.fill_(1.0)
-        torch.cuda.synchronize()
-        bb.copy_(a)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = {"read": a.numel() * 4, "write": bb.numel() * 4}
+        res["copy_calibration_bytes"] = calibrate_copy()
     if not args.no_cpu_baseline:
         us, n = cpu_baseline_decode(p, args.cpu_seconds)
         res["cpu_baseline"] = {

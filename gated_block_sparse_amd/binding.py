@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libsas.so")
 SAS_OK, SAS_ERR_INVALID_ARGUMENT, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE_TOO_SMALL, SAS_ERR_HIP = range(5)
 SAS_F32, SAS_BF16 = 0, 1
 SAS_SELECT_DECODE, SAS_SELECT_TILES = 0, 1
-SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD = range(5)
+(SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD,
+ SAS_OP_DECODE_STEP) = range(6)
 BLOCK = 64
 SIZE_MAX = 2 ** 64 - 1
 
@@ -43,6 +44,8 @@ _SIGNATURES = {
     "sas_block_summaries": (_i32, [_PD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "sas_select": (_i32, [_PD, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sas_decode_fwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sas_decode_step": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _sz, _vp]),
     "sas_prefill_fwd": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sas_bwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
                        _vp, _vp, _sz, _vp]),
@@ -196,6 +199,36 @@ def sas_decode_fwd(q, K, V, seq_lens, idx, log_gate, scale=None, o=None, lse=Non
                                          _ptr(seq_lens), _ptr(idx), _ptr(log_gate), scale, _ptr(o),
                                          _ptr(lse), _ptr(ws), ws_bytes, _stream()))
     return o, lse
+
+
+def sas_decode_step(q, K, V, seq_lens, Wq_sel, summ, top_k, gated=True, scale=None, idx=None,
+                    log_gate=None, score_lse=None, o=None, lse=None, ws=None, want_lse=True):
+    """Fused selection + gated sparse decode attention (the outputs of
+    sas_select(SAS_SELECT_DECODE) followed by sas_decode_fwd).  q [B,Hq,d];
+    K,V [B,Hkv,t_max,d]; summ [B,Hkv,t_max//64,d_sel].
+    Returns (idx, log_gate, score_lse, o, lse | None)."""
+    B, Hq, d = q.shape
+    _, Hkv, t_max, _ = K.shape
+    ds = summ.shape[-1]
+    dims = make_dims(B, Hq, Hkv, d, ds, top_k, t_max, _dtype_code(q))
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dev = q.device
+    if idx is None:
+        idx = torch.empty(B, Hkv, 1, top_k, dtype=torch.int32, device=dev)
+    if log_gate is None:
+        log_gate = torch.empty(B, Hkv, 1, top_k, dtype=torch.float32, device=dev)
+    if score_lse is None:
+        score_lse = torch.empty(B, Hkv, 1, dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(SAS_OP_DECODE_STEP, dims, 0, ws, dev)
+    _check(load_library().sas_decode_step(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
+                                          _ptr(seq_lens), _ptr(Wq_sel), _ptr(summ), int(gated),
+                                          scale, _ptr(idx), _ptr(log_gate), _ptr(score_lse),
+                                          _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream()))
+    return idx, log_gate, score_lse, o, lse
 
 
 def sas_prefill_fwd(Q, K, V, idx, log_gate, scale=None, seq_len=None, O=None, lse=None, ws=None):

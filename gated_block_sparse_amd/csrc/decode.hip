@@ -5,18 +5,21 @@
 //         gate is not passed: the inference rule of SAS close reading 2.1/2.3)
 //   o_h = softmax(z) V,  lse_h = LSE(z)
 //
-// Split-KV: the unit of work is one 64-token block of one (sequence, group):
-// the k selected history blocks plus B0.  A workgroup streams its block's K
-// and V once (16-byte loads, every load instruction covers whole 256-byte
-// rows), applies it to all G query heads of the group (each K/V byte serves G
-// heads), and leaves an unnormalised partial softmax state (max, sum, acc) in
-// the workspace.  A second, small kernel merges the k+1 partials of each head
+// Split-KV: the unit of work is one or two 64-token blocks of one (sequence,
+// group), taken from the k selected history blocks plus B0 (slot k).  A
+// workgroup issues every K and V load of its unit at once (16-byte loads,
+// every load instruction covers whole 256-byte rows), applies them to all G
+// query heads of the group (each K/V byte serves G heads), and leaves an
+// unnormalised partial softmax state (max, sum, acc) in the workspace.  Two
+// blocks per unit are used once the grid has enough units to fill the chip:
+// twice the bytes in flight per thread and half the partials to merge.  A second, small kernel merges the k+1 partials of each head
 // in slot order:  o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u,  issuing
 // all of its loads at once; the kernel boundary orders the two, so no
 // device-wide fences or atomics are needed and results are bitwise
 // reproducible.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "sas_select_dev.h"
 
 namespace sas {
 
@@ -29,75 +32,70 @@ template <int G, int D> struct DecPartial {
   static constexpr int kFloats = G * (D + 2);
 };
 
-template <typename T, int D, int G>
-__global__ void __launch_bounds__(kDecThreads)
-decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
-                  const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
-                  const float* __restrict__ log_gate, float scale2, int Hkv, int t_max, int k,
-                  float* __restrict__ part) {
+// Shared memory of one split unit: cross-wave max, sum and accumulators.
+template <int G, int D> struct SplitLds {
+  float m[4][G];
+  float l[4][G];
+  float acc[4][G][D];
+};
+
+// Attention over the (up to NB) blocks of one unit, all G heads of group
+// `row`: writes the unit's partial state to `out`.  Every thread of the
+// workgroup calls it.
+template <typename T, int D, int G, int NB>
+__device__ __forceinline__ void split_unit(const T* __restrict__ q, const T* __restrict__ K,
+                                           const T* __restrict__ V, size_t row, int t_max,
+                                           const int* start, const int* ntok, const float* beta2,
+                                           float scale2, float* __restrict__ out,
+                                           SplitLds<G, D>& sh) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
   constexpr int LPR = D / EPL;          // lanes per row
   constexpr int RPI = 64 / LPR;         // rows per wave load instruction
-  constexpr int NI = 16 / RPI;          // loads per wave per tensor (16 tokens per wave)
+  constexpr int NI = 16 / RPI;          // loads per wave per tensor per block (16 tokens per wave)
   constexpr int PF = DecPartial<G, D>::kFloats;
-  __shared__ float red_m[4][G];
-  __shared__ float red_l[4][G];
-  __shared__ float red_acc[4][G][D];
-
-  const int u = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int len = clamp_len(seq_lens[b], t_max);
-  const int C = (len - 1) / kBlock;
-  const size_t row = static_cast<size_t>(b) * Hkv + r;
-  float* out = part + (row * (k + 1) + u) * static_cast<size_t>(PF);
-
-  int start = 0, ntok = 0;
-  float beta2 = 0.f;  // bias, already multiplied by log2(e)
-  if (u < k) {
-    const int m = idx[row * k + u];
-    if (m >= 0) {
-      start = m * kBlock;
-      ntok = kBlock;
-      if (log_gate) beta2 = log_gate[row * k + u] * kLog2e;
-    }
-  } else {
-    start = C * kBlock;
-    ntok = len - start;
-  }
-
-  if (ntok == 0) {  // empty slot: a neutral partial
+  int tot = 0;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) tot += ntok[bb];
+  if (tot == 0) {  // only empty slots: a neutral partial
     for (int x = tid; x < PF; x += kDecThreads) out[x] = (x >= G * D && x < G * D + G) ? -INFINITY : 0.f;
-  } else {
-    const int col = lane % LPR, rsub = lane / LPR;
-    const T* Kb = K + (row * t_max + start) * static_cast<size_t>(D) + col * EPL;
-    const T* Vb = V + (row * t_max + start) * static_cast<size_t>(D) + col * EPL;
-    uint4 kr[NI], vr[NI];
+    return;
+  }
+  const int col = lane % LPR, rsub = lane / LPR;
+  uint4 kr[NB][NI], vr[NB][NI];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const T* Kb = K + (row * t_max + start[bb]) * static_cast<size_t>(D) + col * EPL;
+    const T* Vb = V + (row * t_max + start[bb]) * static_cast<size_t>(D) + col * EPL;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int j = wave * 16 + i * RPI + rsub;
-      if (j < ntok) {
-        kr[i] = *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(j) * D);
-        vr[i] = *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(j) * D);
+      if (j < ntok[bb]) {
+        kr[bb][i] = *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(j) * D);
+        vr[bb][i] = *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(j) * D);
       } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
+        kr[bb][i] = make_uint4(0, 0, 0, 0);
+        vr[bb][i] = make_uint4(0, 0, 0, 0);
       }
     }
-    float qv[G][EPL];
-    {
-      const T* qb = q + (row * G) * static_cast<size_t>(D) + col * EPL;
+  }
+  float qv[G][EPL];
+  {
+    const T* qb = q + (row * G) * static_cast<size_t>(D) + col * EPL;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        uint4 raw = *reinterpret_cast<const uint4*>(qb + h * D);
-        Vec16<T>::unpack(raw, qv[h]);
-      }
+    for (int h = 0; h < G; ++h) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qb + h * D);
+      Vec16<T>::unpack(raw, qv[h]);
     }
-    // logits (base-2 domain)
-    float z[NI][G];
+  }
+  // logits (base-2 domain)
+  float z[NB][NI][G];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPL];
-      Vec16<T>::unpack(kr[i], kf);
+      Vec16<T>::unpack(kr[bb][i], kf);
       const int j = wave * 16 + i * RPI + rsub;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -105,151 +103,255 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* _
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot += qv[h][e] * kf[e];
         dot = group_sum(dot, LPR);
-        z[i][h] = (j < ntok) ? dot * scale2 + beta2 : -INFINITY;
+        z[bb][i][h] = (j < ntok[bb]) ? dot * scale2 + beta2[bb] : -INFINITY;
       }
     }
-    float mh[G];
+  float mh[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float v = z[0][h];
+  for (int h = 0; h < G; ++h) {
+    float v = -INFINITY;
 #pragma unroll
-      for (int i = 1; i < NI; ++i) v = fmaxf(v, z[i][h]);
-      mh[h] = wave_max_from(v, LPR);  // across the row groups
-    }
-    if (lane == 0) {
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-      for (int h = 0; h < G; ++h) red_m[wave][h] = mh[h];
-    }
-    __syncthreads();
+      for (int i = 0; i < NI; ++i) v = fmaxf(v, z[bb][i][h]);
+    mh[h] = wave_max_from(v, LPR);  // across the row groups
+  }
+  if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      mh[h] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    for (int h = 0; h < G; ++h) sh.m[wave][h] = mh[h];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    mh[h] = fmaxf(fmaxf(sh.m[0][h], sh.m[1][h]), fmaxf(sh.m[2][h], sh.m[3][h]));
 
-    float acc[G][EPL];
-    float lh[G];
+  float acc[G][EPL];
+  float lh[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      lh[h] = 0.f;
+  for (int h = 0; h < G; ++h) {
+    lh[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-    }
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPL];
-      Vec16<T>::unpack(vr[i], vf);
+      Vec16<T>::unpack(vr[bb][i], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(z[i][h] - mh[h]);  // 0 for masked rows
+        const float p = fast_exp2(z[bb][i][h] - mh[h]);  // 0 for masked rows
         lh[h] += p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];
       }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) lh[h] = wave_sum_from(lh[h], LPR);
-    // Sum acc over the RG = 64/LPR row groups of the wave with a transposed
-    // butterfly: each step halves the values a lane keeps, so lane group q
-    // ends up owning NV/RG distinct (head, element) sums.
-    constexpr int NV = G * EPL, RG = 64 / LPR;
-    float av[NV];
+  for (int h = 0; h < G; ++h) lh[h] = wave_sum_from(lh[h], LPR);
+  // Sum acc over the RG = 64/LPR row groups of the wave with a transposed
+  // butterfly: each step halves the values a lane keeps, so lane group q
+  // ends up owning NV/RG distinct (head, element) sums.
+  constexpr int NV = G * EPL, RG = 64 / LPR;
+  float av[NV];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) av[h * EPL + e] = acc[h][e];
-    int kept = NV;
+    for (int e = 0; e < EPL; ++e) av[h * EPL + e] = acc[h][e];
+  int kept = NV;
 #pragma unroll
-    for (int sft = 32; sft >= LPR; sft >>= 1) {
-      const uint32_t up = (lane & sft) ? 0xFFFFFFFFu : 0u;
-      const int half = kept / 2;
+  for (int sft = 32; sft >= LPR; sft >>= 1) {
+    const uint32_t up = (lane & sft) ? 0xFFFFFFFFu : 0u;
+    const int half = kept / 2;
 #pragma unroll
-      for (int j = 0; j < NV / 2; ++j) {
-        if (j < half) {
-          const uint32_t a = __float_as_uint(av[j]), bb = __float_as_uint(av[j + half]);
-          const float keep = __uint_as_float((bb & up) | (a & ~up));
-          const float send = __uint_as_float((a & up) | (bb & ~up));
-          av[j] = keep + __shfl_xor(send, sft, 64);
-        }
-      }
-      kept = half;
-    }
-    {
-      // lane's row group q = lane / LPR selects which block of NV/RG values it owns
-      const int q = lane / LPR;
-      int owner = 0;
-#pragma unroll
-      for (int bit = RG / 2, sft = 32; bit >= 1; bit >>= 1, sft >>= 1)
-        if (lane & sft) owner += bit;
-      (void)q;
-#pragma unroll
-      for (int j = 0; j < NV / RG; ++j) {
-        const int vi = owner * (NV / RG) + j;
-        red_acc[wave][vi / EPL][col * EPL + (vi % EPL)] = av[j];
+    for (int j = 0; j < NV / 2; ++j) {
+      if (j < half) {
+        const uint32_t a = __float_as_uint(av[j]), bb = __float_as_uint(av[j + half]);
+        const float keep = __uint_as_float((bb & up) | (a & ~up));
+        const float send = __uint_as_float((a & up) | (bb & ~up));
+        av[j] = keep + __shfl_xor(send, sft, 64);
       }
     }
-    if (lane == 0) {
+    kept = half;
+  }
+  {
+    // the lane's row group selects which block of NV/RG values it owns
+    int owner = 0;
 #pragma unroll
-      for (int h = 0; h < G; ++h) red_l[wave][h] = lh[h];
-    }
-    __syncthreads();
-    for (int x = tid; x < G * D; x += kDecThreads) {
-      const int h = x / D, c = x % D;
-      out[x] = red_acc[0][h][c] + red_acc[1][h][c] + red_acc[2][h][c] + red_acc[3][h][c];
-    }
-    if (tid < G) {
-      out[G * D + tid] = mh[tid];
-      out[G * D + G + tid] = red_l[0][tid] + red_l[1][tid] + red_l[2][tid] + red_l[3][tid];
+    for (int bit = RG / 2, sft = 32; bit >= 1; bit >>= 1, sft >>= 1)
+      if (lane & sft) owner += bit;
+#pragma unroll
+    for (int j = 0; j < NV / RG; ++j) {
+      const int vi = owner * (NV / RG) + j;
+      sh.acc[wave][vi / EPL][col * EPL + (vi % EPL)] = av[j];
     }
   }
-
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) sh.l[wave][h] = lh[h];
+  }
+  __syncthreads();
+  for (int x = tid; x < G * D; x += kDecThreads) {
+    const int h = x / D, c = x % D;
+    out[x] = sh.acc[0][h][c] + sh.acc[1][h][c] + sh.acc[2][h][c] + sh.acc[3][h][c];
+  }
+  if (tid < G) {
+    out[G * D + tid] = mh[tid];
+    out[G * D + G + tid] = sh.l[0][tid] + sh.l[1][tid] + sh.l[2][tid] + sh.l[3][tid];
+  }
 }
 
-// One workgroup per (sequence, group): thread x handles outputs x, x + 256 of
-// the group's G*D.  The partials are folded in slot order with the usual
-// online rescaling, loading BATCH slots at a time before using any of them.
-template <typename T, int D, int G>
+// Split kernel of sas_decode_fwd: the unit's blocks come from idx/log_gate.
+template <typename T, int D, int G, int NB>
 __global__ void __launch_bounds__(kDecThreads)
-decode_merge_kernel(int Hkv, int k, const float* __restrict__ part, T* __restrict__ o,
+decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
+                    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
+                    const float* __restrict__ log_gate, float scale2, int Hkv, int t_max, int k,
+                    float* __restrict__ part) {
+  constexpr int PF = DecPartial<G, D>::kFloats;
+  __shared__ SplitLds<G, D> sh;
+  const int unit = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int len = clamp_len(seq_lens[b], t_max);
+  const int C = (len - 1) / kBlock;
+  const size_t row = static_cast<size_t>(b) * Hkv + r;
+  const int n_units = (k + NB) / NB;   // ceil((k + 1) / NB)
+  // the NB slots of this unit: history slots u < k, then B0 as slot k
+  int start[NB], ntok[NB];
+  float beta2[NB];  // bias, already multiplied by log2(e)
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int u = unit * NB + bb;
+    start[bb] = 0;
+    ntok[bb] = 0;
+    beta2[bb] = 0.f;
+    if (u < k) {
+      const int m = idx[row * k + u];
+      if (m >= 0) {
+        start[bb] = m * kBlock;
+        ntok[bb] = kBlock;
+        if (log_gate) beta2[bb] = log_gate[row * k + u] * kLog2e;
+      }
+    } else if (u == k) {
+      start[bb] = C * kBlock;
+      ntok[bb] = len - start[bb];
+    }
+  }
+  split_unit<T, D, G, NB>(q, K, V, row, t_max, start, ntok, beta2, scale2,
+                          part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
+}
+
+// Split kernel of sas_decode_step: the selection of the row is finished here
+// from the per-chunk state of the selection's first stage (the same merge of
+// chunk (max, sum-exp) states and candidate lists as the selection's own
+// merge kernel, so the outputs are identical), then the unit attends its
+// blocks.  Unit 0 also stores the row's idx, log_gate and score_lse.
+template <typename T, int D, int G, int NB>
+__global__ void __launch_bounds__(kDecThreads)
+decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
+                           const T* __restrict__ V, const int32_t* __restrict__ seq_lens,
+                           const float2* __restrict__ cpart, const uint64_t* __restrict__ cand,
+                           int nchunk, int nlist, int kc, int gated, float scale2, int Hkv,
+                           int t_max, int k, int32_t* __restrict__ idx,
+                           float* __restrict__ log_gate, float* __restrict__ score_lse,
+                           float* __restrict__ part) {
+  constexpr int PF = DecPartial<G, D>::kFloats;
+  extern __shared__ uint64_t keys[];   // two buffers of nlist * kc keys
+  __shared__ SplitLds<G, D> sh;
+  __shared__ float red[kDecThreads / 64];
+  __shared__ int32_t sel_blk[kMaxTopK];
+  __shared__ float sel_lg[kMaxTopK];
+  const int unit = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int len = clamp_len(seq_lens[b], t_max);
+  const int C = (len - 1) / kBlock;
+  const size_t row = static_cast<size_t>(b) * Hkv + r;
+  const int n_units = (k + NB) / NB;
+
+  uint64_t* src = keys;
+  const float lse_s = load_chunk_states(cand + row * static_cast<size_t>(nchunk * kc),
+                                        cpart + row * nchunk, nchunk, nlist, kc, C, src, red);
+  src = merge_sorted_lists(src, keys + nlist * kc, nlist, kc);
+  write_selection(src, min(k, C), k, lse_s, sel_blk, sel_lg);
+  __syncthreads();
+  if (unit == 0) {
+    if (tid < k) {
+      idx[row * k + tid] = sel_blk[tid];
+      log_gate[row * k + tid] = sel_lg[tid];
+    }
+    if (tid == 0) score_lse[row] = lse_s;
+  }
+  int start[NB], ntok[NB];
+  float beta2[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int u = unit * NB + bb;
+    start[bb] = 0;
+    ntok[bb] = 0;
+    beta2[bb] = 0.f;
+    if (u < k) {
+      const int m = sel_blk[u];
+      if (m >= 0) {
+        start[bb] = m * kBlock;
+        ntok[bb] = kBlock;
+        if (gated) beta2[bb] = sel_lg[u] * kLog2e;
+      }
+    } else if (u == k) {
+      start[bb] = C * kBlock;
+      ntok[bb] = len - start[bb];
+    }
+  }
+  split_unit<T, D, G, NB>(q, K, V, row, t_max, start, ntok, beta2, scale2,
+                          part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
+}
+
+// One workgroup per (sequence, group), one thread per pair of outputs (a
+// wave per head at d = 128).  Every load of the kernel is issued before any
+// is used: the (max, sum) pairs of all slots go to LDS, each thread's
+// accumulator pairs of all slots to registers, so the merge costs a single
+// round trip to memory.  Then, in slot order,
+//   M = max_u m_u,  w_u = 2^(m_u - M),  o = sum_u w_u acc_u / sum_u w_u l_u.
+constexpr int kMergeMaxSlots = kMaxTopK + 1;
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(G * D / 2 < 64 ? 64 : G * D / 2)
+decode_merge_kernel(int Hkv, int ns, const float* __restrict__ part, T* __restrict__ o,
                     float* __restrict__ lse) {
   constexpr int PF = DecPartial<G, D>::kFloats;
-  constexpr int PER = (G * D + kDecThreads - 1) / kDecThreads;
-  constexpr int BATCH = 24;  // k = 16 or 23: one round trip of loads
+  constexpr int NT = G * D / 2 < 64 ? 64 : G * D / 2;
+  __shared__ float ml[kMergeMaxSlots][2 * G];
   const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
-  const float* base = part + row * (k + 1) * static_cast<size_t>(PF);
+  const float* base = part + row * ns * static_cast<size_t>(PF);
+  const int x = 2 * tid;  // outputs x, x + 1 of head x / D
+  const bool act = x < G * D;
+  float2 av[kMergeMaxSlots];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int x = tid + e * kDecThreads;
-    if (x >= G * D) break;
-    const int g = x / D;
-    float M = -INFINITY, L = 0.f, A = 0.f;
-    for (int u0 = 0; u0 <= k; u0 += BATCH) {
-      float mv[BATCH], lv[BATCH], av[BATCH];
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        const int u = u0 + j;
-        mv[j] = -INFINITY;
-        lv[j] = 0.f;
-        av[j] = 0.f;
-        if (u <= k) {
-          const float* pu = base + static_cast<size_t>(u) * PF;
-          mv[j] = pu[G * D + g];
-          lv[j] = pu[G * D + G + g];
-          av[j] = pu[x];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < BATCH; ++j) {
-        if (mv[j] == -INFINITY) continue;  // empty slot
-        const float mn = fmaxf(M, mv[j]);
-        const float so = exp2f(M - mn), w = exp2f(mv[j] - mn);
-        L = L * so + w * lv[j];
-        A = A * so + w * av[j];
-        M = mn;
-      }
-    }
-    store_scalar<T>(o + (row * G) * static_cast<size_t>(D) + x, A / L);
-    if (lse && (x % D) == 0) lse[row * G + g] = M * kLn2 + logf(L);
+  for (int u = 0; u < kMergeMaxSlots; ++u) {
+    if (u < ns && act) av[u] = *reinterpret_cast<const float2*>(base + static_cast<size_t>(u) * PF + x);
   }
+  for (int i = tid; i < ns * 2 * G; i += NT) {
+    const int u = i / (2 * G), j = i % (2 * G);
+    ml[u][j] = base[static_cast<size_t>(u) * PF + G * D + j];
+  }
+  __syncthreads();
+  if (!act) return;
+  const int g = x / D;
+  float M = -INFINITY;
+  for (int u = 0; u < ns; ++u) M = fmaxf(M, ml[u][g]);
+  float L = 0.f, A0 = 0.f, A1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < kMergeMaxSlots; ++u) {
+    if (u < ns) {
+      const float w = fast_exp2(ml[u][g] - M);  // 0 for an empty slot (m = -inf)
+      L = fmaf(w, ml[u][G + g], L);
+      A0 = fmaf(w, av[u].x, A0);
+      A1 = fmaf(w, av[u].y, A1);
+    }
+  }
+  const float inv = 1.f / L;
+  T* op = o + (row * G) * static_cast<size_t>(D) + x;
+  store_scalar<T>(op, A0 * inv);
+  store_scalar<T>(op + 1, A1 * inv);
+  if (lse && (x % D) == 0) lse[row * G + g] = M * kLn2 + logf(L);
 }
 
 // workspace: partials[B*Hkv*(k+1)*G*(d+2)] fp32
@@ -259,21 +361,128 @@ size_t decode_ws_bytes(const sas_dims& d) {
   return rows * (d.top_k + 1) * G * (d.head_dim + 2) * sizeof(float);
 }
 
-template <typename T, int D, int G>
-static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, const void* V,
-                             const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
-                             float scale, void* o, float* lse, void* ws, hipStream_t st) {
+// Blocks per split workgroup: one while that leaves the grid too small to
+// fill the chip, else two (more bytes in flight per thread, half the partials).
+static int decode_blocks_per_unit(const sas_dims& d) {
+  const long units = static_cast<long>(d.batch) * d.n_kv_heads * (d.top_k + 1);
+  return units >= 1024 ? 2 : 1;
+}
+
+template <typename T, int D, int G, int NB>
+static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K, const void* V,
+                                const int32_t* seq_lens, const int32_t* idx,
+                                const float* log_gate, float scale, void* o, float* lse,
+                                void* ws, hipStream_t st) {
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL((decode_split_kernel<T, D, G>), dim3(d.top_k + 1, d.n_kv_heads, d.batch),
+  const int n_units = (d.top_k + NB) / NB;
+  hipLaunchKernelGGL((decode_split_kernel<T, D, G, NB>), dim3(n_units, d.n_kv_heads, d.batch),
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx, log_gate,
                      scale * kLog2e, d.n_kv_heads, d.t_max, d.top_k, part);
   sas_status s = check_launch("decode_split");
   if (s != SAS_OK) return s;
+  constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
   hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(d.n_kv_heads, d.batch),
-                     dim3(kDecThreads), 0, st, d.n_kv_heads, d.top_k, part, static_cast<T*>(o),
+                     dim3(kMergeThreads), 0, st, d.n_kv_heads, n_units, part, static_cast<T*>(o),
                      lse);
   return check_launch("decode_merge");
+}
+
+template <typename T, int D, int G>
+static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, const void* V,
+                             const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
+                             float scale, void* o, float* lse, void* ws, hipStream_t st) {
+  if (decode_blocks_per_unit(d) == 2)
+    return launch_dec_nb<T, D, G, 2>(d, q, K, V, seq_lens, idx, log_gate, scale, o, lse, ws, st);
+  return launch_dec_nb<T, D, G, 1>(d, q, K, V, seq_lens, idx, log_gate, scale, o, lse, ws, st);
+}
+
+// Fused decode step: the selection's chunk stage, then (rows of more than
+// one chunk) the select-merge + split kernel, then the merge.  Workspace:
+// the selection's, then the partials.  Large grids (two blocks per unit)
+// take the unfused sequence instead.
+template <typename T, int D, int G, int NB>
+static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K, const void* V,
+                                 const int32_t* seq_lens, const float* Wq, const float* summ,
+                                 int gated, float scale, int32_t* idx, float* log_gate,
+                                 float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
+  sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
+                                             ws, st);
+  if (s != SAS_OK) return s;
+  const SelectDecodeLayout L = select_decode_layout(d, ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                         ((select_decode_ws_bytes(d) + 255) & ~size_t(255)));
+  if (L.nchunk == 1)  // the chunk stage already wrote the selection
+    return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
+                                      scale, o, lse, part, st);
+  if constexpr (NB > 1) {
+    // Grids this large keep the chip busy on their own; there the redundant
+    // per-workgroup merge costs more than the launch it saves, so the
+    // selection's own merge kernel runs first (same outputs).
+    s = launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
+    if (s != SAS_OK) return s;
+    return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
+                                      scale, o, lse, part, st);
+  } else {
+  const int n_units = (d.top_k + NB) / NB;
+  hipLaunchKernelGGL((decode_select_split_kernel<T, D, G, NB>),
+                     dim3(n_units, d.n_kv_heads, d.batch), dim3(kDecThreads),
+                     2 * L.nlist * L.kc * sizeof(uint64_t), st, static_cast<const T*>(q),
+                     static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, L.part, L.cand,
+                     L.nchunk, L.nlist, L.kc, gated, scale * kLog2e, d.n_kv_heads, d.t_max,
+                     d.top_k, idx, log_gate, score_lse, part);
+  s = check_launch("decode_select_split");
+  if (s != SAS_OK) return s;
+  constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(d.n_kv_heads, d.batch),
+                     dim3(kMergeThreads), 0, st, d.n_kv_heads, n_units, part, static_cast<T*>(o),
+                     lse);
+  return check_launch("decode_merge");
+  }
+}
+
+template <typename T, int D, int G>
+static sas_status launch_step(const sas_dims& d, const void* q, const void* K, const void* V,
+                              const int32_t* seq_lens, const float* Wq, const float* summ,
+                              int gated, float scale, int32_t* idx, float* log_gate,
+                              float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
+  if (decode_blocks_per_unit(d) == 2)
+    return launch_step_nb<T, D, G, 2>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx,
+                                      log_gate, score_lse, o, lse, ws, st);
+  return launch_step_nb<T, D, G, 1>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate,
+                                    score_lse, o, lse, ws, st);
+}
+
+template <typename T, int D>
+static sas_status step_by_group(const sas_dims& d, const void* q, const void* K, const void* V,
+                                const int32_t* seq_lens, const float* Wq, const float* summ,
+                                int gated, float scale, int32_t* idx, float* log_gate,
+                                float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
+  switch (d.n_q_heads / d.n_kv_heads) {
+    case 1: return launch_step<T, D, 1>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 2: return launch_step<T, D, 2>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 4: return launch_step<T, D, 4>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 8: return launch_step<T, D, 8>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+  }
+  return fail(SAS_ERR_UNSUPPORTED, "decode step: group size");
+}
+
+size_t decode_step_ws_bytes(const sas_dims& d) {
+  return ((select_decode_ws_bytes(d) + 255) & ~size_t(255)) + decode_ws_bytes(d);
+}
+
+sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
+                              const int32_t* seq_lens, const float* Wq, const float* summ,
+                              int gated, float scale, int32_t* idx, float* log_gate,
+                              float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
+  if (d.dtype == SAS_BF16) {
+    if (d.head_dim == 128)
+      return step_by_group<uint16_t, 128>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    return step_by_group<uint16_t, 64>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+  }
+  if (d.head_dim == 128)
+    return step_by_group<float, 128>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+  return step_by_group<float, 64>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
 }
 
 template <typename T, int D>

@@ -156,6 +156,31 @@ sas_status sas_decode_fwd(const sas_dims* dims, const void* q, const void* K, co
                            static_cast<hipStream_t>(stream));
 }
 
+sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, const void* V,
+                           const int32_t* seq_lens, const float* Wq_sel, const float* summ,
+                           int32_t gated, float scale, int32_t* idx, float* log_gate,
+                           float* score_lse, void* o, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  SAS_TRY(check_dims(dims, false));
+  SAS_NONNULL(q);
+  SAS_NONNULL(K);
+  SAS_NONNULL(V);
+  SAS_NONNULL(seq_lens);
+  SAS_NONNULL(Wq_sel);
+  if (dims->t_max >= kBlock) SAS_NONNULL(summ);
+  if (dims->top_k > 0) {
+    SAS_NONNULL(idx);
+    SAS_NONNULL(log_gate);
+  }
+  SAS_NONNULL(score_lse);
+  SAS_NONNULL(o);
+  if (!(scale > 0.0f))
+    return fail(SAS_ERR_INVALID_ARGUMENT, "scale must be a positive number");
+  SAS_TRY(check_ws(decode_step_ws_bytes(*dims), ws, ws_bytes));
+  return launch_decode_step(*dims, q, K, V, seq_lens, Wq_sel, summ, gated != 0, scale, idx,
+                            log_gate, score_lse, o, lse, ws, static_cast<hipStream_t>(stream));
+}
+
 sas_status sas_prefill_fwd(const sas_dims* dims, const void* Q, const void* K, const void* V,
                            int32_t seq_len, const int32_t* idx, const float* log_gate,
                            float scale, void* O, float* lse, void* ws, size_t ws_bytes,
@@ -206,6 +231,7 @@ size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
     case SAS_OP_SELECT_DECODE: return select_decode_ws_bytes(*dims);
     case SAS_OP_SELECT_TILES: return 0;
     case SAS_OP_DECODE_FWD: return decode_ws_bytes(*dims);
+    case SAS_OP_DECODE_STEP: return decode_step_ws_bytes(*dims);
     case SAS_OP_PREFILL_FWD:
       if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
       return prefill_ws_bytes(*dims, q_len);

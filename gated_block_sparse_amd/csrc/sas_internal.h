@@ -13,6 +13,7 @@ constexpr int kBlock = 64;          // tokens per block (the only size built)
 constexpr int kMaxTopK = 64;        // largest k built
 constexpr int kSelChunk = 256;      // history blocks scored per workgroup in decode select
 constexpr int kMaxTileRows = 1024;  // prefill tiles supported by the tile selector
+constexpr int kMaxMergeKeys = 2048; // chunk candidates one decode row may merge
 
 // Set the thread-local error text (printf-style) and return `st`.
 sas_status fail(sas_status st, const char* fmt, ...);
@@ -48,10 +49,36 @@ sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, cons
                                const float* summ, int32_t* idx, float* log_gate,
                                float* score_lse, float* scores, hipStream_t st);
 
+// Where the decode selection keeps its per-chunk state in its workspace:
+// part[rows * nchunk] (max, sum-exp) and cand[rows * nchunk * kc] sorted keys.
+struct SelectDecodeLayout {
+  int nchunk, nlist, kc;  // chunks per row, chunks rounded up to a power of two, keys per chunk
+  float2* part;
+  uint64_t* cand;
+};
+SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws);
+// The first stage of the decode selection alone (scores, per-chunk state);
+// when a row fits one chunk it also writes the final idx/log_gate/score_lse.
+sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
+                                       const float* Wq, const float* summ, int32_t* idx,
+                                       float* log_gate, float* score_lse, void* ws,
+                                       hipStream_t st);
+// Its second stage: merges the per-chunk state into idx/log_gate/score_lse
+// (nothing to do when a row fits one chunk).
+sas_status launch_select_decode_merge(const sas_dims& d, const int32_t* seq_lens, int32_t* idx,
+                                      float* log_gate, float* score_lse, void* ws,
+                                      hipStream_t st);
+
 size_t decode_ws_bytes(const sas_dims& d);
 sas_status launch_decode_fwd(const sas_dims& d, const void* q, const void* K, const void* V,
                              const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
                              float scale, void* o, float* lse, void* ws, hipStream_t st);
+
+size_t decode_step_ws_bytes(const sas_dims& d);
+sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
+                              const int32_t* seq_lens, const float* Wq, const float* summ,
+                              int gated, float scale, int32_t* idx, float* log_gate,
+                              float* score_lse, void* o, float* lse, void* ws, hipStream_t st);
 
 size_t prefill_ws_bytes(const sas_dims& d, int seq_len);
 sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,

@@ -18,31 +18,11 @@
 // Tiles (prefill): one workgroup per (tile, group) does everything.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "sas_select_dev.h"
 
 namespace sas {
 
 constexpr int kSelThreads = 256;
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = group_max(v, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < nw; ++i) r = fmaxf(r, red[i]);
-  return r;
-}
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = group_sum(v, 64);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < nw; ++i) r += red[i];
-  return r;
-}
 
 // qs[j] = (Wq[j,:] . qm) / sqrt(DS), for j < DS (threads tid < DS).
 template <int D, int DS>
@@ -102,23 +82,6 @@ __device__ __forceinline__ void score_rows(const float* __restrict__ summ_row0, 
     transpose_sum32(v, l32);
     const int i = base + hw + 8 * l32;
     if (i < n) sc[i] = v[0];
-  }
-}
-
-// Writes the row's final outputs from the (descending-sorted) keys[0..kk).
-__device__ __forceinline__ void write_selection(const uint64_t* keys, int kk, int k, float lse,
-                                                int32_t* idx, float* log_gate) {
-  const int tid = threadIdx.x;
-  if (tid < kk) {
-    const uint64_t key = keys[tid];
-    const int mb = key_block(key);
-    int rank = 0;
-    for (int j = 0; j < kk; ++j) rank += key_block(keys[j]) < mb;
-    idx[rank] = mb;
-    log_gate[rank] = key_score(key) - lse;
-  } else if (tid < k) {
-    idx[tid] = -1;
-    log_gate[tid] = -INFINITY;
   }
 }
 
@@ -279,39 +242,11 @@ select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
-  const int ncand = nchunk * kc, ntot = nlist * kc;
   uint64_t* src = lds;
-  uint64_t* dst = lds + ntot;
-  const uint64_t* cr = cand + row * static_cast<size_t>(ncand);
-  for (int i = tid; i < ntot; i += kSelThreads) src[i] = i < ncand ? cr[i] : 0ull;
-  const float2* pr = part + row * nchunk;
-  float mloc = -INFINITY;
-  for (int i = tid; i < nchunk; i += kSelThreads) mloc = fmaxf(mloc, pr[i].x);
-  const float M = block_max(mloc, red);
-  float sloc = 0.f;
-  for (int i = tid; i < nchunk; i += kSelThreads) {
-    const float2 v = pr[i];
-    if (v.x != -INFINITY) sloc += v.y * expf(v.x - M);
-  }
-  const float L = block_sum(sloc, red);  // ends with a barrier: src is complete
-  const float lse = C > 0 ? M + logf(L) : -INFINITY;
-  for (int nl = nlist; nl > 1; nl >>= 1) {
-    const int half = nl >> 1;
-    for (int i = tid; i < half * kc; i += kSelThreads) dst[i] = 0ull;
-    __syncthreads();
-    for (int i = tid; i < nl * kc; i += kSelThreads) {
-      const int li = i / kc, pos = i % kc;
-      const uint64_t key = src[i];
-      if (key == 0ull) continue;
-      const int partner = li ^ 1;
-      const int rank = pos + count_greater_desc(src + partner * kc, kc, key);
-      if (rank < kc) dst[(li >> 1) * kc + rank] = key;
-    }
-    __syncthreads();
-    uint64_t* t = src;
-    src = dst;
-    dst = t;
-  }
+  uint64_t* dst = lds + nlist * kc;
+  const float lse = load_chunk_states(cand + row * static_cast<size_t>(nchunk * kc),
+                                      part + row * nchunk, nchunk, nlist, kc, C, src, red);
+  src = merge_sorted_lists(src, dst, nlist, kc);
   write_selection(src, min(k, C), k, lse, idx + row * k, log_gate + row * k);
   if (tid == 0) score_lse[row] = lse;
 }
@@ -330,33 +265,55 @@ size_t select_decode_ws_bytes(const sas_dims& d) {
          rows * nc * static_cast<size_t>(d.top_k > 0 ? d.top_k : 1) * sizeof(uint64_t);
 }
 
+SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws) {
+  SelectDecodeLayout L;
+  L.nchunk = decode_nchunk(d);
+  L.kc = d.top_k > 0 ? d.top_k : 1;
+  L.nlist = 1;
+  while (L.nlist < L.nchunk) L.nlist <<= 1;
+  const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  char* w = static_cast<char*>(ws);
+  L.part = reinterpret_cast<float2*>(w);
+  L.cand = reinterpret_cast<uint64_t*>(w + align256(rows * L.nchunk * sizeof(float2)));
+  return L;
+}
+
+template <typename T, int D, int DS, int G>
+static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
+                                   const float* Wq, const float* summ, int32_t* idx,
+                                   float* log_gate, float* score_lse, float* scores, void* ws,
+                                   hipStream_t st) {
+  const SelectDecodeLayout L = select_decode_layout(d, ws);
+  if (L.nlist * L.kc > kMaxMergeKeys)
+    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
+                L.nlist * L.kc);
+  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G>),
+                     dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,
+                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,
+                     d.t_max / kBlock, d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx,
+                     log_gate, score_lse);
+  return check_launch("select_decode_chunk");
+}
+
+sas_status launch_select_decode_merge(const sas_dims& d, const int32_t* seq_lens, int32_t* idx,
+                                      float* log_gate, float* score_lse, void* ws,
+                                      hipStream_t st) {
+  const SelectDecodeLayout L = select_decode_layout(d, ws);
+  if (L.nchunk == 1) return SAS_OK;
+  hipLaunchKernelGGL(select_decode_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kSelThreads),
+                     2 * L.nlist * L.kc * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max,
+                     d.top_k, L.kc, L.nchunk, L.nlist, L.part, L.cand, idx, log_gate, score_lse);
+  return check_launch("select_decode_merge");
+}
+
 template <typename T, int D, int DS, int G>
 static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq_lens,
                             const float* Wq, const float* summ, int32_t* idx, float* log_gate,
                             float* score_lse, float* scores, void* ws, hipStream_t st) {
-  const int nchunk = decode_nchunk(d);
-  const int k = d.top_k;
-  const int kc = k > 0 ? k : 1;
-  int nlist = 1;
-  while (nlist < nchunk) nlist <<= 1;
-  if (nlist * kc > 2048)
-    return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
-                nlist * kc);
-  const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads;
-  char* w = static_cast<char*>(ws);
-  float2* part = reinterpret_cast<float2*>(w);
-  uint64_t* cand = reinterpret_cast<uint64_t*>(w + align256(rows * nchunk * sizeof(float2)));
-  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G>),
-                     dim3(nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,
-                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,
-                     d.t_max / kBlock, k, kc, nchunk, scores, part, cand, idx, log_gate,
-                     score_lse);
-  sas_status s = check_launch("select_decode_chunk");
-  if (s != SAS_OK || nchunk == 1) return s;
-  hipLaunchKernelGGL(select_decode_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kSelThreads),
-                     2 * nlist * kc * sizeof(uint64_t), st, seq_lens, d.n_kv_heads, d.t_max, k, kc,
-                     nchunk, nlist, part, cand, idx, log_gate, score_lse);
-  return check_launch("select_decode_merge");
+  sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, idx, log_gate,
+                                               score_lse, scores, ws, st);
+  if (s != SAS_OK) return s;
+  return launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
 }
 
 // -------------------------------------------------------------- tiles ---
@@ -444,6 +401,16 @@ struct SelDecode {
 };
 
 template <typename T, int D, int DS, int G>
+struct SelDecodeChunks {
+  static sas_status run(const sas_dims& d, const void* q, const int32_t* seq_lens, const float* Wq,
+                        const float* summ, int32_t* idx, float* log_gate, float* score_lse,
+                        float* scores, void* ws, hipStream_t st) {
+    return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
+                                         scores, ws, st);
+  }
+};
+
+template <typename T, int D, int DS, int G>
 struct SelTiles {
   static sas_status run(const sas_dims& d, const void* Q, int q_len, const float* Wq,
                         const float* summ, int32_t* idx, float* log_gate, float* score_lse,
@@ -487,6 +454,14 @@ sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t*
                                 const float* Wq, const float* summ, int32_t* idx, float* log_gate,
                                 float* score_lse, float* scores, void* ws, hipStream_t st) {
   return by_type<SelDecode>(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse, scores, ws, st);
+}
+
+sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
+                                       const float* Wq, const float* summ, int32_t* idx,
+                                       float* log_gate, float* score_lse, void* ws,
+                                       hipStream_t st) {
+  return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
+                                  static_cast<float*>(nullptr), ws, st);
 }
 
 sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, const float* Wq,

@@ -76,7 +76,8 @@ typedef enum {
   SAS_OP_SELECT_TILES = 1,
   SAS_OP_DECODE_FWD = 2,
   SAS_OP_PREFILL_FWD = 3,
-  SAS_OP_BWD = 4
+  SAS_OP_BWD = 4,
+  SAS_OP_DECODE_STEP = 5
 } sas_op;
 
 /* Problem sizes.  Supported: block_size 64; head_dim and sel_dim 64 or 128;
@@ -141,6 +142,22 @@ sas_status sas_decode_fwd(const sas_dims* dims, const void* q, const void* K, co
                           const int32_t* seq_lens, const int32_t* idx, const float* log_gate,
                           float scale, void* o, float* lse, void* ws, size_t ws_bytes,
                           void* stream);
+
+/* One whole decode step of the selection and the attention, fused (SAS
+ * close reading 2.1-2.2; SAS summary, Method, fused kernel): the same outputs,
+ * bit for bit, as sas_select(SAS_SELECT_DECODE, ...) followed by
+ * sas_decode_fwd(..., gated ? log_gate : NULL, ...) on its selection, in
+ * fewer launches: the merge of the selection's per-chunk candidates runs
+ * inside the attention's split kernel instead of a kernel of its own.
+ * Arguments as in those two calls; idx/log_gate [B,Hkv,1,k] and score_lse
+ * [B,Hkv,1] are outputs here; gated = 0 gives the ungated inference rule for
+ * the attention (log_gate is still written).
+ * ws: at least sas_workspace_bytes(SAS_OP_DECODE_STEP, dims, 0). */
+sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, const void* V,
+                           const int32_t* seq_lens, const float* Wq_sel, const float* summ,
+                           int32_t gated, float scale, int32_t* idx, float* log_gate,
+                           float* score_lse, void* o, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Causal prefill / training forward with one selection per 64-query tile
  * (SAS summary, Method, fused kernel; SAS close reading 2.4): query i of tile

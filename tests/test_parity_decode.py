@@ -1,5 +1,6 @@
 """GPU parity of the decode path against the CPU oracle, through the C ABI:
-sas_block_summaries -> sas_select(DECODE) -> sas_decode_fwd.
+sas_block_summaries -> sas_select(DECODE) -> sas_decode_fwd, and the fused
+sas_decode_step, which must reproduce the last two bit for bit.
 
 Full-size workloads (tiny fp32 4K; Qwen3-4B shape at 64K; batch 8 at
 32K-64K; 512K with planted blocks) plus a sweep of edge cases: contexts of
@@ -98,6 +99,16 @@ def run_decode_case(p: synth.Problem, t_max=None, check_e2e=True, label=""):
                 idx_h[b, r, 0], lg_h[b, r, 0], ref["scores"][b][r], ref["idx"][b, r],
                 ref["gap"][b, r], k, ref["slse"][b, r], tol_f)
 
+    # the fused step reproduces select + decode_fwd bit for bit (gated and ungated)
+    for gated in (True, False):
+        idx_f, lg_f, slse_f, o_f, lse_f = S.sas_decode_step(q, K, V, lens, Wq, summ, k,
+                                                            gated=gated)
+        o_r, lse_r = S.sas_decode_fwd(q, K, V, lens, idx_g, lg_g if gated else None)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_f, idx_g) and torch.equal(lg_f, lg_g), label
+        assert torch.equal(slse_f, slse_g), label
+        assert torch.equal(o_f, o_r) and torch.equal(lse_f, lse_r), (label, gated)
+
     # attention on the oracle's selection
     oidx, olg = idx_dev(ref["idx"][:, :, None]), lg_dev(ref["lg"][:, :, None])
     o, lse = S.sas_decode_fwd(q, K, V, lens, oidx, olg)
@@ -184,6 +195,17 @@ def test_decode_varlen_batch_and_ragged_tmax():
     p = _edge_problem(700, 5, dtype="bf16", Hq=8, Hkv=2, d=128, ds=128, batch=6, lens=lens,
                       t_max=700)
     run_decode_case(p, label="varlen")
+
+
+@pytest.mark.parametrize("k", [7, 8])
+def test_decode_two_blocks_per_unit_ragged(k):
+    """Grids of at least 1024 (sequence, group, slot) units take two blocks per
+    split workgroup: cover an odd and an even slot count, empty history slots
+    (C < k) and single-token B0s."""
+    lens = [1, 64, 65, 130, 300, 511, 512, 513, 700, 1000, 2049, 3000, 4000, 4095, 4096, 4097]
+    p = _edge_problem(4097, k, dtype="bf16", Hq=32, Hkv=8, d=128, ds=128, batch=16, lens=lens,
+                      seed=100 + k)
+    run_decode_case(p, label=f"two-block units k={k}")
 
 
 @pytest.mark.parametrize("T,k", [(64 * 200 + 3, 64), (64 * 3000 + 17, 64), (64 * 9000 + 1, 32)])
