@@ -59,9 +59,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               uint16_t* __restrict__ dQ) {
   constexpr int NT = 128 * HPW;
   constexpr int KS = D / 16, CT = D / 32;
-  constexpr int RSTR = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * RSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * RSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kRowStride<D>];  // K, row reads
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * kTrStride<D>];   // K, transpose reads
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * kRowStride<D>];
 
   const int nhc = G / HPW;
   const int t = n_tiles - 1 - static_cast<int>(blockIdx.x) / nhc;
@@ -104,8 +104,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     const int tok0 = blk * 64;
     __syncthreads();
-    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, tid);
-    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, Vs, tid);
+    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, Kt, tid);
+    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, Vs, nullptr, tid);
     __syncthreads();
 
     f32x16_t s[2], dp[2];
@@ -115,9 +115,9 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       zero16(dp[tt]);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = (32 * tt + l32) * RSTR + 16 * ks + 8 * hi;
-        s[tt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[off])), qb[ks], s[tt]);
-        dp[tt] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const uint4*>(&Vs[off])), db[ks], dp[tt]);
+        const int row = 32 * tt + l32, col = 16 * ks + 8 * hi;
+        s[tt] = mfma32x32x16(lds_row8<kRowStride<D>>(Ks, row, col), qb[ks], s[tt]);
+        dp[tt] = mfma32x32x16(lds_row8<kRowStride<D>>(Vs, row, col), db[ks], dp[tt]);
       }
     }
     const float off = beta2 - lse2;
@@ -144,7 +144,7 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const bf16x8_t bop = acc_to_bop(s, j);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
-        dq[ct] = mfma32x32x16(lds_aop_tr_perm(Ks, RSTR, 32 * ct, j, hi), bop, dq[ct]);
+        dq[ct] = mfma32x32x16(lds_aop_tr_perm<kTrStride<D>>(Kt, 32 * ct, j, hi), bop, dq[ct]);
     }
   }
   if (qvalid) store_acc_col<CT>(dq, scale, dQ + qrow_i * D, hi);
@@ -171,19 +171,20 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
   constexpr int NT = 64 * NWV;
   constexpr int KS = D / 16, CT = D / 32;
-  constexpr int RSTR = D + 8;       // K/V row stride (bf16)
-  // K rows then V rows; reused at the end for the cross-wave dK/dV sum
-  // (64 x D floats fit in 2 x 64 x (D + 8) bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * 64 * RSTR];
+  // K rows then V rows (row reads); reused at the end for the cross-wave
+  // dK/dV sum (64 x (D + 1) floats fit in 2 x 64 x (D + 8) bf16)
+  constexpr int RS = kRowStride<D>, TS = kTrStride<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * 64 * RS];
   uint16_t* const Ks = KVs;
-  uint16_t* const Vs = KVs + 64 * RSTR;
-  __shared__ __attribute__((aligned(16))) uint16_t Qw[NWV][32 * RSTR];   // per wave: 32 query rows
-  __shared__ __attribute__((aligned(16))) uint16_t dOw[NWV][32 * RSTR];
+  uint16_t* const Vs = KVs + 64 * RS;
+  __shared__ __attribute__((aligned(16))) uint16_t Qw[NWV][32 * TS];   // per wave: 32 query rows
+  __shared__ __attribute__((aligned(16))) uint16_t dOw[NWV][32 * TS];
   __shared__ int list_t[kMaxTileRows];
   __shared__ int list_slot[kMaxTileRows];
   __shared__ float dsum_s[NWV][kMaxTileRows];
   __shared__ float lse_w[NWV][64];   // per wave: lse (base 2) and D of the tile's queries
   __shared__ float dq_w[NWV][64];
+  __shared__ float list_beta[kMaxTileRows];   // log-gate (base 2) of each entry
   __shared__ int s_count;
   __shared__ int s_wcount[NWV];
 
@@ -198,6 +199,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (tid == 0) {
     list_t[0] = m;
     list_slot[0] = -1;
+    list_beta[0] = 0.f;
     s_count = 1;
   }
   __syncthreads();
@@ -224,6 +226,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (slot >= 0) {
       list_t[off + before] = t;
       list_slot[off + before] = slot;
+      list_beta[off + before] = log_gate ? log_gate[(grow * n_tiles + t) * k + slot] * kLog2eF : 0.f;
     }
     __syncthreads();
     if (tid == 0) {
@@ -237,8 +240,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- stage the block's K and V rows (B operands, shared by the waves)
   const int tok0 = 64 * m;
-  stage_rows<D, NT>(K + (grow * t_max + tok0) * D, S - tok0, Ks, tid);
-  stage_rows<D, NT>(V + (grow * t_max + tok0) * D, S - tok0, Vs, tid);
+  stage_rows<D, NT>(K + (grow * t_max + tok0) * D, S - tok0, Ks, nullptr, tid);
+  stage_rows<D, NT>(V + (grow * t_max + tok0) * D, S - tok0, Vs, nullptr, tid);
   __syncthreads();
 
   f32x16_t dk[2][CT], dv[2][CT];  // [token tile][channel tile]
@@ -252,17 +255,31 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   uint16_t* qt_s = Qw[wave];
   uint16_t* dot_s = dOw[wave];
 
+  // lse and D of the wave's next (entry, head) pair are loaded one pair
+  // ahead, so their memory latency overlaps the current pair's work
+  float pre_l = 0.f, pre_d = 0.f;
+  auto fetch_rows = [&](int e2, int g2) {
+    const int q2 = 64 * list_t[e2];
+    const size_t hrow2 = (static_cast<size_t>(b) * Hq + r * G + g2) * S + q2;
+    const bool ok = lane < min(64, S - q2);
+    pre_l = ok ? lse[hrow2 + lane] * kLog2eF : 0.f;
+    pre_d = ok ? Dq[hrow2 + lane] : 0.f;
+  };
+  if (wave < G) fetch_rows(0, wave);
+
   for (int e = 0; e < n_list; ++e) {
-    const int t = list_t[e], slot = list_slot[e];
-    const bool diag = slot < 0;
-    const float beta2 = (!diag && log_gate) ? log_gate[(grow * n_tiles + t) * k + slot] * kLog2eF : 0.f;
+    const int t = list_t[e];
+    const bool diag = e == 0;
+    const float beta2 = list_beta[e];
     const int q0 = 64 * t;
     const int nq = min(64, S - q0);
     float dsum = 0.f;
     for (int g = wave; g < G; g += NWV) {
       const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g) * S + q0;
-      lse_w[wave][lane] = lane < nq ? lse[hrow + lane] * kLog2eF : 0.f;
-      dq_w[wave][lane] = lane < nq ? Dq[hrow + lane] : 0.f;
+      lse_w[wave][lane] = pre_l;
+      dq_w[wave][lane] = pre_d;
+      if (g + NWV < G) fetch_rows(e, g + NWV);
+      else if (e + 1 < n_list) fetch_rows(e + 1, wave);
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_wave_barrier();
 #pragma unroll 1
@@ -286,17 +303,17 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           zero16(dp[tt]);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const int off = (32 * tt + l32) * RSTR + 16 * ks + 8 * hi;
-            s[tt] = mfma32x32x16(qa[ks], as_bf16x8(*reinterpret_cast<const uint4*>(&Ks[off])), s[tt]);
-            dp[tt] = mfma32x32x16(da[ks], as_bf16x8(*reinterpret_cast<const uint4*>(&Vs[off])), dp[tt]);
+            const int row = 32 * tt + l32, col = 16 * ks + 8 * hi;
+            s[tt] = mfma32x32x16(qa[ks], lds_row8<RS>(Ks, row, col), s[tt]);
+            dp[tt] = mfma32x32x16(da[ks], lds_row8<RS>(Vs, row, col), dp[tt]);
           }
         }
         // this half tile's Q and dO rows into the wave's LDS (row-major; the
         // dK/dV A operands read them back transposed)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          *reinterpret_cast<uint4*>(&qt_s[l32 * RSTR + 16 * ks + 8 * hi]) = __builtin_bit_cast(uint4, qa[ks]);
-          *reinterpret_cast<uint4*>(&dot_s[l32 * RSTR + 16 * ks + 8 * hi]) = __builtin_bit_cast(uint4, da[ks]);
+          lds_store_row8<TS>(qt_s, l32, 16 * ks + 8 * hi, __builtin_bit_cast(uint4, qa[ks]));
+          lds_store_row8<TS>(dot_s, l32, 16 * ks + 8 * hi, __builtin_bit_cast(uint4, da[ks]));
         }
         // P and dS (rows: queries, columns: this lane's token)
         if (diag || nq < 64 || tok0 + 64 > S) {
@@ -345,8 +362,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             const bf16x8_t sb = acc_to_bop(&dp[tt], j);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-              dv[tt][ct] = mfma32x32x16(lds_aop_tr_perm(dot_s, RSTR, 32 * ct, j, hi), pb, dv[tt][ct]);
-              dk[tt][ct] = mfma32x32x16(lds_aop_tr_perm(qt_s, RSTR, 32 * ct, j, hi), sb, dk[tt][ct]);
+              dv[tt][ct] = mfma32x32x16(lds_aop_tr_perm<TS>(dot_s, 32 * ct, j, hi), pb, dv[tt][ct]);
+              dk[tt][ct] = mfma32x32x16(lds_aop_tr_perm<TS>(qt_s, 32 * ct, j, hi), sb, dk[tt][ct]);
             }
           }
         }
@@ -365,7 +382,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     dlg[(grow * n_tiles + list_t[e]) * k + list_slot[e]] = tot;
   }
   // ---- sum dK^T / dV^T over the waves (through LDS, wave by wave), store
-  float* red = reinterpret_cast<float*>(KVs);
+  float* red = reinterpret_cast<float*>(KVs);   // [64][D + 1]: the pad spreads a column over the banks
   for (int which = 0; which < 2; ++which) {
     for (int w = 0; w < NWV; ++w) {
       __syncthreads();
@@ -378,7 +395,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int v = 0; v < 16; ++v) {
               const int tok = 32 * tt + l32, c = 32 * ct + acc_row(v, hi);
               const float x = which ? dv[tt][ct][v] : dk[tt][ct][v];
-              float* slotp = &red[tok * D + c];
+              float* slotp = &red[tok * (D + 1) + c];
               *slotp = (w == 0) ? x : *slotp + x;
             }
       }
@@ -392,7 +409,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         uint32_t wv[4];
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          uint32_t u = __float_as_uint(red[tok * D + c4 + e4] * mul);
+          uint32_t u = __float_as_uint(red[tok * (D + 1) + c4 + e4] * mul);
           u += 0x7FFFu + ((u >> 16) & 1u);
           wv[e4] = u >> 16;
         }

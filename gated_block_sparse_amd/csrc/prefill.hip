@@ -17,7 +17,9 @@
 //    (the 16 tokens of a k-step are taken in the order the accumulator layout
 //    holds them), and V^T is read in that same order from the row-major V
 //    tile with the LDS transpose read;
-//  * the log-gate is added per block; the diagonal block is masked j > i.
+//  * the log-gate is added per block; the diagonal block is masked j > i;
+//  * the block loop is software-pipelined (see the kernel) so each wave always
+//    has matrix and vector work that do not depend on each other.
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_mfma.h"
@@ -25,8 +27,8 @@
 namespace sas {
 
 // Per-thread share of staging one 64-token block: K and V rows, as 16-byte
-// chunks copied row-major into LDS (V is read back transposed by the LDS
-// transpose read, so no shuffling is needed on the way in).
+// chunks copied row-major into LDS (V, at the transpose-read stride, is read
+// back transposed by the LDS transpose read, so no shuffling on the way in).
 template <int D, int NT>
 struct BlockStage {
   static constexpr int TOT = 64 * (D / 8);           // 16-byte chunks per tensor
@@ -45,18 +47,50 @@ struct BlockStage {
     }
   }
   __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vs, int tid) const {
-    constexpr int RSTR = D + 8;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
       if (c < TOT) {
-        *reinterpret_cast<uint4*>(&Ks[row * RSTR + cc * 8]) = k[i];
-        *reinterpret_cast<uint4*>(&Vs[row * RSTR + cc * 8]) = v[i];
+        lds_store_row8<kRowStride<D>>(Ks, row, cc * 8, k[i]);
+        lds_store_row8<kTrStride<D>>(Vs, row, cc * 8, v[i]);
       }
     }
   }
 };
 
+// S^T (64 tokens x 32 queries) = K Q^T for one staged block.
+template <int D>
+__device__ __forceinline__ void block_scores(const uint16_t* Kc, const bf16x8_t* qb, f32x16_t* s,
+                                             int l32, int hi) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    zero16(s[tt]);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      s[tt] = mfma32x32x16(lds_row8<kRowStride<D>>(Kc, 32 * tt + l32, 16 * ks + 8 * hi), qb[ks],
+                           s[tt]);
+  }
+}
+
+// O^T (D channels x 32 queries) += V^T P^T for one staged block; k-step j =
+// tokens 16j..16j+15 in accumulator order.
+template <int D>
+__device__ __forceinline__ void block_pv(const uint16_t* Vc, const bf16x8_t* pb, f32x16_t* acc,
+                                         int hi) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+      acc[ct] = mfma32x32x16(lds_aop_tr_perm<kTrStride<D>>(Vc, 32 * ct, j, hi), pb[j], acc[ct]);
+}
+
+// Software pipeline over the block list: in iteration i a wave
+//   A: adds block i-1's P V into O^T (MFMA) while it takes block i's max (VALU),
+//   B: computes block i+1's scores (MFMA) while it exponentiates block i (VALU),
+// so the matrix cores and the vector ALUs of a wave have independent work at
+// every point.  Staged blocks live in a ring of four LDS buffers (block i in
+// buffer i % 4); block i+2 is written while blocks i-1 and i+1 are read, so
+// one barrier per iteration suffices.
 template <int D, int HPW>
 __global__ void __launch_bounds__(128 * HPW)
 prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -67,9 +101,9 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int NT = 128 * HPW;      // threads
   constexpr int KS = D / 16;         // k-steps of S^T = K Q^T
   constexpr int CT = D / 32;         // channel tiles of O^T
-  constexpr int KSTR = D + 8;        // K row stride in LDS (bf16), +16 bytes
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * KSTR];
+  constexpr int NBUF = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][64 * kRowStride<D>];  // row reads
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][64 * kTrStride<D>];   // transpose reads
   __shared__ int s_blk[kMaxTopK + 1];
   __shared__ float s_beta[kMaxTopK + 1];
   __shared__ int s_nblk;
@@ -121,53 +155,43 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   __syncthreads();
   const int nblk = s_nblk;
 
+  // History blocks are 0..nh-1, the diagonal block is nh.  The loop body
+  // has no branch apart from the (rare) rescale, so each half of it is one
+  // basic block in which the matrix and vector work can interleave: indices
+  // of blocks beyond the list are clamped (their staging writes land in a
+  // buffer nobody reads again), and the first iteration's P V runs on a
+  // zeroed buffer with P = 0.
+  const int nh = nblk - 1;
   BlockStage<D, NT> stg;
-  {
-    const int tok0 = s_blk[0] * 64;
-    stg.load(Kg + static_cast<size_t>(tok0) * D, Vg + static_cast<size_t>(tok0) * D, S - tok0, tid);
-    stg.store(Ks[0], Vs[0], tid);
-  }
+  auto load_block = [&](int i) {
+    const int tok = s_blk[min(i, nh)] * 64;
+    stg.load(Kg + static_cast<size_t>(tok) * D, Vg + static_cast<size_t>(tok) * D, S - tok, tid);
+  };
+  load_block(0);
+  stg.store(Ks[0], Vs[0], tid);
+  load_block(1);
+  stg.store(Ks[1], Vs[1], tid);
+  for (int c = tid; c < 64 * kTrStride<D> / 8; c += NT)
+    *reinterpret_cast<uint4*>(&Vs[3][8 * c]) = make_uint4(0, 0, 0, 0);
+  load_block(2);
   __syncthreads();
 
-  for (int it = 0; it < nblk; ++it) {
-    const int buf = it & 1;
-    const bool diag = it == nblk - 1;
-    const float beta2 = s_beta[it];
-    if (it + 1 < nblk) {  // prefetch the next block while this one computes
-      const int tok1 = s_blk[it + 1] * 64;
-      stg.load(Kg + static_cast<size_t>(tok1) * D, Vg + static_cast<size_t>(tok1) * D, S - tok1, tid);
-    }
-    const uint16_t* Kc = Ks[buf];
-    const uint16_t* Vc = Vs[buf];
+  f32x16_t s_cur[2];
+  block_scores<D>(Ks[0], qb, s_cur, l32, hi);
+  bf16x8_t p_prev[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p_prev[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
-    // S^T (64 tokens x 32 queries) = K Q^T
-    f32x16_t s[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      zero16(s[tt]);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kc[(32 * tt + l32) * KSTR + 16 * ks + 8 * hi]));
-        s[tt] = mfma32x32x16(a, qb[ks], s[tt]);
-      }
-    }
-    // online softmax on the lane's query column (base-2 domain)
-    if (diag) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (32 * tt + acc_row(v, hi) > qloc) s[tt][v] = -INFINITY;
-    }
+  // Lazy rescaling: the running max only moves (and the accumulators are
+  // only rescaled) when some lane's max grew by more than 2^8; otherwise the
+  // probabilities are taken against the stale max, which bounds them by 256.
+  auto update_max = [&](float beta2) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[tt][v]);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[tt][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescaling: the running max only moves (and the accumulators are
-    // only rescaled) when some lane's max grew by more than 2^8; otherwise the
-    // probabilities are taken against the stale max, which bounds them by 256.
     const float m_cand = fmaxf(m_run, mx * scale2 + beta2);
     if (__any(!(m_cand - m_run <= 8.f))) {
       const float alpha = exp2f(m_run - m_cand);
@@ -178,30 +202,50 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
       m_run = m_cand;
     }
+  };
+  auto probabilities = [&](float beta2) {
     const float off = beta2 - m_run;
     float ls = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(s[tt][v], scale2, off));
-        s[tt][v] = p;
+        const float p = fast_exp2(fmaf(s_cur[tt][v], scale2, off));
+        s_cur[tt][v] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
     l_run += ls;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p_prev[j] = acc_to_bop(s_cur, j);
+  };
 
-    // O^T (D channels x 32 queries) += V^T P^T, k-step j = tokens 16j..16j+15
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t pb = acc_to_bop(s, j);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        acc[ct] = mfma32x32x16(lds_aop_tr_perm(Vc, KSTR, 32 * ct, j, hi), pb, acc[ct]);
-    }
-    if (it + 1 < nblk) stg.store(Ks[buf ^ 1], Vs[buf ^ 1], tid);
+  for (int it = 0; it < nh; ++it) {
+    const float beta2 = s_beta[it];
+    // A: the previous block's P V, this block's max
+    block_pv<D>(Vs[(it + 3) & 3], p_prev, acc, hi);
+    update_max(beta2);
+    // B: the next block's scores, this block's probabilities, staging of
+    // block it+2 and the loads of block it+3
+    f32x16_t s_next[2];
+    block_scores<D>(Ks[(it + 1) & 3], qb, s_next, l32, hi);
+    probabilities(beta2);
+    stg.store(Ks[(it + 2) & 3], Vs[(it + 2) & 3], tid);
+    load_block(it + 3);
     __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) s_cur[tt] = s_next[tt];
   }
+  // the diagonal block: causal mask j > i
+  block_pv<D>(Vs[(nh + 3) & 3], p_prev, acc, hi);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (32 * tt + acc_row(v, hi) > qloc) s_cur[tt][v] = -INFINITY;
+  update_max(0.f);
+  probabilities(0.f);
+  block_pv<D>(Vs[nh & 3], p_prev, acc, hi);
 
   if (qvalid) {
     store_acc_col<CT>(acc, 1.f / l_run, O + ((static_cast<size_t>(b) * Hq + h) * S + qi) * D, hi);

@@ -53,36 +53,62 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
       (lds_s16x4_t*)((__attribute__((address_space(3))) uint16_t*)p));
   return __builtin_bit_cast(uint2, v);
 }
+// LDS tiles of 64 (or 32) rows x D bf16 are row-major with a padded row
+// stride chosen for how the tile is read (64 banks of 4 bytes):
+//   * kRowStride = D + 8 for 16-byte row reads, one chunk of 16 consecutive
+//     rows per pass (row r starts 4r banks further: all 64 banks once);
+//   * kTrStride = D + 32 for the transpose reads below, which take 4
+//     consecutive rows x 64 bytes per pass (rows 16 banks apart).
+// Each stride conflicts for the other pattern (4-way), so a tile that is
+// read both ways is staged twice.  (An XOR swizzle serves both patterns, but
+// its addresses cannot be folded into instruction offsets and the kernels
+// then run out of registers.)  Staging writes of consecutive chunks are
+// conflict-free at either stride for D = 128.
+template <int D> constexpr int kRowStride = D + 8;
+template <int D> constexpr int kTrStride = D + 32;
+
 // A operand of v_mfma_f32_32x32x16_bf16 whose M index is a COLUMN of a
-// row-major LDS matrix X (row stride rs, K along the rows): lane (l32, hi)
+// row-major LDS tile X of row stride RS (K along the rows): lane (l32, hi)
 // gets column i0 + l32, K elements 0-3 from rows k0..k0+3 and 4-7 from rows
 // k1..k1+3 (callers pass per-lane k0/k1 that depend on hi).
-__device__ __forceinline__ bf16x8_t lds_aop_tr(const uint16_t* X, int rs, int i0, int k0, int k1) {
+template <int RS>
+__device__ __forceinline__ bf16x8_t lds_aop_tr(const uint16_t* X, int i0, int k0, int k1) {
   const int lane = threadIdx.x & 63, g = lane >> 4, jj = lane & 15;
   const int col = i0 + 16 * (g & 1) + 4 * (jj & 3);
   const int ro = jj >> 2;
-  const uint2 a = lds_read_tr16(X + (k0 + ro) * rs + col);
-  const uint2 b = lds_read_tr16(X + (k1 + ro) * rs + col);
+  const uint2 a = lds_read_tr16(X + (k0 + ro) * RS + col);
+  const uint2 b = lds_read_tr16(X + (k1 + ro) * RS + col);
   return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 // The A operand matching acc_to_bop(tiles, j): rows 16j + 4hi + {0..3} and
-// 16j + 8 + 4hi + {0..3} of a row-major LDS matrix, column i0 + l32.
-__device__ __forceinline__ bf16x8_t lds_aop_tr_perm(const uint16_t* X, int rs, int i0, int j, int hi) {
-  return lds_aop_tr(X, rs, i0, 16 * j + 4 * hi, 16 * j + 8 + 4 * hi);
+// 16j + 8 + 4hi + {0..3} of the tile, column i0 + l32.
+template <int RS>
+__device__ __forceinline__ bf16x8_t lds_aop_tr_perm(const uint16_t* X, int i0, int j, int hi) {
+  return lds_aop_tr<RS>(X, i0, 16 * j + 4 * hi, 16 * j + 8 + 4 * hi);
+}
+// 16-byte row read: elements col..col+7 of row r (col % 8 == 0).
+template <int RS>
+__device__ __forceinline__ bf16x8_t lds_row8(const uint16_t* X, int r, int col) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(X + r * RS + col));
+}
+template <int RS>
+__device__ __forceinline__ void lds_store_row8(uint16_t* X, int r, int col, uint4 v) {
+  *reinterpret_cast<uint4*>(X + r * RS + col) = v;
 }
 
-// Stage a 64-row block of a row-major [rows][D] bf16 matrix into LDS
-// (row stride D+8).  Rows at or beyond `valid` read as zero.  Every thread of
-// the block participates.
+// Stage a 64-row block of a row-major [rows][D] bf16 matrix into LDS tiles:
+// `rm` at the row-read stride and, when not null, `tr` at the transpose-read
+// stride.  Rows at or beyond `valid` read as zero.  Every thread of the block
+// participates.
 template <int D, int NT>
 __device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src, int valid,
-                                           uint16_t* rm, int tid) {
-  constexpr int RSTR = D + 8;
+                                           uint16_t* rm, uint16_t* tr, int tid) {
   for (int c = tid; c < 64 * (D / 8); c += NT) {
     const int row = c / (D / 8), cc = c % (D / 8);
     uint4 u = make_uint4(0, 0, 0, 0);
     if (row < valid) u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(row) * D + cc * 8);
-    *reinterpret_cast<uint4*>(&rm[row * RSTR + cc * 8]) = u;
+    if (rm) lds_store_row8<kRowStride<D>>(rm, row, cc * 8, u);
+    if (tr) lds_store_row8<kTrStride<D>>(tr, row, cc * 8, u);
   }
 }
 
