@@ -66,14 +66,18 @@ def _args():
 
 DECODE_KERNELS = ("sas::decode_split_kernel", "sas::decode_merge_kernel")
 PREFILL_KERNELS = ("sas::prefill_fwd_kernel",)
+# the sources those kernels are built from
+DECODE_SOURCES = ("decode.hip", "sas_device.h", "sas_internal.h", "sas_select_dev.h")
+PREFILL_SOURCES = ("prefill.hip", "sas_device.h", "sas_internal.h", "sas_mfma.h")
 
 
-def measured_traffic(workload, prefixes):
+def measured_traffic(workload, prefixes, sources):
     """HBM bytes per launch of the roofline kernel(s), from the committed
     PMC summary of this workload (FETCH_SIZE + WRITE_SIZE, copy-calibrated);
-    None when there is none or a kernel source changed since it was taken."""
+    None when there is none or one of the kernels' sources changed since it
+    was taken."""
     from gated_block_sparse_amd import profsum
-    blob = profsum.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"))
+    blob = profsum.load_traffic(os.path.join(ROOT, "profiles", f"traffic_{workload}.md"), sources)
     if blob is None:
         return None
     tot, hit = 0, False
@@ -343,7 +347,7 @@ def run_decode(args, wl):
         "roofline": {"bound": "hbm", "kernel": "sas_decode_fwd (split-KV + merge)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl.name, DECODE_KERNELS),
+                     "traffic": measured_traffic(wl.name, DECODE_KERNELS, DECODE_SOURCES),
                      "algorithmic_bytes": by["attention"]},
         "wall_s_timed_region": round(wall, 3),
     }
@@ -456,7 +460,7 @@ def run_prefill(args, wl):
         "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel (sas_prefill_fwd)",
                      "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(wl.name, PREFILL_KERNELS)},
+                     "traffic": measured_traffic(wl.name, PREFILL_KERNELS, PREFILL_SOURCES)},
         "roofline_bwd": {"bound": "mfma", "kernel": "sas_bwd (pre-pass, dQ, dK/dV kernels)",
                          "achieved": round(bwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4)},

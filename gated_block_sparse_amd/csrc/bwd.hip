@@ -188,7 +188,11 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ int s_count;
   __shared__ int s_wcount[NWV];
 
-  const int m = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  // Early blocks are read by many more tiles than late ones (block 0 by
+  // every tile that selects it), so the grid runs block-major across the
+  // groups: the heaviest workgroups of every group start first.
+  const int m = static_cast<int>(blockIdx.x) / Hkv, r = static_cast<int>(blockIdx.x) % Hkv;
+  const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int Hq = Hkv * G;
@@ -463,7 +467,7 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   s = check_launch("bwd_dq");
   if (s != SAS_OK) return s;
 #define SAS_DKDV_CASE(NWV)                                                                     \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles, d.n_kv_heads, d.batch),         \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),         \
                      dim3(64 * NWV), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, \
                      n_tiles, d.top_k, idx, log_gate, scale2, scale,                              \
                      static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)

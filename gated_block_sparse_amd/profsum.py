@@ -130,9 +130,10 @@ def traffic(args) -> str:
     return "\n".join(lines) + "\n"
 
 
-def load_traffic(path: str):
+def load_traffic(path: str, sources=None):
     """The JSON block of a traffic summary, or None when the file is missing
-    or any kernel source changed since the counters were taken."""
+    or a kernel source changed since the counters were taken (every source,
+    or only the named files when `sources` is given)."""
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -140,7 +141,9 @@ def load_traffic(path: str):
     if not m:
         return None
     blob = json.loads(m.group(1))
-    if blob.get("sources_sha256") != source_hashes():
+    then, now = blob.get("sources_sha256", {}), source_hashes()
+    names = list(now) if sources is None else list(sources)
+    if any(then.get(n) is None or then.get(n) != now.get(n) for n in names):
         return None
     return blob
 
