@@ -45,6 +45,17 @@ Sources are cited by page and section; the short names are:
    tile).  B0 has no gate and gets no gradient; unselected blocks get none
    (sparse scope, SAS close reading 2.3).
 
+8. Selector backward (SAS close reading 2.2, gate equation; 2.3, eq. 8, sparse
+   scope; 2.4 and the training description after it: the selector's own
+   parameters are what the loss trains): with ``dlog g`` of the selected
+   slots from step 7 and the selection held fixed, ``log g = s - LSE(s)`` gives
+   ``ds_m = dlog g_m [m in I] - g_m * sum_{l in I} dlog g_l`` over all C
+   history blocks (for ``m`` not in ``I`` this is eq. 8's sparse-scope term,
+   since ``dlog g_l = g_l dL/dg_l``), and the score definition of step 3
+   carries ``ds`` to ``Wq_sel`` and ``Wk_sel``.  The selector's own chain into
+   the backbone's Q and K is not formed: the backbone is held fixed while the
+   selector trains.
+
 Every stage is its own function so a test can feed one stage's inputs
 independently of the others.  All arithmetic is float64 NumPy; loops are kept
 per block / per head so the code reads like the definitions above.
@@ -329,6 +340,66 @@ def prefill_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray
                 if np.any(sel):
                     dlg[r, t, slot] += colsum[sel].sum()
     return dQ, dK, dV, dlg
+
+
+# --------------------------------------------------------------------------
+# 8. Selector backward
+# --------------------------------------------------------------------------
+def score_grad(s: np.ndarray, idx_row: np.ndarray, dlg_row: np.ndarray) -> np.ndarray:
+    """dL/ds for one row from the log-gate gradients of its selected slots.
+
+    log g_m = s_m - LSE(s), so d(log g_l)/d(s_m) = [l == m] - g_m and
+    dL/ds_m = sum over selected l of dlog g_l ([l == m] - g_m).
+    """
+    if s.size == 0:
+        return np.zeros(0)
+    _, logg = gate(s)
+    g = np.exp(logg)
+    total = 0.0
+    ds = np.zeros(s.size)
+    for m, dl in zip(idx_row, dlg_row):
+        if m >= 0:
+            ds[m] += dl
+            total += dl
+    return ds - g * total
+
+
+def selector_backward(Q: np.ndarray, K: np.ndarray, S: int, Wq_sel: np.ndarray,
+                      Wk_sel: np.ndarray, idx: np.ndarray, dlog_gate: np.ndarray, G: int,
+                      b: int = BLOCK):
+    """Gradients of the loss with respect to the selector weights (prefill tiles).
+
+    Q: [Hq,>=S,d], K: [Hkv,>=S,d]; idx/dlog_gate [Hkv, n_tiles, k] (the
+    selection is held fixed).  Returns (ds rows: list over tiles of [Hkv, t],
+    dWq_sel [d_sel,d], dWk_sel [d_sel,d]).
+
+    The score of tile t and block m is s = mean_{h,i} (Wq_sel q_{h,i}) . summ_m
+    / sqrt(d_sel) with summ_m = mean_{j in B_m} Wk_sel k_j, so
+      ds/dWq_sel = summ_m qbar^T / sqrt(d_sel),  qbar = mean_{h,i} q_{h,i},
+      ds/dWk_sel = (Wq_sel qbar / sqrt(d_sel)) kbar_m^T,  kbar_m = mean_{j in B_m} k_j.
+    """
+    d_sel, d = Wq_sel.shape
+    Hkv = K.shape[0]
+    n_tiles = -(-S // b)
+    summ = block_summaries(K, S, Wk_sel, b)
+    rows = tile_scores(Q, S, Wq_sel, summ, G, b)
+    dWq = np.zeros((d_sel, d))
+    dWk = np.zeros((d_sel, d))
+    ds_rows = []
+    for t in range(n_tiles):
+        i0, i1 = b * t, min(b * t + b, S)
+        ds_t = np.zeros((Hkv, t))
+        for r in range(Hkv):
+            ds = score_grad(rows[t][r], idx[r, t], dlog_gate[r, t])
+            ds_t[r] = ds
+            qbar = Q[r * G:(r + 1) * G, i0:i1].reshape(-1, d).mean(axis=0)
+            u = Wq_sel @ qbar / math.sqrt(d_sel)
+            for m in range(t):
+                kbar = K[r, b * m:b * m + b].mean(axis=0)
+                dWq += ds[m] * np.outer(summ[r, m], qbar) / math.sqrt(d_sel)
+                dWk += ds[m] * np.outer(u, kbar)
+        ds_rows.append(ds_t)
+    return ds_rows, dWq, dWk
 
 
 # --------------------------------------------------------------------------

@@ -10,6 +10,9 @@
   finite differences, plus exact identities of the backward;
 * summaries and scores on inputs with closed-form answers, a planted-key
   recall check, and decode/prefill score consistency;
+* the selector backward: dL/ds of the attention loss by central differences on
+  the scores (eq. 8's sparse-scope term for unselected blocks, sum ds = 0), and
+  dWq_sel / dWk_sel by central differences on the weights;
 * planted mistakes: each mutation of the oracle must make some pin fail.
 """
 import itertools
@@ -438,9 +441,111 @@ def test_planted_blocks_are_recalled():
 # --------------------------------------------------------------------------
 # planted mistakes: every mutation must break at least one pin
 # --------------------------------------------------------------------------
+# selector backward: finite differences through the scores and the weights
+# --------------------------------------------------------------------------
+def _sel_problem(seed, S=21, b=4, Hq=4, Hkv=2, d=8, d_sel=6, k=2):
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO = _rand_prefill(seed, Hq=Hq, Hkv=Hkv, d=d, S=S)
+    Wq = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    Wk = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    n_tiles = -(-S // b)
+    idx, _ = _random_selection(rng, Hkv, n_tiles, k)
+    return Q, K, V, dO, Wq, Wk, idx, S, b, Hq // Hkv
+
+
+def _lg_from_scores(rows, idx):
+    """log g of the selected slots from explicit score rows (softmax over the row)."""
+    Hkv, n_tiles, k = idx.shape
+    lg = np.full(idx.shape, -np.inf)
+    for t in range(n_tiles):
+        for r in range(Hkv):
+            s = rows[t][r]
+            if s.size:
+                ls = s - (s.max() + np.log(np.exp(s - s.max()).sum()))
+                for slot in range(k):
+                    if idx[r, t, slot] >= 0:
+                        lg[r, t, slot] = ls[idx[r, t, slot]]
+    return lg
+
+
+def _attn_loss_of_weights(Q, K, V, dO, S, b, G, idx, Wq, Wk, scale):
+    summ = O.block_summaries(K, S, Wk, b)
+    rows = O.tile_scores(Q, S, Wq, summ, G, b)
+    return _loss(Q, K, V, dO, S, idx, _lg_from_scores(rows, idx), scale, G, b)
+
+
+def check_selector_score_grad_fd(seed=21):
+    """dL/ds over every history block (selected or not) of the attention loss,
+    by central differences on the scores themselves; eq. 8's sparse-scope term
+    for the unselected blocks and sum_m ds_m = 0 come with it."""
+    Q, K, V, dO, Wq, Wk, idx, S, b, G = _sel_problem(seed)
+    scale = 0.43
+    summ = O.block_summaries(K, S, Wk, b)
+    rows = O.tile_scores(Q, S, Wq, summ, G, b)
+    lg = _lg_from_scores(rows, idx)
+    _, _, _, dlg = O.prefill_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    h = 1e-6
+    checked = 0
+    for t in range(len(rows)):
+        for r in range(idx.shape[0]):
+            ds = O.score_grad(rows[t][r], idx[r, t], dlg[r, t])
+            if ds.size:
+                assert abs(ds.sum()) <= 1e-12 * max(1.0, np.abs(ds).max())
+            for m in range(rows[t][r].size):
+                rp = [x.copy() for x in rows]
+                rm = [x.copy() for x in rows]
+                rp[t][r, m] += h
+                rm[t][r, m] -= h
+                fd = (_loss(Q, K, V, dO, S, idx, _lg_from_scores(rp, idx), scale, G, b) -
+                      _loss(Q, K, V, dO, S, idx, _lg_from_scores(rm, idx), scale, G, b)) / (2 * h)
+                assert abs(ds[m] - fd) <= 1e-6 * max(1.0, abs(fd)), (t, r, m, ds[m], fd)
+                if m not in idx[r, t]:
+                    g = np.exp(rows[t][r][m] - (rows[t][r].max() + np.log(
+                        np.exp(rows[t][r] - rows[t][r].max()).sum())))
+                    assert abs(ds[m] + g * dlg[r, t][idx[r, t] >= 0].sum()) <= 1e-12
+                checked += 1
+    assert checked > 20
+
+
+def check_selector_weights_fd(seed=22):
+    """dWq_sel / dWk_sel of the attention loss through gate, scores and
+    summaries, by central differences on every weight."""
+    Q, K, V, dO, Wq, Wk, idx, S, b, G = _sel_problem(seed)
+    scale = 0.39
+    summ = O.block_summaries(K, S, Wk, b)
+    rows = O.tile_scores(Q, S, Wq, summ, G, b)
+    lg = _lg_from_scores(rows, idx)
+    _, _, _, dlg = O.prefill_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    _, dWq, dWk = O.selector_backward(Q, K, S, Wq, Wk, idx, dlg, G, b)
+    h = 1e-6
+    for W, dW, which in ((Wq, dWq, "q"), (Wk, dWk, "k")):
+        fd = np.zeros_like(W)
+        for j, c in itertools.product(range(W.shape[0]), range(W.shape[1])):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[j, c] += h
+            Wm[j, c] -= h
+            args = (Wp, Wk) if which == "q" else (Wq, Wp)
+            lp = _attn_loss_of_weights(Q, K, V, dO, S, b, G, idx, *args, scale)
+            args = (Wm, Wk) if which == "q" else (Wq, Wm)
+            lm = _attn_loss_of_weights(Q, K, V, dO, S, b, G, idx, *args, scale)
+            fd[j, c] = (lp - lm) / (2 * h)
+        assert np.abs(fd).max() > 1e-4
+        np.testing.assert_allclose(dW, fd, atol=1e-6 * np.abs(fd).max(), rtol=1e-5)
+
+
+def test_selector_score_gradient_matches_finite_differences():
+    check_selector_score_grad_fd()
+
+
+def test_selector_weight_gradients_match_finite_differences():
+    check_selector_weights_fd()
+
+
+# --------------------------------------------------------------------------
 PINS = [check_hand_worked, check_topk_lexsort, check_topk_exhaustive, check_gather_vs_dense,
         check_uniform_gate_is_dense_with_bias, check_k0_is_local_causal, check_dlog_gate_fd,
-        check_qkv_grads_fd, check_summaries]
+        check_qkv_grads_fd, check_summaries, check_selector_score_grad_fd,
+        check_selector_weights_fd]
 
 
 def _some_pin_fails():
@@ -469,7 +574,16 @@ def _summaries_sum_not_mean(K, T, Wk, b=O.BLOCK):
 
 
 _ORIG = {"gate": O.gate, "topk": O.topk, "block_summaries": O.block_summaries,
-         "_selected_tokens": O._selected_tokens}
+         "_selected_tokens": O._selected_tokens, "score_grad": O.score_grad}
+
+
+def _score_grad_no_normaliser(s, idx_row, dlg_row):
+    """Forgets the -g_m sum dlog g term of the log-softmax."""
+    out = np.zeros(s.size)
+    for m, dl in zip(idx_row, dlg_row):
+        if m >= 0:
+            out[m] += dl
+    return out
 
 
 def _drop_gate_bias(idx_row, lg_row, b, gated):
@@ -487,6 +601,7 @@ def _off_by_one_block(idx_row, lg_row, b, gated):
     ("block_summaries", _summaries_sum_not_mean),
     ("_selected_tokens", _drop_gate_bias),
     ("_selected_tokens", _off_by_one_block),
+    ("score_grad", _score_grad_no_normaliser),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
