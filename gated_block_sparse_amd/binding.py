@@ -21,7 +21,7 @@ SAS_OK, SAS_ERR_INVALID_ARGUMENT, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE_TOO_SMA
 SAS_F32, SAS_BF16 = 0, 1
 SAS_SELECT_DECODE, SAS_SELECT_TILES = 0, 1
 (SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD,
- SAS_OP_DECODE_STEP) = range(6)
+ SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD) = range(7)
 BLOCK = 64
 SIZE_MAX = 2 ** 64 - 1
 
@@ -49,6 +49,8 @@ _SIGNATURES = {
     "sas_prefill_fwd": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sas_bwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
                        _vp, _vp, _sz, _vp]),
+    "sas_selector_bwd": (_i32, [_PD, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _sz, _vp]),
     "sas_workspace_bytes": (_sz, [_i32, _PD, _i32]),
     "sas_status_str": (ctypes.c_char_p, [_i32]),
     "sas_last_error": (ctypes.c_char_p, []),
@@ -271,3 +273,32 @@ def sas_bwd(Q, K, V, O, dO, lse, idx, log_gate, scale=None, seq_len=None, dQ=Non
                                   _ptr(dK), _ptr(dV), _ptr(dlog_gate), _ptr(ws), ws_bytes,
                                   _stream()))
     return dQ, dK, dV, dlog_gate
+
+
+def sas_selector_bwd(Q, K, Wq_sel, summ, idx, score_lse, dlog_gate, q_len=None, t_max=None,
+                     ds=None, want_ds=False, dWq=None, dWk=None, ws=None):
+    """Selector weight gradients for the tile rows of a prefill.  Q [B,Hq,S,d];
+    K [B,Hkv,t_max,d]; summ [B,Hkv,t_max//64,d_sel]; idx/dlog_gate [B,Hkv,rows,k];
+    score_lse [B,Hkv,rows].  Returns (dWq_sel, dWk_sel, ds | None)."""
+    B, Hq, S, d = Q.shape
+    _, Hkv, tm, _ = K.shape
+    t_max = tm if t_max is None else t_max
+    q_len = S if q_len is None else q_len
+    ds_dim = Wq_sel.shape[0]
+    k = idx.shape[-1]
+    rows = -(-q_len // BLOCK)
+    dims = make_dims(B, Hq, Hkv, d, ds_dim, k, t_max, _dtype_code(Q))
+    dev = Q.device
+    if want_ds and ds is None:
+        ds = torch.full((B, Hkv, rows, t_max // BLOCK), float("nan"), dtype=torch.float32,
+                        device=dev)
+    if dWq is None:
+        dWq = torch.empty_like(Wq_sel)
+    if dWk is None:
+        dWk = torch.empty_like(Wq_sel)
+    ws, ws_bytes = _workspace(SAS_OP_SELECTOR_BWD, dims, q_len, ws, dev)
+    _check(load_library().sas_selector_bwd(ctypes.byref(dims), _ptr(Q), q_len, _ptr(K),
+                                           _ptr(Wq_sel), _ptr(summ), _ptr(idx), _ptr(score_lse),
+                                           _ptr(dlog_gate), _ptr(ds), _ptr(dWq), _ptr(dWk),
+                                           _ptr(ws), ws_bytes, _stream()))
+    return dWq, dWk, ds

@@ -224,6 +224,31 @@ sas_status sas_bwd(const sas_dims* dims, const void* Q, const void* K, const voi
                     dlog_gate, ws, static_cast<hipStream_t>(stream));
 }
 
+sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, const void* K,
+                            const float* Wq_sel, const float* summ, const int32_t* idx,
+                            const float* score_lse, const float* dlog_gate, float* ds,
+                            float* dWq_sel, float* dWk_sel, void* ws, size_t ws_bytes,
+                            void* stream) {
+  SAS_TRY(check_dims(dims, false));
+  SAS_TRY(check_len(dims, q_len, "q_len"));
+  if (cdiv(q_len, kBlock) > kMaxTileRows)
+    return fail(SAS_ERR_UNSUPPORTED, "q_len=%d gives more than %d tiles", q_len, kMaxTileRows);
+  SAS_NONNULL(Q);
+  SAS_NONNULL(K);
+  SAS_NONNULL(Wq_sel);
+  SAS_NONNULL(score_lse);
+  SAS_NONNULL(dWq_sel);
+  SAS_NONNULL(dWk_sel);
+  if (dims->t_max >= kBlock) SAS_NONNULL(summ);
+  if (dims->top_k > 0) {
+    SAS_NONNULL(idx);
+    SAS_NONNULL(dlog_gate);
+  }
+  SAS_TRY(check_ws(selector_bwd_ws_bytes(*dims, q_len), ws, ws_bytes));
+  return launch_selector_bwd(*dims, Q, q_len, K, Wq_sel, summ, idx, score_lse, dlog_gate, ds,
+                             dWq_sel, dWk_sel, ws, static_cast<hipStream_t>(stream));
+}
+
 size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
   const bool bf16_only = (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD);
   if (check_dims(dims, bf16_only) != SAS_OK) return SIZE_MAX;
@@ -232,6 +257,9 @@ size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
     case SAS_OP_SELECT_TILES: return 0;
     case SAS_OP_DECODE_FWD: return decode_ws_bytes(*dims);
     case SAS_OP_DECODE_STEP: return decode_step_ws_bytes(*dims);
+    case SAS_OP_SELECTOR_BWD:
+      if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
+      return selector_bwd_ws_bytes(*dims, q_len);
     case SAS_OP_PREFILL_FWD:
       if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
       return prefill_ws_bytes(*dims, q_len);

@@ -80,6 +80,12 @@ sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, c
                               int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st);
 
+size_t selector_bwd_ws_bytes(const sas_dims& d, int q_len);
+sas_status launch_selector_bwd(const sas_dims& d, const void* Q, int q_len, const void* K,
+                               const float* Wq, const float* summ, const int32_t* idx,
+                               const float* score_lse, const float* dlg, float* ds, float* dWq,
+                               float* dWk, void* ws, hipStream_t st);
+
 size_t prefill_ws_bytes(const sas_dims& d, int seq_len);
 sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,
                               int seq_len, const int32_t* idx, const float* log_gate,

@@ -22,68 +22,6 @@
 
 namespace sas {
 
-constexpr int kSelThreads = 256;
-
-// qs[j] = (Wq[j,:] . qm) / sqrt(DS), for j < DS (threads tid < DS).
-template <int D, int DS>
-__device__ __forceinline__ void project_query(const float* __restrict__ Wq, const float* qm,
-                                              float* qs) {
-  const int tid = threadIdx.x;
-  if (tid < DS) {
-    const float4* w = reinterpret_cast<const float4*>(Wq + static_cast<size_t>(tid) * D);
-    float acc = 0.f;
-#pragma unroll 8
-    for (int c4 = 0; c4 < D / 4; ++c4) {
-      const float4 x = w[c4];
-      acc += x.x * qm[4 * c4 + 0];
-      acc += x.y * qm[4 * c4 + 1];
-      acc += x.z * qm[4 * c4 + 2];
-      acc += x.w * qm[4 * c4 + 3];
-    }
-    qs[tid] = acc * (1.0f / sqrtf(static_cast<float>(DS)));
-  }
-}
-
-// Scores of blocks [0, n) of one (b, r) (rows of summ_row0) into sc[0..n).
-// Each half wave owns 32 rows per round (rows hw + 8j, j < 32): all 32
-// 16-byte loads are issued before any arithmetic, then a transposed butterfly
-// (16+8+4+2+1 shuffles) leaves the full dot of row j in lane j.
-template <int DS>
-__device__ __forceinline__ void score_rows(const float* __restrict__ summ_row0, const float* qs,
-                                           int n, float* sc) {
-  constexpr int PL = DS / 32;  // floats per lane (2 or 4)
-  const int tid = threadIdx.x, hw = tid >> 5, l32 = tid & 31;
-  float qv[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) qv[e] = qs[l32 * PL + e];
-  for (int base = 0; base < n; base += 32 * (kSelThreads / 32)) {
-    float v[32];
-    if constexpr (PL == 4) {
-      float4 x[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int i = base + hw + 8 * j;
-        x[j] = i < n ? *reinterpret_cast<const float4*>(summ_row0 + static_cast<size_t>(i) * DS + l32 * PL)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = x[j].x * qv[0] + x[j].y * qv[1] + x[j].z * qv[2] + x[j].w * qv[3];
-    } else {
-      float2 x[32];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int i = base + hw + 8 * j;
-        x[j] = i < n ? *reinterpret_cast<const float2*>(summ_row0 + static_cast<size_t>(i) * DS + l32 * PL)
-                     : make_float2(0.f, 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = x[j].x * qv[0] + x[j].y * qv[1];
-    }
-    transpose_sum32(v, l32);
-    const int i = base + hw + 8 * l32;
-    if (i < n) sc[i] = v[0];
-  }
-}
 
 // ------------------------------------------------------------- decode ---
 // Chunk kernel: grid (chunk, group, sequence), kSelChunk blocks per chunk.
@@ -323,10 +261,7 @@ select_tiles_kernel(const T* __restrict__ Q, int q_len, const float* __restrict_
                     const float* __restrict__ summ, int Hkv, int c_max, int rows, int k,
                     int32_t* __restrict__ idx, float* __restrict__ log_gate,
                     float* __restrict__ score_lse, float* __restrict__ scores) {
-  constexpr int EPL = Vec16<T>::N;
-  constexpr int LPR = D / EPL;
-  constexpr int RG = kSelThreads / LPR;  // row groups
-  __shared__ float qpart[RG][D];
+  __shared__ float qpart[kSelThreads / (D / Vec16<T>::N)][D];
   __shared__ float qm[D];
   __shared__ float qs[DS];
   __shared__ float sc[kMaxTileRows];
@@ -339,31 +274,7 @@ select_tiles_kernel(const T* __restrict__ Q, int q_len, const float* __restrict_
   const int nq = min(kBlock, q_len - i0);
   const size_t row = (static_cast<size_t>(b) * Hkv + r) * rows + t;
 
-  // pooled query over the group's G heads and the tile's nq queries
-  {
-    const int col = tid % LPR, rg = tid / LPR;
-    float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    const int nrows = G * nq;
-    for (int x = rg; x < nrows; x += RG) {
-      const int h = r * G + x / nq, i = i0 + x % nq;
-      const T* src = Q + ((static_cast<size_t>(b) * Hkv * G + h) * q_len + i) * D + col * EPL;
-      float f[EPL];
-      Vec16<T>::unpack(*reinterpret_cast<const uint4*>(src), f);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += f[e];
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qpart[rg][col * EPL + e] = acc[e];
-  }
-  __syncthreads();
-  if (tid < D) {
-    float a = 0.f;
-    for (int g = 0; g < RG; ++g) a += qpart[g][tid];
-    qm[tid] = a / static_cast<float>(G * nq);
-  }
-  __syncthreads();
+  tile_pooled_query<T, D, G>(Q, q_len, Hkv, b, r, i0, nq, &qpart[0][0], qm);
   project_query<D, DS>(Wq, qm, qs);
   __syncthreads();
 

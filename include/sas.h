@@ -77,7 +77,8 @@ typedef enum {
   SAS_OP_DECODE_FWD = 2,
   SAS_OP_PREFILL_FWD = 3,
   SAS_OP_BWD = 4,
-  SAS_OP_DECODE_STEP = 5
+  SAS_OP_DECODE_STEP = 5,
+  SAS_OP_SELECTOR_BWD = 6
 } sas_op;
 
 /* Problem sizes.  Supported: block_size 64; head_dim and sel_dim 64 or 128;
@@ -189,6 +190,34 @@ sas_status sas_bwd(const sas_dims* dims, const void* Q, const void* K, const voi
                    const void* O, const void* dO, const float* lse, int32_t seq_len,
                    const int32_t* idx, const float* log_gate, float scale, void* dQ, void* dK,
                    void* dV, float* dlog_gate, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of the selector into its weights, for the tile rows of a prefill
+ * (SAS close reading 2.2, gate equation; 2.3, eq. 8, sparse scope; 2.4 and
+ * the training description after it).  With the selection held fixed and
+ * dlog_gate of the selected slots (from sas_bwd), for each row t of group r
+ * and each of its C = t history blocks m:
+ *     ds_m = dlog_gate[slot of m] [m selected] - g_m * sum_slots dlog_gate,
+ *     g_m  = exp(s_m - score_lse),
+ * and through s_m = (Wq_sel qbar) . summ_m / sqrt(d_sel), summ_m = Wk_sel kbar_m
+ * (qbar: mean of the tile's queries over the group's heads; kbar_m: mean key
+ * of block m):
+ *     dWq_sel = sum over rows and m of ds_m summ_m qbar^T / sqrt(d_sel),
+ *     dWk_sel = sum over rows and m of ds_m (Wq_sel qbar / sqrt(d_sel)) kbar_m^T.
+ * The chain into Q and K through the selector is not formed (the backbone is
+ * held fixed while the selector trains).
+ * Q: dtype [B,Hq,q_len,d]; K: dtype [B,Hkv,t_max,d]; Wq_sel fp32 [d_sel,d];
+ * summ fp32 [B,Hkv,t_max/64,d_sel] (sas_block_summaries of K); idx/dlog_gate
+ * [B,Hkv,rows,k] and score_lse [B,Hkv,rows] (sas_select in SAS_SELECT_TILES
+ * mode, then sas_bwd); rows = ceil(q_len/64) <= 1024, q_len <= t_max.
+ * ds (nullable) fp32 [B,Hkv,rows,t_max/64]: entries m < t of row t are written.
+ * dWq_sel, dWk_sel fp32 [d_sel,d] are overwritten (summed over the batch).
+ * Results are bitwise reproducible (no atomics).
+ * ws: at least sas_workspace_bytes(SAS_OP_SELECTOR_BWD, dims, q_len). */
+sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, const void* K,
+                            const float* Wq_sel, const float* summ, const int32_t* idx,
+                            const float* score_lse, const float* dlog_gate, float* ds,
+                            float* dWq_sel, float* dWk_sel, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* Workspace bytes an op needs for these sizes (q_len: prefill/tiles length,
  * ignored otherwise).  Returns SIZE_MAX if the sizes are invalid or

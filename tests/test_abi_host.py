@@ -104,6 +104,26 @@ def test_decode_step_validation(lib):
     assert step(_dims(head_dim=96), 1 << 40) == B.SAS_ERR_UNSUPPORTED
 
 
+def test_selector_bwd_validation(lib):
+    d = _dims()
+    need = B.sas_workspace_bytes(B.SAS_OP_SELECTOR_BWD, d, 16384)
+    # ds of every (row, block), then per row a_row, qbar, u, then per block e_m, kbar_m
+    rows, grp, c_max = 256, 8, 65536 // 64
+    sel = (grp * rows * c_max * 4 + 255) // 256 * 256
+    rowb = (grp * rows * (2 * 128 + 128) * 4 + 255) // 256 * 256
+    assert need == sel + rowb + grp * rows * (128 + 128) * 4
+    sb = lambda dims, q_len, ws_bytes, dlg=FAKE, dwk=FAKE: lib.sas_selector_bwd(
+        ctypes.byref(dims), FAKE, q_len, FAKE, FAKE, FAKE, FAKE, FAKE, dlg, None, FAKE, dwk,
+        FAKE, ws_bytes, None)
+    assert sb(d, 16384, need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+    assert sb(d, 0, need) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sb(d, 65537, 1 << 40) == B.SAS_ERR_INVALID_ARGUMENT     # q_len > t_max
+    assert sb(d, 16384, need, dlg=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sb(d, 16384, need, dwk=None) == B.SAS_ERR_INVALID_ARGUMENT
+    big = _dims(t_max=64 * 1025 * 64)
+    assert sb(big, 64 * 1025, 1 << 40) == B.SAS_ERR_UNSUPPORTED
+
+
 def test_prefill_and_bwd_validation(lib):
     d = _dims()
     pf = lambda dims, seq_len: lib.sas_prefill_fwd(ctypes.byref(dims), FAKE, FAKE, FAKE, seq_len,
