@@ -21,8 +21,8 @@ Inputs are resident in HBM before timing starts.  Each timed step is
 bracketed by HIP events on the stream the library launches on; between steps
 (outside the events) a 512 MiB write and a 1 GiB read sweep evict the L2s and
 the 256 MB Infinity Cache, so every step reads its bytes from HBM.
-``--workload qwen3_4b_prefill_16k`` times the training-style prefill forward +
-backward instead.
+``--workload qwen3_4b_prefill_16k`` times the training-style prefill forward,
+backward and selector backward instead.
 
 Extra fields beside the contract keys: ``breakdown_us`` (per-op medians),
 ``roofline`` for the dominant kernel, ``cpu_baseline`` (the float64 CPU
@@ -405,6 +405,8 @@ def run_prefill(args, wl):
     ws_sel = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_SELECT_TILES, dims, S)), dtype=torch.uint8, device=dev)
     ws_fwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_PREFILL_FWD, dims, S)), dtype=torch.uint8, device=dev)
     ws_bwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_BWD, dims, S)), dtype=torch.uint8, device=dev)
+    ws_sb = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_SELECTOR_BWD, dims, S)), dtype=torch.uint8, device=dev)
+    dWq, dWk = torch.empty_like(Wq), torch.empty_like(Wq)
 
     def step(evs=None):
         rec = (lambda i: evs[i].record(stream)) if evs else (lambda i: None)
@@ -417,12 +419,14 @@ def run_prefill(args, wl):
         rec(2)
         Sb.sas_bwd(Q, K, V, O, dO, lse, idx, lg, dQ=dQ, dK=dK, dV=dV, dlog_gate=dlg, ws=ws_bwd)
         rec(3)
+        Sb.sas_selector_bwd(Q, K, Wq, summ, idx, slse, dlg, dWq=dWq, dWk=dWk, ws=ws_sb)
+        rec(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     n = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n)]
     t0 = time.perf_counter()
     for i in range(n):
         if not args.no_flush:
@@ -433,7 +437,8 @@ def run_prefill(args, wl):
     t_sel = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
     t_fwd = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
     t_bwd = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
-    tot = [e[0].elapsed_time(e[3]) * 1e3 for e in evs]
+    t_sb = [e[3].elapsed_time(e[4]) * 1e3 for e in evs]
+    tot = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
     med = statistics.median
     us_fwd, us_bwd, us_step = med(t_fwd), med(t_bwd), med(tot)
     fwd_tf = fwd_flop / (us_fwd * 1e-6) / 1e12
@@ -454,6 +459,7 @@ def run_prefill(args, wl):
             "summaries_and_select": round(med(t_sel), 2),
             "prefill_fwd": {"median": round(us_fwd, 2), "p10": round(_pct(t_fwd, .1), 2), "p90": round(_pct(t_fwd, .9), 2)},
             "bwd": {"median": round(us_bwd, 2), "p10": round(_pct(t_bwd, .1), 2), "p90": round(_pct(t_bwd, .9), 2)},
+            "selector_bwd": {"median": round(med(t_sb), 2), "p10": round(_pct(t_sb, .1), 2), "p90": round(_pct(t_sb, .9), 2)},
         },
         "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
         "bwd_TFLOPs": round(bwd_tf, 1),
