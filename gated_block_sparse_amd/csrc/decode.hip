@@ -206,35 +206,37 @@ template <typename T, int D, int G, int NB>
 __global__ void __launch_bounds__(kDecThreads)
 decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
                     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
-                    const float* __restrict__ log_gate, float scale2, int Hkv, int t_max, int k,
-                    float* __restrict__ part) {
+                    const float* __restrict__ log_gate, int gated, float scale2, int Hkv,
+                    int t_max, int k, float* __restrict__ part) {
   constexpr int PF = DecPartial<G, D>::kFloats;
   __shared__ SplitLds<G, D> sh;
   const int unit = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  const int len = clamp_len(seq_lens[b], t_max);
-  const int C = (len - 1) / kBlock;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const int n_units = (k + NB) / NB;   // ceil((k + 1) / NB)
+  // All the small loads of the unit are issued together, with no branch
+  // between them (slot indices clamped into range; idx and log_gate always
+  // point at readable memory, see the launcher), so they cost one memory
+  // round trip before the K/V loads instead of a chain of them.
+  int mi[NB];
+  float lgi[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const size_t at = row * k + min(unit * NB + bb, k > 0 ? k - 1 : 0);
+    mi[bb] = idx[at];
+    lgi[bb] = log_gate[at];
+  }
+  const int len = clamp_len(seq_lens[b], t_max);
+  const int C = (len - 1) / kBlock;
   // the NB slots of this unit: history slots u < k, then B0 as slot k
   int start[NB], ntok[NB];
   float beta2[NB];  // bias, already multiplied by log2(e)
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
     const int u = unit * NB + bb;
-    start[bb] = 0;
-    ntok[bb] = 0;
-    beta2[bb] = 0.f;
-    if (u < k) {
-      const int m = idx[row * k + u];
-      if (m >= 0) {
-        start[bb] = m * kBlock;
-        ntok[bb] = kBlock;
-        if (log_gate) beta2[bb] = log_gate[row * k + u] * kLog2e;
-      }
-    } else if (u == k) {
-      start[bb] = C * kBlock;
-      ntok[bb] = len - start[bb];
-    }
+    const bool hist = u < k && mi[bb] >= 0, cur = u == k;
+    start[bb] = hist ? mi[bb] * kBlock : (cur ? C * kBlock : 0);
+    ntok[bb] = hist ? kBlock : (cur ? len - C * kBlock : 0);
+    beta2[bb] = (hist && gated) ? lgi[bb] * kLog2e : 0.f;
   }
   split_unit<T, D, G, NB>(q, K, V, row, t_max, start, ntok, beta2, scale2,
                           part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
@@ -375,10 +377,15 @@ static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K,
                                 void* ws, hipStream_t st) {
   float* part = static_cast<float*>(ws);
   const int n_units = (d.top_k + NB) / NB;
+  // k = 0 or the ungated rule may pass NULL idx / log_gate: the kernel then
+  // reads (and ignores) seq_lens in their place, so its loads need no branch
+  const int32_t* idx_r = d.top_k > 0 ? idx : seq_lens;
+  const float* lg_r = (d.top_k > 0 && log_gate) ? log_gate : reinterpret_cast<const float*>(idx_r);
   hipLaunchKernelGGL((decode_split_kernel<T, D, G, NB>), dim3(n_units, d.n_kv_heads, d.batch),
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
-                     static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx, log_gate,
-                     scale * kLog2e, d.n_kv_heads, d.t_max, d.top_k, part);
+                     static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx_r, lg_r,
+                     log_gate != nullptr ? 1 : 0, scale * kLog2e, d.n_kv_heads, d.t_max,
+                     d.top_k, part);
   sas_status s = check_launch("decode_split");
   if (s != SAS_OK) return s;
   constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
