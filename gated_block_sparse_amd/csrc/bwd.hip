@@ -171,14 +171,15 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
   constexpr int NT = 64 * NWV;
   constexpr int KS = D / 16, CT = D / 32;
-  // K rows then V rows (row reads); reused at the end for the cross-wave
-  // dK/dV sum (64 x (D + 1) floats fit in 2 x 64 x (D + 8) bf16)
+  // One LDS arena: K rows and V rows (row reads), then per wave the 32 query
+  // rows of Q and dO of the current half tile (transpose reads).  At the end
+  // it is reused for the cross-wave dK/dV sum: NWV x 32 x (D + 1) floats.
   constexpr int RS = kRowStride<D>, TS = kTrStride<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * 64 * RS];
-  uint16_t* const Ks = KVs;
-  uint16_t* const Vs = KVs + 64 * RS;
-  __shared__ __attribute__((aligned(16))) uint16_t Qw[NWV][32 * TS];   // per wave: 32 query rows
-  __shared__ __attribute__((aligned(16))) uint16_t dOw[NWV][32 * TS];
+  constexpr int kArena = 2 * 64 * RS + 2 * NWV * 32 * TS;   // bf16 elements
+  static_assert(NWV * 32 * (D + 1) * 4 <= kArena * 2, "reduction buffer");
+  __shared__ __attribute__((aligned(16))) uint16_t arena[kArena];
+  uint16_t* const Ks = arena;
+  uint16_t* const Vs = arena + 64 * RS;
   __shared__ int list_t[kMaxTileRows];
   __shared__ int list_slot[kMaxTileRows];
   __shared__ float dsum_s[NWV][kMaxTileRows];
@@ -256,8 +257,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       zero16(dk[tt][ct]);
       zero16(dv[tt][ct]);
     }
-  uint16_t* qt_s = Qw[wave];
-  uint16_t* dot_s = dOw[wave];
+  uint16_t* qt_s = arena + 2 * 64 * RS + wave * 32 * TS;
+  uint16_t* dot_s = arena + 2 * 64 * RS + (NWV + wave) * 32 * TS;
 
   // lse and D of the wave's next (entry, head) pair are loaded one pair
   // ahead, so their memory latency overlaps the current pair's work
@@ -385,42 +386,43 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int w = 0; w < NWV; ++w) tot += dsum_s[w][e];
     dlg[(grow * n_tiles + list_t[e]) * k + list_slot[e]] = tot;
   }
-  // ---- sum dK^T / dV^T over the waves (through LDS, wave by wave), store
-  float* red = reinterpret_cast<float*>(KVs);   // [64][D + 1]: the pad spreads a column over the banks
+  // ---- sum dK^T / dV^T over the waves and store: per (tensor, 32-token
+  // half) every wave writes its tiles to its own slice of the arena at once,
+  // then all threads add the slices in wave order and store bf16 rows.
+  float* red = reinterpret_cast<float*>(arena);   // [NWV][32][D + 1]
+  constexpr int RSTR = D + 1;                     // the pad spreads a column over the banks
+#pragma unroll
   for (int which = 0; which < 2; ++which) {
-    for (int w = 0; w < NWV; ++w) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
       __syncthreads();
-      if (wave == w) {
+      float* mine = red + wave * 32 * RSTR;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
+        for (int v = 0; v < 16; ++v)
+          mine[l32 * RSTR + 32 * ct + acc_row(v, hi)] = which ? dv[tt][ct][v] : dk[tt][ct][v];
+      __syncthreads();
+      uint16_t* dst = which ? dV : dK;
+      const float mul = which ? 1.f : scale;
+      for (int i = tid; i < 32 * (D / 4); i += NT) {
+        const int tl = i / (D / 4), c4 = (i % (D / 4)) * 4;
+        const int tok = 32 * tt + tl;
+        if (tok0 + tok < S) {
+          uint32_t wv[4];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int tok = 32 * tt + l32, c = 32 * ct + acc_row(v, hi);
-              const float x = which ? dv[tt][ct][v] : dk[tt][ct][v];
-              float* slotp = &red[tok * (D + 1) + c];
-              *slotp = (w == 0) ? x : *slotp + x;
-            }
-      }
-    }
-    __syncthreads();
-    uint16_t* dst = which ? dV : dK;
-    const float mul = which ? 1.f : scale;
-    for (int i = tid; i < 64 * (D / 4); i += NT) {
-      const int tok = i / (D / 4), c4 = (i % (D / 4)) * 4;
-      if (tok0 + tok < S) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          uint32_t u = __float_as_uint(red[tok * (D + 1) + c4 + e4] * mul);
-          u += 0x7FFFu + ((u >> 16) & 1u);
-          wv[e4] = u >> 16;
+          for (int e4 = 0; e4 < 4; ++e4) {
+            float x = 0.f;
+            for (int w = 0; w < NWV; ++w) x += red[(w * 32 + tl) * RSTR + c4 + e4];
+            uint32_t u = __float_as_uint(x * mul);
+            u += 0x7FFFu + ((u >> 16) & 1u);
+            wv[e4] = u >> 16;
+          }
+          uint2 pk;
+          pk.x = wv[0] | (wv[1] << 16);
+          pk.y = wv[2] | (wv[3] << 16);
+          *reinterpret_cast<uint2*>(dst + (grow * t_max + tok0 + tok) * D + c4) = pk;
         }
-        uint2 pk;
-        pk.x = wv[0] | (wv[1] << 16);
-        pk.y = wv[2] | (wv[3] << 16);
-        *reinterpret_cast<uint2*>(dst + (grow * t_max + tok0 + tok) * D + c4) = pk;
       }
     }
   }

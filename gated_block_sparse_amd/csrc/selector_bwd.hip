@@ -16,7 +16,8 @@
 //      ds, a_row;
 //   2. one workgroup per history block: kbar_m and e_m (a sum over the rows
 //      that see the block);
-//   3. one thread per weight: the two sums above.
+//   3. the two sums above: chunk partials of the outer products, then their
+//      sum in chunk order.
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_select_dev.h"
@@ -72,14 +73,16 @@ selector_bwd_rows_kernel(const T* __restrict__ Q, int q_len, const float* __rest
   // a_row = sum_m ds_m summ_m; qbar and u for the weight sums
   float* rd = rowdat + row * SelRow<D, DS>::kFloats;
   if (tid < DS) {
-    float a0 = 0.f, a1 = 0.f;
+    // 8 independent accumulators: eight summary loads in flight at a time
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int m = 0;
-    for (; m + 1 < C; m += 2) {
-      a0 = fmaf(sc[m], srow[static_cast<size_t>(m) * DS + tid], a0);
-      a1 = fmaf(sc[m + 1], srow[static_cast<size_t>(m + 1) * DS + tid], a1);
+    for (; m + 7 < C; m += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        a[u] = fmaf(sc[m + u], srow[static_cast<size_t>(m + u) * DS + tid], a[u]);
     }
-    if (m < C) a0 = fmaf(sc[m], srow[static_cast<size_t>(m) * DS + tid], a0);
-    rd[tid] = a0 + a1;
+    for (; m < C; ++m) a[0] = fmaf(sc[m], srow[static_cast<size_t>(m) * DS + tid], a[0]);
+    rd[tid] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     rd[DS + D + tid] = qs[tid];
   }
   if (tid < D) rd[DS + tid] = qm[tid];
@@ -111,57 +114,95 @@ selector_bwd_blocks_kernel(const T* __restrict__ K, int Hkv, int t_max, int c_ma
   }
   // e_m = sum over the rows that see block m (tiles t > m) of ds_(t, m) u_t
   if (tid < DS) {
-    float e0 = 0.f, e1 = 0.f;
+    // 8 independent accumulators: eight rows' loads in flight at a time
+    float e[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    constexpr int F = SelRow<D, DS>::kFloats;
     int t = m + 1;
-    for (; t + 1 < rows; t += 2) {
-      const size_t r0 = grp * rows + t;
-      e0 = fmaf(ds_ws[r0 * c_max + m], rowdat[r0 * SelRow<D, DS>::kFloats + DS + D + tid], e0);
-      e1 = fmaf(ds_ws[(r0 + 1) * c_max + m],
-                rowdat[(r0 + 1) * SelRow<D, DS>::kFloats + DS + D + tid], e1);
+    for (; t + 7 < rows; t += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const size_t r0 = grp * rows + t + u;
+        e[u] = fmaf(ds_ws[r0 * c_max + m], rowdat[r0 * F + DS + D + tid], e[u]);
+      }
     }
-    if (t < rows) {
+    for (; t < rows; ++t) {
       const size_t r0 = grp * rows + t;
-      e0 = fmaf(ds_ws[r0 * c_max + m], rowdat[r0 * SelRow<D, DS>::kFloats + DS + D + tid], e0);
+      e[0] = fmaf(ds_ws[r0 * c_max + m], rowdat[r0 * F + DS + D + tid], e[0]);
     }
-    bd[tid] = e0 + e1;
+    bd[tid] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
   }
 }
 
-// dWq[j][c] (blockIdx.y == 0) or dWk[j][c] (blockIdx.y == 1), row j =
-// blockIdx.x, column c = threadIdx.x.
+// The weight sums, in two fixed-order stages.  Stage 1: workgroup (chunk,
+// which) adds the outer products of up to kSbChunk entries (rows for dWq,
+// history blocks for dWk) into a partial [DS][D] in the workspace; thread
+// (c, half) keeps the DS/2 rows j of column c in registers, and the entries'
+// vectors are staged in LDS.  Stage 2: one thread per weight adds the
+// chunk partials in chunk order.
+constexpr int kSbChunk = 64;
+
+template <int D, int DS>
+__global__ void __launch_bounds__(2 * D)
+selector_bwd_partial_kernel(int n_groups, int rows, const float* __restrict__ rowdat,
+                            const float* __restrict__ blkdat, float* __restrict__ partial) {
+  constexpr int JH = DS / 2;
+  __shared__ float left[kSbChunk][DS];
+  __shared__ float right[kSbChunk][D];
+  const int which = blockIdx.y, chunk = blockIdx.x;
+  const int c = threadIdx.x % D, half = threadIdx.x / D;
+  // entries of this chunk: rows (dWq) or history blocks m < rows - 1 (dWk)
+  const int per_group = which == 0 ? rows : rows - 1;
+  const int n_entries = n_groups * per_group;
+  const int e0 = chunk * kSbChunk, ne = min(kSbChunk, n_entries - e0);
+  auto entry_ptr = [&](int e) -> const float* {
+    const int g = e / per_group, i = e % per_group;
+    return which == 0 ? rowdat + (static_cast<size_t>(g) * rows + i) * SelRow<D, DS>::kFloats
+                      : blkdat + (static_cast<size_t>(g) * rows + i) * SelBlk<D, DS>::kFloats;
+  };
+  for (int x = threadIdx.x; x < ne * DS; x += 2 * D) left[x / DS][x % DS] = entry_ptr(e0 + x / DS)[x % DS];
+  for (int x = threadIdx.x; x < ne * D; x += 2 * D) right[x / D][x % D] = entry_ptr(e0 + x / D)[DS + x % D];
+  __syncthreads();
+  float acc[JH];
+#pragma unroll
+  for (int j = 0; j < JH; ++j) acc[j] = 0.f;
+  for (int e = 0; e < ne; ++e) {
+    const float rv = right[e][c];   // qbar (dWq) or kbar (dWk)
+#pragma unroll
+    for (int j = 0; j < JH; ++j) acc[j] = fmaf(left[e][half * JH + j], rv, acc[j]);
+  }
+  float* out = partial + ((static_cast<size_t>(which) * gridDim.x + chunk) * DS + half * JH) * D + c;
+#pragma unroll
+  for (int j = 0; j < JH; ++j) out[static_cast<size_t>(j) * D] = acc[j];
+}
+
 template <int D, int DS>
 __global__ void __launch_bounds__(D)
-selector_bwd_weights_kernel(int n_groups, int rows, const float* __restrict__ rowdat,
-                            const float* __restrict__ blkdat, float* __restrict__ dWq,
-                            float* __restrict__ dWk) {
-  const int j = blockIdx.x, c = threadIdx.x;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-  if (blockIdx.y == 0) {
-    constexpr int F = SelRow<D, DS>::kFloats;
-    const int n = n_groups * rows;
-    for (int x = 0; x < n; ++x) a[x & 3] = fmaf(rowdat[x * F + j], rowdat[x * F + DS + c], a[x & 3]);
-    dWq[j * D + c] = ((a[0] + a[1]) + (a[2] + a[3])) * (1.0f / sqrtf(static_cast<float>(DS)));
-  } else {
-    constexpr int F = SelBlk<D, DS>::kFloats;
-    for (int g = 0; g < n_groups; ++g)
-      for (int m = 0; m + 1 < rows; ++m) {
-        const int x = g * rows + m;
-        a[m & 3] = fmaf(blkdat[x * F + j], blkdat[x * F + DS + c], a[m & 3]);
-      }
-    dWk[j * D + c] = (a[0] + a[1]) + (a[2] + a[3]);
-  }
+selector_bwd_weights_kernel(int n_chunks, const float* __restrict__ partial,
+                            float* __restrict__ dWq, float* __restrict__ dWk) {
+  const int which = blockIdx.y, j = blockIdx.x, c = threadIdx.x;
+  const float* src = partial + (static_cast<size_t>(which) * n_chunks * DS + j) * D + c;
+  float a = 0.f;
+  for (int ch = 0; ch < n_chunks; ++ch) a += src[static_cast<size_t>(ch) * DS * D];
+  if (which == 0) dWq[j * D + c] = a * (1.0f / sqrtf(static_cast<float>(DS)));
+  else dWk[j * D + c] = a;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// workspace: ds [B*Hkv*rows*c_max] | rowdat [B*Hkv*rows*(2DS+D)] | blkdat [B*Hkv*rows*(DS+D)]
+static int sb_chunks(const sas_dims& d, int rows) {
+  return cdiv(d.batch * d.n_kv_heads * rows, kSbChunk);
+}
+
+// workspace: ds [B*Hkv*rows*c_max] | rowdat [B*Hkv*rows*(2DS+D)] |
+//            blkdat [B*Hkv*rows*(DS+D)] | partial [2][chunks][DS][D]
 size_t selector_bwd_ws_bytes(const sas_dims& d, int q_len) {
-  const size_t rows = cdiv(q_len, kBlock);
+  const int rows = cdiv(q_len, kBlock);
   const size_t grp = static_cast<size_t>(d.batch) * d.n_kv_heads;
   const size_t c_max = d.t_max / kBlock;
   return align256(grp * rows * c_max * sizeof(float)) +
          align256(grp * rows * (2 * d.sel_dim + d.head_dim) * sizeof(float)) +
-         grp * rows * (d.sel_dim + d.head_dim) * sizeof(float);
+         align256(grp * rows * (d.sel_dim + d.head_dim) * sizeof(float)) +
+         2 * static_cast<size_t>(sb_chunks(d, rows)) * d.sel_dim * d.head_dim * sizeof(float);
 }
 
 template <typename T, int D, int DS, int G>
@@ -178,6 +219,9 @@ static sas_status launch_sbwd(const sas_dims& d, const void* Q, int q_len, const
   float* rowdat = reinterpret_cast<float*>(w);
   w += align256(grp * rows * SelRow<D, DS>::kFloats * sizeof(float));
   float* blkdat = reinterpret_cast<float*>(w);
+  w += align256(grp * rows * SelBlk<D, DS>::kFloats * sizeof(float));
+  float* partial = reinterpret_cast<float*>(w);
+  const int n_chunks = sb_chunks(d, rows);
   hipLaunchKernelGGL((selector_bwd_rows_kernel<T, D, DS, G>), dim3(rows, d.n_kv_heads, d.batch),
                      dim3(kSelThreads), 0, st, static_cast<const T*>(Q), q_len, Wq, summ, idx,
                      score_lse, dlg, d.n_kv_heads, c_max, rows, d.top_k, ds_ws, ds, rowdat);
@@ -191,8 +235,13 @@ static sas_status launch_sbwd(const sas_dims& d, const void* Q, int q_len, const
     s = check_launch("selector_bwd_blocks");
     if (s != SAS_OK) return s;
   }
-  hipLaunchKernelGGL((selector_bwd_weights_kernel<D, DS>), dim3(DS, 2), dim3(D), 0, st,
-                     static_cast<int>(grp), rows, rowdat, blkdat, dWq, dWk);
+  // dWk's chunks beyond its entries (grp * (rows - 1) of them) hold zeros
+  hipLaunchKernelGGL((selector_bwd_partial_kernel<D, DS>), dim3(n_chunks, 2), dim3(2 * D), 0, st,
+                     static_cast<int>(grp), rows, rowdat, blkdat, partial);
+  s = check_launch("selector_bwd_partial");
+  if (s != SAS_OK) return s;
+  hipLaunchKernelGGL((selector_bwd_weights_kernel<D, DS>), dim3(DS, 2), dim3(D), 0, st, n_chunks,
+                     partial, dWq, dWk);
   return check_launch("selector_bwd_weights");
 }
 

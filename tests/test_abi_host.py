@@ -107,11 +107,14 @@ def test_decode_step_validation(lib):
 def test_selector_bwd_validation(lib):
     d = _dims()
     need = B.sas_workspace_bytes(B.SAS_OP_SELECTOR_BWD, d, 16384)
-    # ds of every (row, block), then per row a_row, qbar, u, then per block e_m, kbar_m
+    # ds of every (row, block), per row a_row, qbar, u, per block e_m, kbar_m, then the
+    # chunk partials of the two weight sums
     rows, grp, c_max = 256, 8, 65536 // 64
     sel = (grp * rows * c_max * 4 + 255) // 256 * 256
     rowb = (grp * rows * (2 * 128 + 128) * 4 + 255) // 256 * 256
-    assert need == sel + rowb + grp * rows * (128 + 128) * 4
+    blkb = (grp * rows * (128 + 128) * 4 + 255) // 256 * 256
+    chunks = (grp * rows + 63) // 64      # outer-product partials of 64 entries each
+    assert need == sel + rowb + blkb + 2 * chunks * 128 * 128 * 4
     sb = lambda dims, q_len, ws_bytes, dlg=FAKE, dwk=FAKE: lib.sas_selector_bwd(
         ctypes.byref(dims), FAKE, q_len, FAKE, FAKE, FAKE, FAKE, FAKE, dlg, None, FAKE, dwk,
         FAKE, ws_bytes, None)
