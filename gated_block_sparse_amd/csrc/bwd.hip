@@ -59,9 +59,13 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               uint16_t* __restrict__ dQ) {
   constexpr int NT = 128 * HPW;
   constexpr int KS = D / 16, CT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * kRowStride<D>];  // K, row reads
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[64 * kTrStride<D>];   // K, transpose reads
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * kRowStride<D>];
+  // two buffers: block i is staged in buffer i % 2 while block i-1 is used
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kRowStride<D>];  // K, row reads
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][64 * kTrStride<D>];   // K, transpose reads
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * kRowStride<D>];
+  __shared__ int s_blk[kMaxTopK + 1];
+  __shared__ float s_beta[kMaxTopK + 1];
+  __shared__ int s_nblk;
 
   const int nhc = G / HPW;
   const int t = n_tiles - 1 - static_cast<int>(blockIdx.x) / nhc;
@@ -93,59 +97,97 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
 
-  for (int it = 0; it <= k; ++it) {
-    const bool diag = it == k;
-    int blk = t;
-    float beta2 = 0.f;
-    if (!diag) {
-      blk = idx[srow * k + it];
-      if (blk < 0) continue;
-      if (log_gate) beta2 = log_gate[srow * k + it] * kLog2eF;
+  // block list: the valid selected blocks (in slot order), then the diagonal
+  if (wave == 0) {
+    const bool ok = lane < k && idx[srow * k + lane] >= 0;
+    const unsigned long long mask = __ballot(ok);
+    if (ok) {
+      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+      s_blk[pos] = idx[srow * k + lane];
+      s_beta[pos] = log_gate ? log_gate[srow * k + lane] * kLog2eF : 0.f;
     }
-    const int tok0 = blk * 64;
-    __syncthreads();
-    stage_rows<D, NT>(Kg + static_cast<size_t>(tok0) * D, S - tok0, Ks, Kt, tid);
-    stage_rows<D, NT>(Vg + static_cast<size_t>(tok0) * D, S - tok0, Vs, nullptr, tid);
-    __syncthreads();
+    if (lane == 0) {
+      const int nv = __popcll(mask);
+      s_blk[nv] = t;
+      s_beta[nv] = 0.f;
+      s_nblk = nv + 1;
+    }
+  }
+  __syncthreads();
+  const int nblk = s_nblk;
+  // per-thread share of one block's K and V rows (16-byte chunks), loaded into
+  // registers one block ahead of its LDS store
+  constexpr int TOT = 64 * (D / 8), CH = (TOT + NT - 1) / NT;
+  uint4 kreg[CH], vreg[CH];
+  auto load_block = [&](int i) {
+    const int tok = s_blk[i] * 64;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int x = tid + c * NT, row = x / (D / 8), cc = x % (D / 8);
+      const bool ok = x < TOT && tok + row < S;
+      kreg[c] = ok ? *reinterpret_cast<const uint4*>(Kg + static_cast<size_t>(tok + row) * D + cc * 8)
+                   : make_uint4(0, 0, 0, 0);
+      vreg[c] = ok ? *reinterpret_cast<const uint4*>(Vg + static_cast<size_t>(tok + row) * D + cc * 8)
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int x = tid + c * NT, row = x / (D / 8), cc = x % (D / 8);
+      if (x < TOT) {
+        lds_store_row8<kRowStride<D>>(Ks[buf], row, cc * 8, kreg[c]);
+        lds_store_row8<kTrStride<D>>(Kt[buf], row, cc * 8, kreg[c]);
+        lds_store_row8<kRowStride<D>>(Vs[buf], row, cc * 8, vreg[c]);
+      }
+    }
+  };
+  load_block(0);
+  store_block(0);
+  __syncthreads();
 
-    f32x16_t s[2], dp[2];
+  for (int it = 0; it < nblk; ++it) {
+    const bool diag = it == nblk - 1;
+    const float beta2 = s_beta[it];
+    const int buf = it & 1;
+    if (it + 1 < nblk) load_block(it + 1);   // in flight while this block computes
+    const float off = beta2 - lse2;
+    // one 32-token half at a time, so only one S^T / dP^T pair is live
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      zero16(s[tt]);
-      zero16(dp[tt]);
+      f32x16_t st, dp;
+      zero16(st);
+      zero16(dp);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int row = 32 * tt + l32, col = 16 * ks + 8 * hi;
-        s[tt] = mfma32x32x16(lds_row8<kRowStride<D>>(Ks, row, col), qb[ks], s[tt]);
-        dp[tt] = mfma32x32x16(lds_row8<kRowStride<D>>(Vs, row, col), db[ks], dp[tt]);
+        st = mfma32x32x16(lds_row8<kRowStride<D>>(Ks[buf], row, col), qb[ks], st);
+        dp = mfma32x32x16(lds_row8<kRowStride<D>>(Vs[buf], row, col), db[ks], dp);
       }
-    }
-    const float off = beta2 - lse2;
-    if (diag || !qvalid) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      if (diag || !qvalid) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int tok = 32 * tt + acc_row(v, hi);
           const bool ok = qvalid && !(diag && tok > qloc);
-          const float p = ok ? fast_exp2(fmaf(s[tt][v], scale2, off)) : 0.f;
-          s[tt][v] = p * (dp[tt][v] - Dv);  // dS^T
+          const float p = ok ? fast_exp2(fmaf(st[v], scale2, off)) : 0.f;
+          st[v] = p * (dp[v] - Dv);  // dS^T
         }
-    } else {
+      } else {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int v = 0; v < 16; ++v) st[v] = fast_exp2(fmaf(st[v], scale2, off)) * (dp[v] - Dv);
+      }
+      // dQ^T (D x 32 queries) += K^T dS^T over this half's k-steps j = 2tt, 2tt+1
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          s[tt][v] = fast_exp2(fmaf(s[tt][v], scale2, off)) * (dp[tt][v] - Dv);
+      for (int jj = 0; jj < 2; ++jj) {
+        const bf16x8_t bop = acc_to_bop(&st, jj);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          dq[ct] = mfma32x32x16(lds_aop_tr_perm<kTrStride<D>>(Kt[buf], 32 * ct, 2 * tt + jj, hi),
+                                bop, dq[ct]);
+      }
     }
-    // dQ^T (D x 32 queries) += K^T dS^T, k-step j = tokens 16j..16j+15
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t bop = acc_to_bop(s, j);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        dq[ct] = mfma32x32x16(lds_aop_tr_perm<kTrStride<D>>(Kt, 32 * ct, j, hi), bop, dq[ct]);
-    }
+    if (it + 1 < nblk) store_block(buf ^ 1);
+    __syncthreads();
   }
   if (qvalid) store_acc_col<CT>(dq, scale, dQ + qrow_i * D, hi);
 }
