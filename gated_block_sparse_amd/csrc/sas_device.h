@@ -116,6 +116,29 @@ __device__ __forceinline__ float transpose_sum32(float* v, int l32) {
   return v[0];
 }
 
+// The same with R < 32 partial values: the transposing steps run over the
+// low log2(R) lane bits, then plain butterfly sums over the rest; lane l32
+// ends with the sum of v[l32 % R] over the half wave.
+template <int R>
+__device__ __forceinline__ float transpose_sum(float* v, int l32) {
+  static_assert(R >= 1 && R <= 32 && (R & (R - 1)) == 0, "R: power of two up to 32");
+#pragma unroll
+  for (int sft = R / 2; sft >= 1; sft >>= 1) {
+    const uint32_t up = (l32 & sft) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int j = 0; j < sft; ++j) {
+      const uint32_t a = __float_as_uint(v[j]), b = __float_as_uint(v[j + sft]);
+      const float keep = __uint_as_float((b & up) | (a & ~up));
+      const float send = __uint_as_float((a & up) | (b & ~up));
+      v[j] = keep + __shfl_xor(send, sft, 64);
+    }
+  }
+  float s = v[0];
+#pragma unroll
+  for (int sft = R; sft < 32; sft <<= 1) s += __shfl_xor(s, sft, 64);
+  return s;
+}
+
 // Order-preserving map of an fp32 score to uint32 (larger float -> larger
 // integer); -0 and +0 map to the same value.
 __device__ __forceinline__ uint32_t score_bits(float s) {

@@ -11,7 +11,8 @@ namespace sas {
 
 constexpr int kBlock = 64;          // tokens per block (the only size built)
 constexpr int kMaxTopK = 64;        // largest k built
-constexpr int kSelChunk = 256;      // history blocks scored per workgroup in decode select
+constexpr int kChunkGridCap = 256;   // decode select: at most this many chunk workgroups ...
+constexpr int kChunkKeysCap = 512;   // ... and merged candidate keys per row for chunks < 256 blocks
 constexpr int kMaxTileRows = 1024;  // prefill tiles supported by the tile selector
 constexpr int kMaxMergeKeys = 2048; // chunk candidates one decode row may merge
 

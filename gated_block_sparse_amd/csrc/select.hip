@@ -11,7 +11,7 @@
 // ~m), a strict total order, so the sort is exact and deterministic.
 //
 // Decode: C can reach thousands of blocks and the summary scan is the HBM
-// traffic, so the row is cut into chunks of kSelChunk blocks, one workgroup
+// traffic, so the row is cut into chunks of 64-256 blocks, one workgroup
 // each: score (half a wave per 128-float summary row), chunk max/sum-exp, and
 // the chunk's own top-k by an LDS bitonic sort.  A second small kernel per row
 // merges the chunk LSE states and the chunk candidates.
@@ -24,15 +24,18 @@ namespace sas {
 
 
 // ------------------------------------------------------------- decode ---
-// Chunk kernel: grid (chunk, group, sequence), kSelChunk blocks per chunk.
-// Every load the workgroup needs (q, one Wq_sel row per thread, 32 summary
-// slices per lane) is issued before any arithmetic, so the kernel pays about
-// one memory round trip.  Each wave then sorts its 64 scores with a shuffle
-// bitonic network, the four sorted lists are merged by rank (a key's rank is
-// its position in its own list plus the number of larger keys in the others,
+// Chunk kernel: grid (chunk, group, sequence), 8R blocks per chunk (half
+// wave hw owns blocks hw + 8j, j < R).  Every load the workgroup needs (the
+// lane's channels of the group's query heads, its slices of d_sel/8 Wq_sel
+// rows and of R summary rows) is issued before any arithmetic, so the kernel
+// pays about one memory round trip; both the projection and the scores read
+// whole rows per half wave (coalesced) and finish with a transposing
+// butterfly sum.  Each wave then sorts its 64 scores with a shuffle bitonic
+// network, the four sorted lists are merged by rank (a key's rank is its
+// position in its own list plus the number of larger keys in the others,
 // found by binary search), and the chunk's top-k keys plus its (max, sum-exp)
 // go to the workspace.  A row that fits one chunk is finished right here.
-template <typename T, int D, int DS, int G>
+template <typename T, int D, int DS, int G, int R>
 __global__ void __launch_bounds__(kSelThreads)
 select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
                            const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
@@ -41,8 +44,12 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
                            uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse) {
   constexpr int PL = DS / 32;                 // summary floats per lane
+  constexpr int PD = D / 32;                  // query channels per lane
+  constexpr int RW = DS / 8;                  // Wq_sel rows per half wave
   constexpr int NW = kSelThreads / 64;
-  __shared__ float qm[D];
+  constexpr int kChunk = 8 * R;
+  static_assert(PL == 2 || PL == 4, "d_sel");
+  static_assert(PD == 2 || PD == 4, "d");
   __shared__ float qs[DS];
   __shared__ uint64_t lists[NW][64];
   __shared__ uint64_t best[kMaxTopK];
@@ -52,28 +59,39 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   const int lane = tid & 63, wave = tid >> 6, hw = tid >> 5, l32 = tid & 31;
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
-  const int m0 = chunk * kSelChunk;
+  const int m0 = chunk * kChunk;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const size_t p = row * nchunk + chunk;
-  const int n = max(0, min(kSelChunk, C - m0));
+  const int n = max(0, min(kChunk, C - m0));
 
   // ---- all loads up front
-  float qraw[G];
-  if (tid < D) {
-    const T* qb = q + (row * G) * static_cast<size_t>(D) + tid;
+  float qraw[G][PD];
+  {
+    const T* qb = q + (row * G) * static_cast<size_t>(D) + PD * l32;
 #pragma unroll
-    for (int h = 0; h < G; ++h) qraw[h] = load_scalar<T>(qb + h * D);
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < PD; ++e) qraw[h][e] = load_scalar<T>(qb + h * D + e);
   }
-  float4 wrow[D / 4];
-  if (tid < DS) {
-    const float4* w = reinterpret_cast<const float4*>(Wq + static_cast<size_t>(tid) * D);
+  float wv[RW][PD];
+  {
+    const float* wr = Wq + static_cast<size_t>(hw) * D + PD * l32;
 #pragma unroll
-    for (int c4 = 0; c4 < D / 4; ++c4) wrow[c4] = w[c4];
+    for (int j = 0; j < RW; ++j) {
+      const float* w = wr + static_cast<size_t>(8 * j) * D;
+      if constexpr (PD == 4) {
+        const float4 x = *reinterpret_cast<const float4*>(w);
+        wv[j][0] = x.x; wv[j][1] = x.y; wv[j][2] = x.z; wv[j][3] = x.w;
+      } else {
+        const float2 x = *reinterpret_cast<const float2*>(w);
+        wv[j][0] = x.x; wv[j][1] = x.y;
+      }
+    }
   }
   const float* srow = summ + (row * c_max + m0) * static_cast<size_t>(DS) + l32 * PL;
-  float xs[32][PL];
+  float xs[R][PL];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < R; ++j) {
     const int i = hw + 8 * j;
 #pragma unroll
     for (int e = 0; e < PL; ++e) xs[j][e] = 0.f;
@@ -87,45 +105,47 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
       }
     }
   }
-  // ---- pooled query, projected
-  if (tid < D) {
-    float a = 0.f;
+  // ---- pooled query, projected: half wave hw owns Wq_sel rows hw + 8j
+  {
+    float qm[PD];
 #pragma unroll
-    for (int h = 0; h < G; ++h) a += qraw[h];
-    qm[tid] = a / G;
-  }
-  __syncthreads();
-  if (tid < DS) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int e = 0; e < PD; ++e) {
+      float a = 0.f;
 #pragma unroll
-    for (int c4 = 0; c4 < D / 4; ++c4) {
-      a0 += wrow[c4].x * qm[4 * c4];
-      a1 += wrow[c4].y * qm[4 * c4 + 1];
-      a2 += wrow[c4].z * qm[4 * c4 + 2];
-      a3 += wrow[c4].w * qm[4 * c4 + 3];
+      for (int h = 0; h < G; ++h) a += qraw[h][e];
+      qm[e] = a / G;
     }
-    qs[tid] = ((a0 + a1) + (a2 + a3)) * (1.0f / sqrtf(static_cast<float>(DS)));
+    float pv[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < PD; ++e) a += wv[j][e] * qm[e];
+      pv[j] = a;
+    }
+    const float proj = transpose_sum<RW>(pv, l32);
+    if (l32 < RW) qs[hw + 8 * l32] = proj * (1.0f / sqrtf(static_cast<float>(DS)));
   }
   __syncthreads();
-  // ---- scores: half wave hw owns rows hw + 8j; the transposed butterfly
-  // leaves row hw + 8*l32 in lane l32
-  float v[32];
+  // ---- scores: the transposed butterfly leaves row hw + 8 * (l32 % R) in
+  // lane l32 (lanes l32 >= R hold copies and stand aside)
+  float v[R];
   {
     float qv[PL];
 #pragma unroll
     for (int e = 0; e < PL; ++e) qv[e] = qs[l32 * PL + e];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < R; ++j) {
       float a = 0.f;
 #pragma unroll
       for (int e = 0; e < PL; ++e) a += xs[j][e] * qv[e];
       v[j] = a;
     }
   }
-  transpose_sum32(v, l32);
-  const int i_row = hw + 8 * l32;
-  const bool valid = i_row < n;
-  const float sc = valid ? v[0] : -INFINITY;
+  const float sdot = transpose_sum<R>(v, l32);
+  const int i_row = hw + 8 * (l32 & (R - 1));
+  const bool valid = l32 < R && i_row < n;
+  const float sc = valid ? sdot : -INFINITY;
   if (scores && valid) scores[row * c_max + m0 + i_row] = sc;
 
   // ---- chunk (max, sum exp)
@@ -189,9 +209,27 @@ select_decode_merge_kernel(const int32_t* __restrict__ seq_lens, int Hkv, int t_
   if (tid == 0) score_lse[row] = lse;
 }
 
-static int decode_nchunk(const sas_dims& d) {
-  const int n = cdiv(d.t_max / kBlock, kSelChunk);
+// Blocks per decode chunk, 8R with R rows per half wave: the smallest chunk
+// that keeps the grid within one workgroup per CU and the merged candidate
+// lists short (more, smaller chunks mean more loads in flight at batch 1),
+// else 256.
+static int chunk_count(int c_max, int R) {
+  const int n = cdiv(c_max, 8 * R);
   return n > 0 ? n : 1;
+}
+static int decode_chunk_rows(const sas_dims& d) {
+  const long rows = static_cast<long>(d.batch) * d.n_kv_heads;
+  const int kc = d.top_k > 0 ? d.top_k : 1;
+  for (int R = 8; R < 32; R <<= 1) {
+    const int nc = chunk_count(d.t_max / kBlock, R);
+    int nl = 1;
+    while (nl < nc) nl <<= 1;
+    if (rows * nc <= kChunkGridCap && nl * kc <= kChunkKeysCap) return R;
+  }
+  return 32;
+}
+static int decode_nchunk(const sas_dims& d) {
+  return chunk_count(d.t_max / kBlock, decode_chunk_rows(d));
 }
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -225,11 +263,18 @@ static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32
   if (L.nlist * L.kc > kMaxMergeKeys)
     return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
                 L.nlist * L.kc);
-  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G>),
-                     dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,
-                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,
-                     d.t_max / kBlock, d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx,
-                     log_gate, score_lse);
+#define SAS_SD_CHUNK(R)                                                                       \
+  hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G, R>),                              \
+                     dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,           \
+                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,       \
+                     d.t_max / kBlock, d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx,    \
+                     log_gate, score_lse)
+  switch (decode_chunk_rows(d)) {
+    case 8: SAS_SD_CHUNK(8); break;
+    case 16: SAS_SD_CHUNK(16); break;
+    default: SAS_SD_CHUNK(32); break;
+  }
+#undef SAS_SD_CHUNK
   return check_launch("select_decode_chunk");
 }
 

@@ -208,8 +208,12 @@ def test_decode_two_blocks_per_unit_ragged(k):
     run_decode_case(p, label=f"two-block units k={k}")
 
 
-@pytest.mark.parametrize("T,k", [(64 * 200 + 3, 64), (64 * 3000 + 17, 64), (64 * 9000 + 1, 32)])
+@pytest.mark.parametrize("T,k", [(64 * 200 + 3, 64), (64 * 3000 + 17, 64), (64 * 9000 + 1, 32),
+                                 (64 * 3000 + 17, 16)])
 def test_decode_large_k_and_many_chunks(T, k):
+    """Rows of many selection chunks; the chunk length follows the grid and
+    k (two groups here): 64 blocks for the first case, 256 for the second and
+    third, 128 for the last."""
     run_decode_case(_edge_problem(T, k, dtype="bf16", Hq=8, Hkv=2, d=128, ds=128, seed=T),
                     label=f"T={T} k={k}")
 
