@@ -192,6 +192,59 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (qvalid) store_acc_col<CT>(dq, scale, dQ + qrow_i * D, hi);
 }
 
+// The tiles that read key block m of one (sequence, group): the diagonal
+// tile first, then every later tile whose ascending idx row contains m, in
+// ascending tile order, with the slot and the log-gate (base 2) of the entry.
+// All NWV waves of the workgroup call it; returns the entry count.
+template <int NWV>
+__device__ int reading_tiles(int m, int n_tiles, int k, const int32_t* __restrict__ idx_rows,
+                             const float* __restrict__ lg_rows, int* list_t, int* list_slot,
+                             float* list_beta, int* s_count, int* s_wcount) {
+  constexpr int NT = 64 * NWV;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    list_t[0] = m;
+    list_slot[0] = -1;
+    list_beta[0] = 0.f;
+    *s_count = 1;
+  }
+  __syncthreads();
+  for (int base = m + 1; base < n_tiles; base += NT) {
+    const int t = base + tid;
+    int slot = -1;
+    if (t < n_tiles && k > 0) {
+      const int32_t* row = idx_rows + static_cast<size_t>(t) * k;
+      int lo = 0, hi2 = k;
+      while (lo < hi2) {
+        const int mid = (lo + hi2) >> 1;
+        const int v = row[mid];
+        if (v >= 0 && v < m) lo = mid + 1;
+        else hi2 = mid;
+      }
+      if (lo < k && row[lo] == m) slot = lo;
+    }
+    const unsigned long long mask = __ballot(slot >= 0);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wcount[wave] = __popcll(mask);
+    __syncthreads();
+    int off = *s_count;
+    for (int w = 0; w < wave; ++w) off += s_wcount[w];
+    if (slot >= 0) {
+      list_t[off + before] = t;
+      list_slot[off + before] = slot;
+      list_beta[off + before] = lg_rows ? lg_rows[static_cast<size_t>(t) * k + slot] * kLog2eF : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int add = 0;
+      for (int w = 0; w < NWV; ++w) add += s_wcount[w];
+      *s_count += add;
+    }
+    __syncthreads();
+  }
+  return *s_count;
+}
+
 // --------------------------------------------------------- dK/dV pass ---
 // One workgroup per (key block m, group r, sequence) with up to 4 waves; wave
 // w handles heads w, w + 4, ... of the group and all 64 tokens of the block,
@@ -241,49 +294,9 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int Hq = Hkv * G;
   const size_t grow = static_cast<size_t>(b) * Hkv + r;
 
-  // ---- the tiles that read this block: the diagonal one, then every later
-  // tile whose ascending idx row contains m (in ascending tile order)
-  if (tid == 0) {
-    list_t[0] = m;
-    list_slot[0] = -1;
-    list_beta[0] = 0.f;
-    s_count = 1;
-  }
-  __syncthreads();
-  for (int base = m + 1; base < n_tiles; base += NT) {
-    const int t = base + tid;
-    int slot = -1;
-    if (t < n_tiles && k > 0) {
-      const int32_t* row = idx + (grow * n_tiles + t) * k;
-      int lo = 0, hi2 = k;
-      while (lo < hi2) {
-        const int mid = (lo + hi2) >> 1;
-        const int v = row[mid];
-        if (v >= 0 && v < m) lo = mid + 1;
-        else hi2 = mid;
-      }
-      if (lo < k && row[lo] == m) slot = lo;
-    }
-    const unsigned long long mask = __ballot(slot >= 0);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) s_wcount[wave] = __popcll(mask);
-    __syncthreads();
-    int off = s_count;
-    for (int w = 0; w < wave; ++w) off += s_wcount[w];
-    if (slot >= 0) {
-      list_t[off + before] = t;
-      list_slot[off + before] = slot;
-      list_beta[off + before] = log_gate ? log_gate[(grow * n_tiles + t) * k + slot] * kLog2eF : 0.f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int add = 0;
-      for (int w = 0; w < NWV; ++w) add += s_wcount[w];
-      s_count += add;
-    }
-    __syncthreads();
-  }
-  const int n_list = s_count;
+  const int n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
+                                        log_gate ? log_gate + grow * n_tiles * k : nullptr,
+                                        list_t, list_slot, list_beta, &s_count, s_wcount);
 
   // ---- stage the block's K and V rows (B operands, shared by the waves)
   const int tok0 = 64 * m;
@@ -470,6 +483,283 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
+// ------------------------------------------ dK/dV pass, token split ---
+// D = 128.  One workgroup per (key block m, group r, sequence) with four
+// waves; wave w owns tokens 16w..16w+15 of the block for every head of the
+// group and keeps their dK^T and dV^T (D x 16 each) in registers, so no
+// cross-wave sum is needed.  The work is a sequence of steps (entry e, head
+// g, query half qt).  A step's 32 Q rows, 32 dO rows and the 32 queries' lse
+// and D go from global memory straight into one slot of an LDS ring (LDS
+// DMA, kTsSlots slots), kTsSlots - 1 steps ahead of the step being computed,
+// so the latency of these gathered rows overlaps the products of earlier
+// steps; the four waves share every slot.  Two workgroups fit on a CU.
+//
+// Products per step and wave (v_mfma_f32_16x16x32_bf16): S = Q K^T and
+// dP = dO V^T (32 queries x 16 tokens; K and V rows of the wave's tokens are
+// B operands held in registers), then dV^T += dO^T P and dK^T += Q^T dS with
+// the query index as the contraction: the accumulators of the two 16-query
+// tiles are the B operand as they lie in the lanes, and the LDS transpose
+// read yields the A operand in the same query order.
+//
+// Slot layout: row q (0..31) of Q or dO takes 256 bytes; its 16-byte chunk c
+// sits at position c ^ f(q % 16) with f(q) = 2 (q % 8) + q / 8.  The 16-byte
+// row reads (16 rows, one chunk) and the transpose reads (8 rows x 2 chunks
+// per 32 lanes) then each cover all banks once.  The DMA writes 64 lanes x
+// 16 bytes contiguously, so each lane fetches the chunk that belongs at its
+// position.
+constexpr int kTsSlots = 4;
+constexpr int kTsRow = 256;                          // bytes per Q / dO row (D = 128)
+constexpr int kTsTensor = 32 * kTsRow;               // one tensor of a slot
+constexpr int kTsSlot = 2 * kTsTensor + 64 * 4;      // Q, dO, lse[32], D[32]
+
+__device__ __forceinline__ int ts_swz(int q) { return 2 * (q & 7) + ((q >> 3) & 1); }
+
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// One LDS DMA copy: every lane fetches BYTES (16 or 4) from its own global
+// address; lane L's bytes land at LDS address lds_addr + L * BYTES (M0 holds
+// the wave-uniform base).  Issued from asm so that the compiler does not
+// track it: it would otherwise make every later read of the ring wait for
+// all copies in flight; completion is waited for explicitly (ts_sync).  M0
+// is saved and restored around the copy.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* g, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t keep;
+  if constexpr (BYTES == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
+}
+
+// Waits until at most N of this wave's vector-memory operations (here: LDS
+// DMA copies) are outstanding and its LDS operations are done, then joins the
+// workgroup barrier.  Written as one asm statement with a memory clobber so
+// that no LDS access moves across it; a fence would wait for every copy in
+// flight, including those of later steps.
+template <int N>
+__device__ __forceinline__ void ts_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int G>
+__global__ void __launch_bounds__(256, 2)
+bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv,
+                   int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
+                   const float* __restrict__ log_gate, float scale2, float scale,
+                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
+  constexpr int D = 128, NWV = 4, KS = D / 32, CT = D / 16;
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kTsSlots * kTsSlot];
+  __shared__ int list_t[kMaxTileRows];
+  __shared__ int list_slot[kMaxTileRows];
+  __shared__ float list_beta[kMaxTileRows];
+  __shared__ float red[2][NWV];
+  __shared__ int s_count;
+  __shared__ int s_wcount[NWV];
+
+  const int m = static_cast<int>(blockIdx.x) / Hkv, r = static_cast<int>(blockIdx.x) % Hkv;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, i4 = lane >> 4;
+  const int Hq = Hkv * G;
+  const size_t grow = static_cast<size_t>(b) * Hkv + r;
+
+  const int n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
+                                        log_gate ? log_gate + grow * n_tiles * k : nullptr,
+                                        list_t, list_slot, list_beta, &s_count, s_wcount);
+  const int n_steps = n_list * G * 2;
+  const uint32_t ring_lds = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)ring));
+
+  // ---- LDS DMA of step s2 into slot s2 % kTsSlots.  Every wave copies rows
+  // 8w..8w+7 of Q and of dO (two 1 KB copies each), wave 0 also the lse and
+  // D of the 32 queries.  Steps past the end repeat the last step's copies
+  // (into a slot nobody reads), so every step issues the same number of
+  // copies per wave and the wait counts below stay exact.  Query rows past
+  // the sequence end repeat its last row (finite values; masked below).
+  auto issue = [&](int s2) {
+    const int sc = min(s2, n_steps - 1);
+    const int qt2 = sc & 1, g2 = (sc >> 1) % G, e2 = (sc >> 1) / G;
+    const int qbase = 64 * list_t[e2] + 32 * qt2;
+    const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g2) * S;
+    const uint32_t slot = ring_lds + (s2 % kTsSlots) * kTsSlot;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int row0 = 8 * wave + 4 * n;
+      const int ql = row0 + i4;
+      const size_t src = (hrow + min(qbase + ql, S - 1)) * D + 8 * (l16 ^ ts_swz(ql));
+      lds_dma<16>(Q + src, slot + row0 * kTsRow);
+      lds_dma<16>(dO + src, slot + kTsTensor + row0 * kTsRow);
+    }
+    if (wave == 0) {
+      const float* src = (lane < 32 ? lse : Dq) + hrow + min(qbase + (lane & 31), S - 1);
+      lds_dma<4>(src, slot + 2 * kTsTensor);
+    }
+  };
+  // ---- K and V rows of the wave's tokens: B operands, k-step ks holds
+  // channels 32ks + 8 i4 .. +7 of token 16w + l16 (zero past the sequence)
+  const int tok0 = 64 * m;
+  const int tok = 16 * wave + l16;
+  const bool tok_ok = tok0 + tok < S;
+  bf16x8_t kb[KS], vb[KS];
+  {
+    const size_t row = (grow * t_max + tok0 + (tok_ok ? tok : 0)) * D + 8 * i4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kx = *reinterpret_cast<const uint4*>(K + row + 32 * ks);
+      const uint4 vx = *reinterpret_cast<const uint4*>(V + row + 32 * ks);
+      kb[ks] = as_bf16x8(tok_ok ? kx : make_uint4(0, 0, 0, 0));
+      vb[ks] = as_bf16x8(tok_ok ? vx : make_uint4(0, 0, 0, 0));
+    }
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < kTsSlots - 1; ++s2) issue(s2);
+
+  f32x4_t dk[CT], dv[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      dk[ct][v] = 0.f;
+      dv[ct][v] = 0.f;
+    }
+
+  // per-lane LDS offsets.  Row reads (A of S and dP): row 16 qtile + l16,
+  // chunk 4 ks + i4.  Transpose reads (A of dV^T and dK^T): rows
+  // 4 i4 + l16/4 (+16), bytes 32 ct + 8 (l16 % 4) of the row.
+  const int fr = ts_swz(l16);
+  const int rd_base = l16 * kTsRow + 16 * ((i4 ^ fr) & 3);
+  const int rd_x = fr >> 2;
+  const int q1 = 4 * i4 + (l16 >> 2);
+  const int ft = ts_swz(q1);
+  const int tr_base = q1 * kTsRow + 16 * (((l16 >> 1) & 1) ^ (ft & 1)) + 8 * (l16 & 1);
+  const int tr_x = ft >> 1;
+
+  float dsum = 0.f;
+  int pending = -1;   // entry whose per-wave dlog_gate partials sit in red[]
+  for (int s = 0; s < n_steps; ++s) {
+    // this wave's copies for step s are done once at most the copies of
+    // kTsSlots - 2 later steps remain; the barrier makes every wave's copies
+    // visible and frees the slot read in step s - 1 for the next copy
+    if (wave == 0) ts_sync<5 * (kTsSlots - 2)>();
+    else ts_sync<4 * (kTsSlots - 2)>();
+    issue(s + kTsSlots - 1);
+    if (pending >= 1 && tid == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) tot += red[pending & 1][w];
+      dlg[(grow * n_tiles + list_t[pending]) * k + list_slot[pending]] = tot;
+    }
+    if (pending >= 0) pending = -1;
+
+    const int qt = s & 1, g = (s >> 1) % G, e = (s >> 1) / G;
+    const bool diag = e == 0;
+    const float beta2 = list_beta[e];
+    const int nq = min(64, S - 64 * list_t[e]);
+    const unsigned char* slot = ring + (s % kTsSlots) * kTsSlot;
+    const unsigned char* Qs = slot;
+    const unsigned char* Os = slot + kTsTensor;
+    const float* ls = reinterpret_cast<const float*>(slot + 2 * kTsTensor);
+
+    // S and dP: 32 queries (two 16-row tiles) x the wave's 16 tokens
+    f32x4_t sa[2], pa[2];
+#pragma unroll
+    for (int qtile = 0; qtile < 2; ++qtile) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sa[qtile][v] = 0.f;
+        pa[qtile][v] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = qtile * 16 * kTsRow + rd_base + 64 * (ks ^ rd_x);
+        const bf16x8_t qa = as_bf16x8(*reinterpret_cast<const uint4*>(Qs + off));
+        const bf16x8_t oa = as_bf16x8(*reinterpret_cast<const uint4*>(Os + off));
+        sa[qtile] = mfma16x16x32(qa, kb[ks], sa[qtile]);
+        pa[qtile] = mfma16x16x32(oa, vb[ks], pa[qtile]);
+      }
+    }
+    // P and dS; lane holds queries 16 qtile + 4 i4 + v of token tok
+#pragma unroll
+    for (int qtile = 0; qtile < 2; ++qtile)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = 16 * qtile + 4 * i4 + v;
+        const int qq = 32 * qt + q;
+        const bool ok = tok_ok && qq < nq && !(diag && tok > qq);
+        const float p =
+            ok ? fast_exp2(fmaf(sa[qtile][v], scale2, beta2 - ls[q] * kLog2eF)) : 0.f;
+        const float ds = p * (pa[qtile][v] - ls[32 + q]);
+        sa[qtile][v] = p;
+        pa[qtile][v] = ds;
+        dsum += ds;
+      }
+    bf16x8_t pb, sb;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pb[v] = static_cast<__bf16>(sa[0][v]);
+      pb[4 + v] = static_cast<__bf16>(sa[1][v]);
+      sb[v] = static_cast<__bf16>(pa[0][v]);
+      sb[4 + v] = static_cast<__bf16>(pa[1][v]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over the 32 queries of the step
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int off = tr_base + 32 * (ct ^ tr_x);
+      const uint2 o0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Os + off));
+      const uint2 o1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Os + off + 16 * kTsRow));
+      const uint2 x0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Qs + off));
+      const uint2 x1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(Qs + off + 16 * kTsRow));
+      dv[ct] = mfma16x16x32(as_bf16x8(make_uint4(o0.x, o0.y, o1.x, o1.y)), pb, dv[ct]);
+      dk[ct] = mfma16x16x32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), sb, dk[ct]);
+    }
+    // last step of the entry: the wave's dlog_gate partial
+    if (qt == 1 && g == G - 1) {
+      const float w = wave_sum_from(dsum, 1);
+      if (lane == 0) red[e & 1][wave] = w;
+      dsum = 0.f;
+      pending = e;
+    }
+  }
+  ts_sync<0>();
+  if (pending >= 1 && tid == 0) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) tot += red[pending & 1][w];
+    dlg[(grow * n_tiles + list_t[pending]) * k + list_slot[pending]] = tot;
+  }
+  // ---- store: lane holds channels 16 ct + 4 i4 + v of token tok
+  if (tok_ok) {
+    const size_t orow = (grow * t_max + tok0 + tok) * D + 4 * i4;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      uint2 pk, pv;
+      pk.x = bf16_rne(dk[ct][0] * scale) | (bf16_rne(dk[ct][1] * scale) << 16);
+      pk.y = bf16_rne(dk[ct][2] * scale) | (bf16_rne(dk[ct][3] * scale) << 16);
+      pv.x = bf16_rne(dv[ct][0]) | (bf16_rne(dv[ct][1]) << 16);
+      pv.y = bf16_rne(dv[ct][2]) | (bf16_rne(dv[ct][3]) << 16);
+      *reinterpret_cast<uint2*>(dK + orow + 16 * ct) = pk;
+      *reinterpret_cast<uint2*>(dV + orow + 16 * ct) = pv;
+    }
+  }
+}
+
 // ------------------------------------------------------------ launcher ---
 size_t bwd_ws_bytes(const sas_dims& d, int seq_len) {
   return static_cast<size_t>(d.batch) * d.n_q_heads * seq_len * sizeof(float);
@@ -510,6 +800,21 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
 #undef SAS_DQ_CASE
   s = check_launch("bwd_dq");
   if (s != SAS_OK) return s;
+  if constexpr (D == 128) {
+#define SAS_DKDV_TS(GG)                                                                          \
+  hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),          \
+                     dim3(256), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, \
+                     d.top_k, idx, log_gate, scale2, scale, static_cast<uint16_t*>(dK),          \
+                     static_cast<uint16_t*>(dV), dlg)
+    switch (G) {
+      case 1: SAS_DKDV_TS(1); break;
+      case 2: SAS_DKDV_TS(2); break;
+      case 4: SAS_DKDV_TS(4); break;
+      default: SAS_DKDV_TS(8); break;
+    }
+#undef SAS_DKDV_TS
+    return check_launch("bwd_dkdv_ts");
+  }
 #define SAS_DKDV_CASE(NWV)                                                                     \
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),         \
                      dim3(64 * NWV), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, \

@@ -187,6 +187,7 @@ def run_bwd_case(p, ctx, exact_blocks=None, label=""):
 @pytest.mark.parametrize("S,Hq,Hkv,d,k", [
     (64, 4, 1, 128, 4), (100, 4, 1, 128, 4), (1000, 8, 2, 128, 3), (2048, 8, 2, 128, 16),
     (777, 2, 2, 64, 5), (700, 16, 2, 64, 6), (1, 4, 1, 128, 2), (333, 8, 2, 128, 0),
+    (500, 2, 2, 128, 5), (300, 4, 2, 128, 3), (640, 8, 1, 128, 4), (129, 16, 2, 128, 2),
 ])
 def test_bwd_small(S, Hq, Hkv, d, k):
     p = _problem(S, Hq, Hkv, d, 128, k, seed=S + 7 * Hq)
