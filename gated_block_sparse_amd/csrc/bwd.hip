@@ -15,11 +15,13 @@
 //  3. KV-outer (one workgroup per key block x group): the workgroup finds the
 //     tiles that selected its block (binary search in each later tile's
 //     ascending idx row) plus the diagonal tile, then for every such tile and
-//     head recomputes S = Q K^T (a lane owns one token column), dP = dO V^T,
-//     dS, and accumulates dV^T += dO^T P and dK^T += Q^T dS in registers, one
-//     wave per head.  It is the only writer of dK/dV for its block and of the
-//     dlog_gate entries that point at it, which it sums over heads in a fixed
-//     order.
+//     head recomputes S = Q K^T, dP = dO V^T, dS, and accumulates
+//     dV^T += dO^T P and dK^T += Q^T dS in registers: for d = 128 each wave
+//     owns 16 tokens of the block for all heads, the gathered Q/dO rows
+//     arriving by LDS DMA several steps ahead (bwd_dkdv_ts_kernel); for
+//     d = 64 one wave per head owns all 64 tokens (bwd_dkdv_kernel).  It is
+//     the only writer of dK/dV for its block and of the dlog_gate entries
+//     that point at it, which it sums in a fixed order.
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_mfma.h"
