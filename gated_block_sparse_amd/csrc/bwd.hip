@@ -516,47 +516,6 @@ constexpr int kTsSlot = 2 * kTsTensor + 64 * 4;      // Q, dO, lse[32], D[32]
 
 __device__ __forceinline__ int ts_swz(int q) { return 2 * (q & 7) + ((q >> 3) & 1); }
 
-typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ uint32_t bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// One LDS DMA copy: every lane fetches BYTES (16 or 4) from its own global
-// address; lane L's bytes land at LDS address lds_addr + L * BYTES (M0 holds
-// the wave-uniform base).  Issued from asm so that the compiler does not
-// track it: it would otherwise make every later read of the ring wait for
-// all copies in flight; completion is waited for explicitly (ts_sync).  M0
-// is saved and restored around the copy.
-template <int BYTES>
-__device__ __forceinline__ void lds_dma(const void* g, uint32_t lds_addr) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-  uint32_t keep;
-  if constexpr (BYTES == 16)
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
-  else
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-        "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
-}
-
-// Waits until at most N of this wave's vector-memory operations (here: LDS
-// DMA copies) are outstanding and its LDS operations are done, then joins the
-// workgroup barrier.  Written as one asm statement with a memory clobber so
-// that no LDS access moves across it; a fence would wait for every copy in
-// flight, including those of later steps.
-template <int N>
-__device__ __forceinline__ void ts_sync() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 
 template <int G>
 __global__ void __launch_bounds__(256, 2)
@@ -586,8 +545,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                                         log_gate ? log_gate + grow * n_tiles * k : nullptr,
                                         list_t, list_slot, list_beta, &s_count, s_wcount);
   const int n_steps = n_list * G * 2;
-  const uint32_t ring_lds = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)ring));
+  const uint32_t ring_lds = lds_addr_of(ring);
 
   // ---- LDS DMA of step s2 into slot s2 % kTsSlots.  Every wave copies rows
   // 8w..8w+7 of Q and of dO (two 1 KB copies each), wave 0 also the lse and
@@ -659,8 +617,8 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // this wave's copies for step s are done once at most the copies of
     // kTsSlots - 2 later steps remain; the barrier makes every wave's copies
     // visible and frees the slot read in step s - 1 for the next copy
-    if (wave == 0) ts_sync<5 * (kTsSlots - 2)>();
-    else ts_sync<4 * (kTsSlots - 2)>();
+    if (wave == 0) dma_sync<5 * (kTsSlots - 2)>();
+    else dma_sync<4 * (kTsSlots - 2)>();
     issue(s + kTsSlots - 1);
     if (pending >= 1 && tid == 0) {
       float tot = 0.f;
@@ -739,7 +697,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       pending = e;
     }
   }
-  ts_sync<0>();
+  dma_sync<0>();
   if (pending >= 1 && tid == 0) {
     float tot = 0.f;
 #pragma unroll

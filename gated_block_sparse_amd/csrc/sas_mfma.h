@@ -135,4 +135,53 @@ __device__ __forceinline__ void store_acc_col(const f32x16_t* acc, float mul, ui
     }
 }
 
+
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---- LDS DMA (global_load_lds).
+// LDS byte address of a __shared__ object (what M0 takes).
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const unsigned char*)p));
+}
+// One LDS DMA copy: every lane fetches BYTES (16 or 4) from its own global
+// address; lane L's bytes land at LDS address lds_addr + L * BYTES (M0 holds
+// the wave-uniform base).  Issued from asm so that the compiler does not
+// track it: it would otherwise make every later read of the ring wait for
+// all copies in flight; completion is waited for explicitly (dma_sync).  M0
+// is saved and restored around the copy.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* g, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t keep;
+  if constexpr (BYTES == 16)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "global_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(keep) : "s"(m0v), "v"(g) : "memory");
+}
+
+// Waits until at most N of this wave's vector-memory operations (here: LDS
+// DMA copies) are outstanding and its LDS operations are done, then joins the
+// workgroup barrier.  Written as one asm statement with a memory clobber so
+// that no LDS access moves across it; a fence would wait for every copy in
+// flight, including those of later steps.
+template <int N>
+__device__ __forceinline__ void dma_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 }  // namespace sas
