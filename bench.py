@@ -4,18 +4,21 @@
 Default workload: one decode step of one attention layer at the Qwen3-4B
 attention shape (32 query heads, 8 KV heads, d=128, bf16 KV cache, fp32
 accumulation), 64K context, block 64, top-k=16 + the current block, selector
-dim 128, synthetic seeded inputs.  A step is the whole decode-time path:
+dim 128, synthetic seeded inputs.  A step is the whole decode-time path, one
+sas_decode_step call with Wk_sel given:
 
-  1. sas_block_summaries on the newest complete block (the steady-state
-     refresh; it is due once every 64 steps, run here every step),
-  2. sas_decode_step: selector score over every history-block summary,
-     softmax-gate LSE, Top-K, then split-KV gated attention over the selected
-     blocks + B0 and the LSE merge (the selection's final merge runs inside
-     the attention's split kernel).
+  1. the summary of the newest complete block (the steady-state refresh; it
+     is due once every 64 steps, run here every step), fused into the
+     selection's first kernel,
+  2. selector score over every history-block summary, softmax-gate LSE,
+     Top-K, then split-KV gated attention over the selected blocks + B0 and
+     the LSE merge (the selection's final merge runs inside the attention's
+     split kernel).
 
-The same step is also timed through the separate entry points (sas_select,
-then sas_decode_fwd) for the per-op breakdown; the two give identical
-outputs (checked before timing).  The roofline figure is sas_decode_fwd's.
+The same step is also timed through the separate entry points
+(sas_block_summaries, sas_select, then sas_decode_fwd) for the per-op
+breakdown; the two give identical outputs (checked before timing).  The
+roofline figure is sas_decode_fwd's.
 
 Inputs are resident in HBM before timing starts.  Each timed step is
 bracketed by HIP events on the stream the library launches on; between steps
@@ -200,19 +203,16 @@ def run_decode(args, wl):
     idx2, lg2, slse2 = torch.empty_like(idx), torch.empty_like(lg), torch.empty_like(slse)
     o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
     a_step = (pd, q.data_ptr(), K.data_ptr(), V.data_ptr(), lens.data_ptr(), Wq.data_ptr(),
-              summ.data_ptr(), 1, scale, idx2.data_ptr(), lg2.data_ptr(), slse2.data_ptr(),
+              Wk.data_ptr(), summ.data_ptr(), 1, scale, idx2.data_ptr(), lg2.data_ptr(), slse2.data_ptr(),
               o2.data_ptr(), lse2.data_ptr(), ws_step.data_ptr(), ws_step.numel(), sp)
 
     def step_fused(evs=None):
-        """The production step: refresh + the fused selection/attention."""
+        """The production step: one sas_decode_step (refresh fused in)."""
         if evs:
             evs[0].record(stream)
-        st = lib.sas_block_summaries(*a_sum)
+        st = lib.sas_decode_step(*a_step)
         if evs:
             evs[1].record(stream)
-        st |= lib.sas_decode_step(*a_step)
-        if evs:
-            evs[2].record(stream)
         if st:
             raise S.SasError(st, lib.sas_last_error().decode())
 
@@ -256,24 +256,23 @@ def run_decode(args, wl):
     t_dec = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
 
     # the fused production step, cold the same way
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_steps)]
     for i in range(K_steps):
         if not args.no_flush:
             flush(i)
         step_fused(evf[i])
     torch.cuda.synchronize()
-    tot_f = [e[0].elapsed_time(e[2]) * 1e3 for e in evf]
-    t_fused = [e[1].elapsed_time(e[2]) * 1e3 for e in evf]
+    tot_f = [e[0].elapsed_time(e[1]) * 1e3 for e in evf]
 
     # hot-cache figures: the same steps with no eviction in between
     evh = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
     for i in range(K_steps):
         step(evh[i])
-    evhf = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    evhf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_steps)]
     for i in range(K_steps):
         step_fused(evhf[i])
     torch.cuda.synchronize()
-    hot_step = statistics.median([e[0].elapsed_time(e[2]) * 1e3 for e in evhf])
+    hot_step = statistics.median([e[0].elapsed_time(e[1]) * 1e3 for e in evhf])
     hot_step_unfused = statistics.median([e[0].elapsed_time(e[3]) * 1e3 for e in evh])
     hot_dec = statistics.median([e[2].elapsed_time(e[3]) * 1e3 for e in evh])
 
@@ -287,9 +286,9 @@ def run_decode(args, wl):
         s2.wait_stream(stream)
         with torch.cuda.stream(s2):
             sp2 = s2.cuda_stream
-            a2 = [a[:-1] + (sp2,) for a in (a_sum, a_step)]   # the stream is the last argument
+            a2 = a_step[:-1] + (sp2,)   # the stream is the last argument
             g.capture_begin()
-            sts = [lib.sas_block_summaries(*a2[0]), lib.sas_decode_step(*a2[1])]
+            sts = [lib.sas_decode_step(*a2)]
             g.capture_end()
         if any(sts):
             raise S.SasError(max(sts), lib.sas_last_error().decode())
@@ -334,7 +333,6 @@ def run_decode(args, wl):
             "summary_refresh": {"median": round(med(t_sum), 3)},
             "select": {"median": round(med(t_sel), 3), "p10": round(_pct(t_sel, .1), 3), "p90": round(_pct(t_sel, .9), 3)},
             "decode_attention": {"median": round(us_dec, 3), "p10": round(_pct(t_dec, .1), 3), "p90": round(_pct(t_dec, .9), 3)},
-            "select_and_attention_fused": {"median": round(med(t_fused), 3), "p10": round(_pct(t_fused, .1), 3), "p90": round(_pct(t_fused, .9), 3)},
             "step": {"median": round(us_step, 3), "p10": round(_pct(tot_f, .1), 3), "p90": round(_pct(tot_f, .9), 3)},
             "step_unfused": {"median": round(med(tot), 3), "p10": round(_pct(tot, .1), 3), "p90": round(_pct(tot, .9), 3)},
             "step_hot": round(hot_step, 3),

@@ -44,8 +44,8 @@ _SIGNATURES = {
     "sas_block_summaries": (_i32, [_PD, _vp, _vp, _vp, _i32, _i32, _vp, _vp]),
     "sas_select": (_i32, [_PD, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sas_decode_fwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
-    "sas_decode_step": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp, _vp,
-                               _vp, _vp, _sz, _vp]),
+    "sas_decode_step": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _sz, _vp]),
     "sas_prefill_fwd": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sas_bwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
                        _vp, _vp, _sz, _vp]),
@@ -204,10 +204,13 @@ def sas_decode_fwd(q, K, V, seq_lens, idx, log_gate, scale=None, o=None, lse=Non
 
 
 def sas_decode_step(q, K, V, seq_lens, Wq_sel, summ, top_k, gated=True, scale=None, idx=None,
-                    log_gate=None, score_lse=None, o=None, lse=None, ws=None, want_lse=True):
+                    log_gate=None, score_lse=None, o=None, lse=None, ws=None, want_lse=True,
+                    Wk_sel=None):
     """Fused selection + gated sparse decode attention (the outputs of
     sas_select(SAS_SELECT_DECODE) followed by sas_decode_fwd).  q [B,Hq,d];
-    K,V [B,Hkv,t_max,d]; summ [B,Hkv,t_max//64,d_sel].
+    K,V [B,Hkv,t_max,d]; summ [B,Hkv,t_max//64,d_sel].  With Wk_sel, the
+    summary of each sequence's newest complete block is refreshed into summ
+    first (as sas_block_summaries over that block).
     Returns (idx, log_gate, score_lse, o, lse | None)."""
     B, Hq, d = q.shape
     _, Hkv, t_max, _ = K.shape
@@ -227,7 +230,8 @@ def sas_decode_step(q, K, V, seq_lens, Wq_sel, summ, top_k, gated=True, scale=No
         lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     ws, ws_bytes = _workspace(SAS_OP_DECODE_STEP, dims, 0, ws, dev)
     _check(load_library().sas_decode_step(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V),
-                                          _ptr(seq_lens), _ptr(Wq_sel), _ptr(summ), int(gated),
+                                          _ptr(seq_lens), _ptr(Wq_sel), _ptr(Wk_sel), _ptr(summ),
+                                          int(gated),
                                           scale, _ptr(idx), _ptr(log_gate), _ptr(score_lse),
                                           _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream()))
     return idx, log_gate, score_lse, o, lse

@@ -411,10 +411,10 @@ static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, co
 template <typename T, int D, int G, int NB>
 static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K, const void* V,
                                  const int32_t* seq_lens, const float* Wq, const float* summ,
-                                 int gated, float scale, int32_t* idx, float* log_gate,
+                                 const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
                                  float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
-  sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
-                                             ws, st);
+  sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate,
+                                             score_lse, ws, st);
   if (s != SAS_OK) return s;
   const SelectDecodeLayout L = select_decode_layout(d, ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -451,25 +451,25 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
 template <typename T, int D, int G>
 static sas_status launch_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              int gated, float scale, int32_t* idx, float* log_gate,
+                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
   if (decode_blocks_per_unit(d) == 2)
-    return launch_step_nb<T, D, G, 2>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx,
+    return launch_step_nb<T, D, G, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx,
                                       log_gate, score_lse, o, lse, ws, st);
-  return launch_step_nb<T, D, G, 1>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate,
+  return launch_step_nb<T, D, G, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate,
                                     score_lse, o, lse, ws, st);
 }
 
 template <typename T, int D>
 static sas_status step_by_group(const sas_dims& d, const void* q, const void* K, const void* V,
                                 const int32_t* seq_lens, const float* Wq, const float* summ,
-                                int gated, float scale, int32_t* idx, float* log_gate,
+                                const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
                                 float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_step<T, D, 1>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 2: return launch_step<T, D, 2>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 4: return launch_step<T, D, 4>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 8: return launch_step<T, D, 8>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 1: return launch_step<T, D, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 2: return launch_step<T, D, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 4: return launch_step<T, D, 4>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 8: return launch_step<T, D, 8>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
   }
   return fail(SAS_ERR_UNSUPPORTED, "decode step: group size");
 }
@@ -480,16 +480,16 @@ size_t decode_step_ws_bytes(const sas_dims& d) {
 
 sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              int gated, float scale, int32_t* idx, float* log_gate,
+                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
   if (d.dtype == SAS_BF16) {
     if (d.head_dim == 128)
-      return step_by_group<uint16_t, 128>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    return step_by_group<uint16_t, 64>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+      return step_by_group<uint16_t, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    return step_by_group<uint16_t, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
   }
   if (d.head_dim == 128)
-    return step_by_group<float, 128>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-  return step_by_group<float, 64>(d, q, K, V, seq_lens, Wq, summ, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    return step_by_group<float, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+  return step_by_group<float, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
 }
 
 template <typename T, int D>

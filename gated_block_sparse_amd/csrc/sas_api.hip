@@ -157,7 +157,8 @@ sas_status sas_decode_fwd(const sas_dims* dims, const void* q, const void* K, co
 }
 
 sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, const void* V,
-                           const int32_t* seq_lens, const float* Wq_sel, const float* summ,
+                           const int32_t* seq_lens, const float* Wq_sel, const float* Wk_sel,
+                           float* summ,
                            int32_t gated, float scale, int32_t* idx, float* log_gate,
                            float* score_lse, void* o, float* lse, void* ws, size_t ws_bytes,
                            void* stream) {
@@ -177,7 +178,7 @@ sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, c
   if (!(scale > 0.0f))
     return fail(SAS_ERR_INVALID_ARGUMENT, "scale must be a positive number");
   SAS_TRY(check_ws(decode_step_ws_bytes(*dims), ws, ws_bytes));
-  return launch_decode_step(*dims, q, K, V, seq_lens, Wq_sel, summ, gated != 0, scale, idx,
+  return launch_decode_step(*dims, q, K, V, seq_lens, Wq_sel, summ, Wk_sel, gated != 0, scale, idx,
                             log_gate, score_lse, o, lse, ws, static_cast<hipStream_t>(stream));
 }
 

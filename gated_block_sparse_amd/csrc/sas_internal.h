@@ -60,10 +60,13 @@ struct SelectDecodeLayout {
 SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws);
 // The first stage of the decode selection alone (scores, per-chunk state);
 // when a row fits one chunk it also writes the final idx/log_gate/score_lse.
+// With Wk non-null, the workgroup holding each row's newest complete block
+// C-1 first recomputes that block's summary from K (the summaries kernel's
+// arithmetic, same bits), stores it into summ and scores with it.
 sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
-                                       const float* Wq, const float* summ, int32_t* idx,
-                                       float* log_gate, float* score_lse, void* ws,
-                                       hipStream_t st);
+                                       const float* Wq, const float* summ, const void* K,
+                                       const float* Wk, int32_t* idx, float* log_gate,
+                                       float* score_lse, void* ws, hipStream_t st);
 // Its second stage: merges the per-chunk state into idx/log_gate/score_lse
 // (nothing to do when a row fits one chunk).
 sas_status launch_select_decode_merge(const sas_dims& d, const int32_t* seq_lens, int32_t* idx,
@@ -78,7 +81,7 @@ sas_status launch_decode_fwd(const sas_dims& d, const void* q, const void* K, co
 size_t decode_step_ws_bytes(const sas_dims& d);
 sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              int gated, float scale, int32_t* idx, float* log_gate,
+                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st);
 
 size_t selector_bwd_ws_bytes(const sas_dims& d, int q_len);

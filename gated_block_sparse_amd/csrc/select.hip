@@ -19,6 +19,7 @@
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_select_dev.h"
+#include "sas_summary_dev.h"
 
 namespace sas {
 
@@ -38,8 +39,10 @@ namespace sas {
 template <typename T, int D, int DS, int G, int R>
 __global__ void __launch_bounds__(kSelThreads)
 select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
-                           const float* __restrict__ Wq, const float* __restrict__ summ, int Hkv,
-                           int t_max, int c_max, int k, int kc, int nchunk,
+                           const float* __restrict__ Wq, const float* summ,
+                           const T* __restrict__ K, const float* __restrict__ Wk,
+                           float* summ_out, int Hkv, int t_max, int c_max, int k, int kc,
+                           int nchunk,
                            float* __restrict__ scores, float2* __restrict__ part,
                            uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse) {
@@ -54,6 +57,9 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   __shared__ uint64_t lists[NW][64];
   __shared__ uint64_t best[kMaxTopK];
   __shared__ float red[2][NW];
+  __shared__ float rmean[D];   // fused refresh: pooled keys, then the new summary
+  __shared__ float rsumm[DS];
+  static_assert(kSelThreads == kSumThreads, "the refresh uses the summaries' thread mapping");
 
   const int b = blockIdx.z, r = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hw = tid >> 5, l32 = tid & 31;
@@ -63,6 +69,9 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const size_t p = row * nchunk + chunk;
   const int n = max(0, min(kChunk, C - m0));
+  // fused refresh (Wk given): this workgroup holds the newest complete block
+  const int mnew = C - 1;
+  const bool refresh = Wk != nullptr && n > 0 && mnew >= m0 && mnew < m0 + n;
 
   // ---- all loads up front
   float qraw[G][PD];
@@ -103,6 +112,35 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
         const float2 x = *reinterpret_cast<const float2*>(srow + static_cast<size_t>(i) * DS);
         xs[j][0] = x.x; xs[j][1] = x.y;
       }
+    }
+  }
+  // ---- fused refresh of block mnew: its summary is recomputed from K with
+  // the summaries kernel's own arithmetic, stored, and replaces the (stale)
+  // slice of row mnew loaded above
+  if (refresh) {
+    WkSlice<D, DS> wsl;
+    wsl.load(Wk, tid);
+    if (wave == 0) {
+      BlockMean<T, D> bm;
+      bm.load(K + (row * t_max + static_cast<size_t>(mnew) * kBlock) * D, lane);
+      bm.reduce(lane, rmean);
+    }
+    __syncthreads();
+    const float a = wsl.project(rmean, tid);
+    if (tid % WkSlice<D, DS>::SPLIT == 0) {
+      const int jo = tid / WkSlice<D, DS>::SPLIT;
+      rsumm[jo] = a;
+      summ_out[(row * c_max + mnew) * static_cast<size_t>(DS) + jo] = a;
+    }
+    __syncthreads();
+    const int i = mnew - m0;
+    if (hw == (i & 7)) {
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (j == (i >> 3)) {
+#pragma unroll
+          for (int e = 0; e < PL; ++e) xs[j][e] = rsumm[l32 * PL + e];
+        }
     }
   }
   // ---- pooled query, projected: half wave hw owns Wq_sel rows hw + 8j
@@ -256,9 +294,9 @@ SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws) {
 
 template <typename T, int D, int DS, int G>
 static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
-                                   const float* Wq, const float* summ, int32_t* idx,
-                                   float* log_gate, float* score_lse, float* scores, void* ws,
-                                   hipStream_t st) {
+                                   const float* Wq, const float* summ, const void* K,
+                                   const float* Wk, int32_t* idx, float* log_gate,
+                                   float* score_lse, float* scores, void* ws, hipStream_t st) {
   const SelectDecodeLayout L = select_decode_layout(d, ws);
   if (L.nlist * L.kc > kMaxMergeKeys)
     return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
@@ -266,9 +304,9 @@ static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32
 #define SAS_SD_CHUNK(R)                                                                       \
   hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G, R>),                              \
                      dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,           \
-                     static_cast<const T*>(q), seq_lens, Wq, summ, d.n_kv_heads, d.t_max,       \
-                     d.t_max / kBlock, d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx,    \
-                     log_gate, score_lse)
+                     static_cast<const T*>(q), seq_lens, Wq, summ, static_cast<const T*>(K),    \
+                     Wk, const_cast<float*>(summ), d.n_kv_heads, d.t_max, d.t_max / kBlock,     \
+                     d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx, log_gate, score_lse)
   switch (decode_chunk_rows(d)) {
     case 8: SAS_SD_CHUNK(8); break;
     case 16: SAS_SD_CHUNK(16); break;
@@ -293,8 +331,8 @@ template <typename T, int D, int DS, int G>
 static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq_lens,
                             const float* Wq, const float* summ, int32_t* idx, float* log_gate,
                             float* score_lse, float* scores, void* ws, hipStream_t st) {
-  sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, idx, log_gate,
-                                               score_lse, scores, ws, st);
+  sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, nullptr, nullptr, idx,
+                                               log_gate, score_lse, scores, ws, st);
   if (s != SAS_OK) return s;
   return launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
 }
@@ -359,10 +397,11 @@ struct SelDecode {
 template <typename T, int D, int DS, int G>
 struct SelDecodeChunks {
   static sas_status run(const sas_dims& d, const void* q, const int32_t* seq_lens, const float* Wq,
-                        const float* summ, int32_t* idx, float* log_gate, float* score_lse,
-                        float* scores, void* ws, hipStream_t st) {
-    return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
-                                         scores, ws, st);
+                        const float* summ, const void* K, const float* Wk, int32_t* idx,
+                        float* log_gate, float* score_lse, float* scores, void* ws,
+                        hipStream_t st) {
+    return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate,
+                                         score_lse, scores, ws, st);
   }
 };
 
@@ -413,10 +452,10 @@ sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t*
 }
 
 sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
-                                       const float* Wq, const float* summ, int32_t* idx,
-                                       float* log_gate, float* score_lse, void* ws,
-                                       hipStream_t st) {
-  return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, idx, log_gate, score_lse,
+                                       const float* Wq, const float* summ, const void* K,
+                                       const float* Wk, int32_t* idx, float* log_gate,
+                                       float* score_lse, void* ws, hipStream_t st) {
+  return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate, score_lse,
                                   static_cast<float*>(nullptr), ws, st);
 }
 

@@ -13,23 +13,18 @@
 // lanes combine their slices of one output with a butterfly.
 #include "sas_device.h"
 #include "sas_internal.h"
+#include "sas_summary_dev.h"
 
 namespace sas {
 
 constexpr int kSumBlocks = 16;   // blocks per workgroup
-constexpr int kSumThreads = 256;
 
 template <typename T, int D, int DS>
 __global__ void __launch_bounds__(kSumThreads)
 block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_lens,
                        const float* __restrict__ Wk, int blk_begin, int blk_end, int Hkv,
                        int t_max, int c_max, float* __restrict__ summ) {
-  constexpr int EPL = Vec16<T>::N;          // elements per 16-byte load
-  constexpr int LPR = D / EPL;              // lanes per K row
-  constexpr int RPI = 64 / LPR;             // rows per load instruction (per wave)
-  constexpr int NI = kBlock / RPI;          // load instructions per block
-  constexpr int SPLIT = kSumThreads / DS;   // lanes per output channel
-  constexpr int CW = D / SPLIT;             // input channels per lane
+  using WS = WkSlice<D, DS>;
   __shared__ float mean[kSumBlocks][D];
 
   const int b = blockIdx.z, r = blockIdx.y;
@@ -41,53 +36,21 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   const int nblk = last - first;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j = tid / SPLIT, part = tid % SPLIT;
-  float w[CW];
-  {
-    const float4* wr = reinterpret_cast<const float4*>(Wk + static_cast<size_t>(j) * D + part * CW);
-#pragma unroll
-    for (int c4 = 0; c4 < CW / 4; ++c4) {
-      const float4 x = wr[c4];
-      w[4 * c4 + 0] = x.x;
-      w[4 * c4 + 1] = x.y;
-      w[4 * c4 + 2] = x.z;
-      w[4 * c4 + 3] = x.w;
-    }
-  }
+  WS ws;
+  ws.load(Wk, tid);
 
   const T* Kr = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
-  const int col = lane % LPR, row0 = lane / LPR;
   for (int jb = wave; jb < nblk; jb += 4) {
-    const T* blk = Kr + static_cast<size_t>(first + jb) * kBlock * D;
-    uint4 raw[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      raw[i] = *reinterpret_cast<const uint4*>(blk + (row0 + i * RPI) * D + col * EPL);
-    float acc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float f[EPL];
-      Vec16<T>::unpack(raw[i], f);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += f[e];
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = wave_sum_from(acc[e], LPR);
-    if (lane < LPR) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) mean[jb][col * EPL + e] = acc[e] * (1.0f / kBlock);
-    }
+    BlockMean<T, D> bm;
+    bm.load(Kr + static_cast<size_t>(first + jb) * kBlock * D, lane);
+    bm.reduce(lane, mean[jb]);
   }
   __syncthreads();
 
   float* dst = summ + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(c_max) * DS;
+  const int j = tid / WS::SPLIT, part = tid % WS::SPLIT;
   for (int jb = 0; jb < nblk; ++jb) {
-    float a = 0.f;
-#pragma unroll
-    for (int c = 0; c < CW; ++c) a += w[c] * mean[jb][part * CW + c];
-    a = group_sum(a, SPLIT);
+    const float a = ws.project(mean[jb], tid);
     if (part == 0) dst[static_cast<size_t>(first + jb) * DS + j] = a;
   }
 }

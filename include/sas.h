@@ -150,12 +150,19 @@ sas_status sas_decode_fwd(const sas_dims* dims, const void* q, const void* K, co
  * sas_decode_fwd(..., gated ? log_gate : NULL, ...) on its selection, in
  * fewer launches: the merge of the selection's per-chunk candidates runs
  * inside the attention's split kernel instead of a kernel of its own.
- * Arguments as in those two calls; idx/log_gate [B,Hkv,1,k] and score_lse
+ * Wk_sel (nullable) fp32 [d_sel,d]: when given, the step first refreshes the
+ * summary of each sequence's newest complete history block m = C-1 (C =
+ * (seq_lens[b]-1)/64 >= 1), exactly as sas_block_summaries(..., C-1, C, ...)
+ * would (same bits), writes it into summ and scores with it: the same
+ * outputs, summ included, as that call followed by the two above.  summ is
+ * then read and written; with Wk_sel NULL it is only read.
+ * Arguments as in those calls; idx/log_gate [B,Hkv,1,k] and score_lse
  * [B,Hkv,1] are outputs here; gated = 0 gives the ungated inference rule for
  * the attention (log_gate is still written).
  * ws: at least sas_workspace_bytes(SAS_OP_DECODE_STEP, dims, 0). */
 sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, const void* V,
-                           const int32_t* seq_lens, const float* Wq_sel, const float* summ,
+                           const int32_t* seq_lens, const float* Wq_sel, const float* Wk_sel,
+                           float* summ,
                            int32_t gated, float scale, int32_t* idx, float* log_gate,
                            float* score_lse, void* o, float* lse, void* ws, size_t ws_bytes,
                            void* stream);

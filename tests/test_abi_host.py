@@ -94,14 +94,15 @@ def test_decode_step_validation(lib):
     # the selection's chunk state, 256-byte aligned, then the attention partials
     sel = B.sas_workspace_bytes(B.SAS_OP_SELECT_DECODE, d)
     assert need == (sel + 255) // 256 * 256 + B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d)
-    step = lambda dims, ws_bytes, scale=0.1, q=FAKE, lg=FAKE: lib.sas_decode_step(
-        ctypes.byref(dims), q, FAKE, FAKE, FAKE, FAKE, FAKE, 1, scale, FAKE, lg, FAKE, FAKE,
+    step = lambda dims, ws_bytes, scale=0.1, q=FAKE, lg=FAKE, wk=None: lib.sas_decode_step(
+        ctypes.byref(dims), q, FAKE, FAKE, FAKE, FAKE, wk, FAKE, 1, scale, FAKE, lg, FAKE, FAKE,
         FAKE, FAKE, ws_bytes, None)
     assert step(d, need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
     assert step(d, need, scale=-1.0) == B.SAS_ERR_INVALID_ARGUMENT
     assert step(d, need, q=None) == B.SAS_ERR_INVALID_ARGUMENT
     assert step(d, need, lg=None) == B.SAS_ERR_INVALID_ARGUMENT   # k > 0 needs log_gate
     assert step(_dims(head_dim=96), 1 << 40) == B.SAS_ERR_UNSUPPORTED
+    assert step(_dims(head_dim=96), 1 << 40, wk=FAKE) == B.SAS_ERR_UNSUPPORTED
 
 
 def test_selector_bwd_validation(lib):

@@ -109,6 +109,22 @@ def run_decode_case(p: synth.Problem, t_max=None, check_e2e=True, label=""):
         assert torch.equal(slse_f, slse_g), label
         assert torch.equal(o_f, o_r) and torch.equal(lse_f, lse_r), (label, gated)
 
+    # the step with its fused refresh: summ starts with every newest complete
+    # block's summary spoiled, and must end equal to sas_block_summaries' bits
+    # with the same selection and attention as before
+    summ_s = summ.clone()
+    for b in range(B):
+        C = O.n_history_blocks(int(p.seq_lens[b]))
+        if C:
+            summ_s[b, :, C - 1] = 1e3
+    idx_f, lg_f, slse_f, o_f, lse_f = S.sas_decode_step(q, K, V, lens, Wq, summ_s, k, Wk_sel=Wk)
+    o_r, lse_r = S.sas_decode_fwd(q, K, V, lens, idx_g, lg_g)
+    torch.cuda.synchronize()
+    assert torch.equal(summ_s, summ), label
+    assert torch.equal(idx_f, idx_g) and torch.equal(lg_f, lg_g), label
+    assert torch.equal(slse_f, slse_g), label
+    assert torch.equal(o_f, o_r) and torch.equal(lse_f, lse_r), label
+
     # attention on the oracle's selection
     oidx, olg = idx_dev(ref["idx"][:, :, None]), lg_dev(ref["lg"][:, :, None])
     o, lse = S.sas_decode_fwd(q, K, V, lens, oidx, olg)
