@@ -44,8 +44,8 @@ template <int G, int D> struct SplitLds {
 // workgroup calls it.
 template <typename T, int D, int G, int NB>
 __device__ __forceinline__ void split_unit(const T* __restrict__ q, const T* __restrict__ K,
-                                           const T* __restrict__ V, size_t row, int t_max,
-                                           const int* start, const int* ntok, const float* beta2,
+                                           const T* __restrict__ V, size_t row,
+                                           const size_t* brow, const int* ntok, const float* beta2,
                                            float scale2, float* __restrict__ out,
                                            SplitLds<G, D>& sh) {
   constexpr int EPL = Vec16<T>::N;      // elements per 16-byte load
@@ -65,8 +65,8 @@ __device__ __forceinline__ void split_unit(const T* __restrict__ q, const T* __r
   uint4 kr[NB][NI], vr[NB][NI];
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
-    const T* Kb = K + (row * t_max + start[bb]) * static_cast<size_t>(D) + col * EPL;
-    const T* Vb = V + (row * t_max + start[bb]) * static_cast<size_t>(D) + col * EPL;
+    const T* Kb = K + brow[bb] * static_cast<size_t>(D) + col * EPL;
+    const T* Vb = V + brow[bb] * static_cast<size_t>(D) + col * EPL;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int j = wave * 16 + i * RPI + rsub;
@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(kDecThreads)
 decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
                     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
                     const float* __restrict__ log_gate, int gated, float scale2, int Hkv,
-                    int t_max, int k, float* __restrict__ part) {
+                    int t_max, int k, KvPages pg, float* __restrict__ part) {
   constexpr int PF = DecPartial<G, D>::kFloats;
   __shared__ SplitLds<G, D> sh;
   const int unit = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
@@ -228,17 +228,18 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* _
   const int len = clamp_len(seq_lens[b], t_max);
   const int C = (len - 1) / kBlock;
   // the NB slots of this unit: history slots u < k, then B0 as slot k
-  int start[NB], ntok[NB];
+  size_t brow[NB];
+  int ntok[NB];
   float beta2[NB];  // bias, already multiplied by log2(e)
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
     const int u = unit * NB + bb;
     const bool hist = u < k && mi[bb] >= 0, cur = u == k;
-    start[bb] = hist ? mi[bb] * kBlock : (cur ? C * kBlock : 0);
+    brow[bb] = (hist || cur) ? kv_block_row(pg, b, r, hist ? mi[bb] : C, Hkv, t_max) : 0;
     ntok[bb] = hist ? kBlock : (cur ? len - C * kBlock : 0);
     beta2[bb] = (hist && gated) ? lgi[bb] * kLog2e : 0.f;
   }
-  split_unit<T, D, G, NB>(q, K, V, row, t_max, start, ntok, beta2, scale2,
+  split_unit<T, D, G, NB>(q, K, V, row, brow, ntok, beta2, scale2,
                           part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
 }
 
@@ -253,7 +254,7 @@ decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
                            const T* __restrict__ V, const int32_t* __restrict__ seq_lens,
                            const float2* __restrict__ cpart, const uint64_t* __restrict__ cand,
                            int nchunk, int nlist, int kc, int gated, float scale2, int Hkv,
-                           int t_max, int k, int32_t* __restrict__ idx,
+                           int t_max, int k, KvPages pg, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse,
                            float* __restrict__ part) {
   constexpr int PF = DecPartial<G, D>::kFloats;
@@ -281,27 +282,28 @@ decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
     }
     if (tid == 0) score_lse[row] = lse_s;
   }
-  int start[NB], ntok[NB];
+  size_t brow[NB];
+  int ntok[NB];
   float beta2[NB];
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) {
     const int u = unit * NB + bb;
-    start[bb] = 0;
+    brow[bb] = 0;
     ntok[bb] = 0;
     beta2[bb] = 0.f;
     if (u < k) {
       const int m = sel_blk[u];
       if (m >= 0) {
-        start[bb] = m * kBlock;
+        brow[bb] = kv_block_row(pg, b, r, m, Hkv, t_max);
         ntok[bb] = kBlock;
         if (gated) beta2[bb] = sel_lg[u] * kLog2e;
       }
     } else if (u == k) {
-      start[bb] = C * kBlock;
-      ntok[bb] = len - start[bb];
+      brow[bb] = kv_block_row(pg, b, r, C, Hkv, t_max);
+      ntok[bb] = len - C * kBlock;
     }
   }
-  split_unit<T, D, G, NB>(q, K, V, row, t_max, start, ntok, beta2, scale2,
+  split_unit<T, D, G, NB>(q, K, V, row, brow, ntok, beta2, scale2,
                           part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
 }
 
@@ -374,7 +376,7 @@ template <typename T, int D, int G, int NB>
 static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K, const void* V,
                                 const int32_t* seq_lens, const int32_t* idx,
                                 const float* log_gate, float scale, void* o, float* lse,
-                                void* ws, hipStream_t st) {
+                                void* ws, hipStream_t st, KvPages pg = KvPages{nullptr, 0}) {
   float* part = static_cast<float*>(ws);
   const int n_units = (d.top_k + NB) / NB;
   // k = 0 or the ungated rule may pass NULL idx / log_gate: the kernel then
@@ -385,7 +387,7 @@ static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K,
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx_r, lg_r,
                      log_gate != nullptr ? 1 : 0, scale * kLog2e, d.n_kv_heads, d.t_max,
-                     d.top_k, part);
+                     d.top_k, pg, part);
   sas_status s = check_launch("decode_split");
   if (s != SAS_OK) return s;
   constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
@@ -411,9 +413,10 @@ static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, co
 template <typename T, int D, int G, int NB>
 static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K, const void* V,
                                  const int32_t* seq_lens, const float* Wq, const float* summ,
-                                 const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
-                                 float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
-  sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate,
+                                 const float* Wk, KvPages pg, int gated, float scale,
+                                 int32_t* idx, float* log_gate, float* score_lse, void* o,
+                                 float* lse, void* ws, hipStream_t st) {
+  sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate,
                                              score_lse, ws, st);
   if (s != SAS_OK) return s;
   const SelectDecodeLayout L = select_decode_layout(d, ws);
@@ -421,7 +424,7 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
                                          ((select_decode_ws_bytes(d) + 255) & ~size_t(255)));
   if (L.nchunk == 1)  // the chunk stage already wrote the selection
     return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
-                                      scale, o, lse, part, st);
+                                      scale, o, lse, part, st, pg);
   if constexpr (NB > 1) {
     // Grids this large keep the chip busy on their own; there the redundant
     // per-workgroup merge costs more than the launch it saves, so the
@@ -429,7 +432,7 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
     s = launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
     if (s != SAS_OK) return s;
     return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
-                                      scale, o, lse, part, st);
+                                      scale, o, lse, part, st, pg);
   } else {
   const int n_units = (d.top_k + NB) / NB;
   hipLaunchKernelGGL((decode_select_split_kernel<T, D, G, NB>),
@@ -437,7 +440,7 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
                      2 * L.nlist * L.kc * sizeof(uint64_t), st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, L.part, L.cand,
                      L.nchunk, L.nlist, L.kc, gated, scale * kLog2e, d.n_kv_heads, d.t_max,
-                     d.top_k, idx, log_gate, score_lse, part);
+                     d.top_k, pg, idx, log_gate, score_lse, part);
   s = check_launch("decode_select_split");
   if (s != SAS_OK) return s;
   constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
@@ -451,25 +454,26 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
 template <typename T, int D, int G>
 static sas_status launch_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
-                              float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
+                              const float* Wk, KvPages pg, int gated, float scale, int32_t* idx,
+                              float* log_gate, float* score_lse, void* o, float* lse, void* ws,
+                              hipStream_t st) {
   if (decode_blocks_per_unit(d) == 2)
-    return launch_step_nb<T, D, G, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx,
+    return launch_step_nb<T, D, G, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx,
                                       log_gate, score_lse, o, lse, ws, st);
-  return launch_step_nb<T, D, G, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate,
+  return launch_step_nb<T, D, G, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate,
                                     score_lse, o, lse, ws, st);
 }
 
 template <typename T, int D>
 static sas_status step_by_group(const sas_dims& d, const void* q, const void* K, const void* V,
                                 const int32_t* seq_lens, const float* Wq, const float* summ,
-                                const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
+                                const float* Wk, KvPages pg, int gated, float scale, int32_t* idx, float* log_gate,
                                 float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_step<T, D, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 2: return launch_step<T, D, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 4: return launch_step<T, D, 4>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    case 8: return launch_step<T, D, 8>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 1: return launch_step<T, D, 1>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 2: return launch_step<T, D, 2>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 4: return launch_step<T, D, 4>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    case 8: return launch_step<T, D, 8>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
   }
   return fail(SAS_ERR_UNSUPPORTED, "decode step: group size");
 }
@@ -480,16 +484,16 @@ size_t decode_step_ws_bytes(const sas_dims& d) {
 
 sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
+                              const float* Wk, KvPages pg, int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st) {
   if (d.dtype == SAS_BF16) {
     if (d.head_dim == 128)
-      return step_by_group<uint16_t, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-    return step_by_group<uint16_t, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+      return step_by_group<uint16_t, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    return step_by_group<uint16_t, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
   }
   if (d.head_dim == 128)
-    return step_by_group<float, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
-  return step_by_group<float, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+    return step_by_group<float, 128>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
+  return step_by_group<float, 64>(d, q, K, V, seq_lens, Wq, summ, Wk, pg, gated, scale, idx, log_gate, score_lse, o, lse, ws, st);
 }
 
 template <typename T, int D>

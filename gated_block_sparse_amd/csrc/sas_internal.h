@@ -23,6 +23,31 @@ sas_status check_launch(const char* what);
 
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// ------------------------------------------------------ K/V cache layout ---
+// Contiguous (table == nullptr): K/V [B,Hkv,t_max,d], summaries
+// [B,Hkv,t_max/64,d_sel].  Paged: logical block m of sequence b lives in page
+// table[b * max_pages + m] of a pool K/V [n_pages,Hkv,64,d], and its summary
+// in row (page, r) of [n_pages,Hkv,d_sel].
+struct KvPages {
+  const int32_t* table;
+  int max_pages;
+};
+// Index of the first K/V row of block m of (b, r).
+__device__ __forceinline__ size_t kv_block_row(const KvPages& pg, int b, int r, int m, int Hkv,
+                                               int t_max) {
+  if (pg.table)
+    return (static_cast<size_t>(pg.table[static_cast<size_t>(b) * pg.max_pages + m]) * Hkv + r) *
+           kBlock;
+  return (static_cast<size_t>(b) * Hkv + r) * t_max + static_cast<size_t>(m) * kBlock;
+}
+// Summary row of block m of (b, r).
+__device__ __forceinline__ size_t summ_row(const KvPages& pg, int b, int r, int m, int Hkv,
+                                           int c_max) {
+  if (pg.table)
+    return static_cast<size_t>(pg.table[static_cast<size_t>(b) * pg.max_pages + m]) * Hkv + r;
+  return (static_cast<size_t>(b) * Hkv + r) * c_max + m;
+}
+
 // ---------------------------------------------------------------- bf16 ---
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -41,6 +66,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
                                   const float* Wk, int blk_begin, int blk_end, float* summ,
                                   hipStream_t st);
+sas_status launch_page_summaries(const sas_dims& d, const void* K, const int32_t* pages, int n,
+                                 const float* Wk, float* summ, hipStream_t st);
 
 size_t select_decode_ws_bytes(const sas_dims& d);
 sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t* seq_lens,
@@ -65,8 +92,9 @@ SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws);
 // arithmetic, same bits), stores it into summ and scores with it.
 sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                        const float* Wq, const float* summ, const void* K,
-                                       const float* Wk, int32_t* idx, float* log_gate,
-                                       float* score_lse, void* ws, hipStream_t st);
+                                       const float* Wk, KvPages pg, int32_t* idx,
+                                       float* log_gate, float* score_lse, void* ws,
+                                       hipStream_t st);
 // Its second stage: merges the per-chunk state into idx/log_gate/score_lse
 // (nothing to do when a row fits one chunk).
 sas_status launch_select_decode_merge(const sas_dims& d, const int32_t* seq_lens, int32_t* idx,
@@ -81,7 +109,7 @@ sas_status launch_decode_fwd(const sas_dims& d, const void* q, const void* K, co
 size_t decode_step_ws_bytes(const sas_dims& d);
 sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,
                               const int32_t* seq_lens, const float* Wq, const float* summ,
-                              const float* Wk, int gated, float scale, int32_t* idx, float* log_gate,
+                              const float* Wk, KvPages pg, int gated, float scale, int32_t* idx, float* log_gate,
                               float* score_lse, void* o, float* lse, void* ws, hipStream_t st);
 
 size_t selector_bwd_ws_bytes(const sas_dims& d, int q_len);

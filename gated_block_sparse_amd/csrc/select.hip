@@ -41,8 +41,8 @@ __global__ void __launch_bounds__(kSelThreads)
 select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ seq_lens,
                            const float* __restrict__ Wq, const float* summ,
                            const T* __restrict__ K, const float* __restrict__ Wk,
-                           float* summ_out, int Hkv, int t_max, int c_max, int k, int kc,
-                           int nchunk,
+                           float* summ_out, KvPages pg, int Hkv, int t_max, int c_max, int k,
+                           int kc, int nchunk,
                            float* __restrict__ scores, float2* __restrict__ part,
                            uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse) {
@@ -97,7 +97,6 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
       }
     }
   }
-  const float* srow = summ + (row * c_max + m0) * static_cast<size_t>(DS) + l32 * PL;
   float xs[R][PL];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
@@ -105,11 +104,12 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < PL; ++e) xs[j][e] = 0.f;
     if (i < n) {
+      const float* sp = summ + summ_row(pg, b, r, m0 + i, Hkv, c_max) * DS + l32 * PL;
       if constexpr (PL == 4) {
-        const float4 x = *reinterpret_cast<const float4*>(srow + static_cast<size_t>(i) * DS);
+        const float4 x = *reinterpret_cast<const float4*>(sp);
         xs[j][0] = x.x; xs[j][1] = x.y; xs[j][2] = x.z; xs[j][3] = x.w;
       } else {
-        const float2 x = *reinterpret_cast<const float2*>(srow + static_cast<size_t>(i) * DS);
+        const float2 x = *reinterpret_cast<const float2*>(sp);
         xs[j][0] = x.x; xs[j][1] = x.y;
       }
     }
@@ -122,7 +122,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
     wsl.load(Wk, tid);
     if (wave == 0) {
       BlockMean<T, D> bm;
-      bm.load(K + (row * t_max + static_cast<size_t>(mnew) * kBlock) * D, lane);
+      bm.load(K + kv_block_row(pg, b, r, mnew, Hkv, t_max) * D, lane);
       bm.reduce(lane, rmean);
     }
     __syncthreads();
@@ -130,7 +130,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
     if (tid % WkSlice<D, DS>::SPLIT == 0) {
       const int jo = tid / WkSlice<D, DS>::SPLIT;
       rsumm[jo] = a;
-      summ_out[(row * c_max + mnew) * static_cast<size_t>(DS) + jo] = a;
+      summ_out[summ_row(pg, b, r, mnew, Hkv, c_max) * DS + jo] = a;
     }
     __syncthreads();
     const int i = mnew - m0;
@@ -295,7 +295,7 @@ SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws) {
 template <typename T, int D, int DS, int G>
 static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                    const float* Wq, const float* summ, const void* K,
-                                   const float* Wk, int32_t* idx, float* log_gate,
+                                   const float* Wk, KvPages pg, int32_t* idx, float* log_gate,
                                    float* score_lse, float* scores, void* ws, hipStream_t st) {
   const SelectDecodeLayout L = select_decode_layout(d, ws);
   if (L.nlist * L.kc > kMaxMergeKeys)
@@ -305,7 +305,7 @@ static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32
   hipLaunchKernelGGL((select_decode_chunk_kernel<T, D, DS, G, R>),                              \
                      dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,           \
                      static_cast<const T*>(q), seq_lens, Wq, summ, static_cast<const T*>(K),    \
-                     Wk, const_cast<float*>(summ), d.n_kv_heads, d.t_max, d.t_max / kBlock,     \
+                     Wk, const_cast<float*>(summ), pg, d.n_kv_heads, d.t_max, d.t_max / kBlock, \
                      d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx, log_gate, score_lse)
   switch (decode_chunk_rows(d)) {
     case 8: SAS_SD_CHUNK(8); break;
@@ -331,8 +331,9 @@ template <typename T, int D, int DS, int G>
 static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq_lens,
                             const float* Wq, const float* summ, int32_t* idx, float* log_gate,
                             float* score_lse, float* scores, void* ws, hipStream_t st) {
-  sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, nullptr, nullptr, idx,
-                                               log_gate, score_lse, scores, ws, st);
+  sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, nullptr, nullptr,
+                                               KvPages{nullptr, 0}, idx, log_gate, score_lse,
+                                               scores, ws, st);
   if (s != SAS_OK) return s;
   return launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
 }
@@ -397,10 +398,10 @@ struct SelDecode {
 template <typename T, int D, int DS, int G>
 struct SelDecodeChunks {
   static sas_status run(const sas_dims& d, const void* q, const int32_t* seq_lens, const float* Wq,
-                        const float* summ, const void* K, const float* Wk, int32_t* idx,
-                        float* log_gate, float* score_lse, float* scores, void* ws,
+                        const float* summ, const void* K, const float* Wk, KvPages pg,
+                        int32_t* idx, float* log_gate, float* score_lse, float* scores, void* ws,
                         hipStream_t st) {
-    return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate,
+    return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate,
                                          score_lse, scores, ws, st);
   }
 };
@@ -453,9 +454,10 @@ sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t*
 
 sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                        const float* Wq, const float* summ, const void* K,
-                                       const float* Wk, int32_t* idx, float* log_gate,
-                                       float* score_lse, void* ws, hipStream_t st) {
-  return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, K, Wk, idx, log_gate, score_lse,
+                                       const float* Wk, KvPages pg, int32_t* idx,
+                                       float* log_gate, float* score_lse, void* ws,
+                                       hipStream_t st) {
+  return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate, score_lse,
                                   static_cast<float*>(nullptr), ws, st);
 }
 

@@ -105,6 +105,27 @@ def test_decode_step_validation(lib):
     assert step(_dims(head_dim=96), 1 << 40, wk=FAKE) == B.SAS_ERR_UNSUPPORTED
 
 
+def test_paged_validation(lib):
+    d = _dims()
+    need = B.sas_workspace_bytes(B.SAS_OP_DECODE_STEP, d)
+
+    def step(dims, max_pages, table=FAKE, summ=FAKE, ws_bytes=need):
+        return lib.sas_decode_step_paged(
+            ctypes.byref(dims), FAKE, FAKE, FAKE, table, max_pages, FAKE, FAKE, None, summ, 1,
+            0.1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+    assert step(d, 1024, ws_bytes=need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+    assert step(d, 1023) == B.SAS_ERR_INVALID_ARGUMENT    # 65536 tokens need 1024 pages
+    assert step(d, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert step(d, 1024, table=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert step(d, 1024, summ=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert step(_dims(head_dim=96), 1 << 20) == B.SAS_ERR_UNSUPPORTED
+    psum = lambda n, pages=FAKE: lib.sas_page_summaries(ctypes.byref(d), FAKE, pages, n, FAKE,
+                                                        FAKE, None)
+    assert psum(-1) == B.SAS_ERR_INVALID_ARGUMENT
+    assert psum(0, pages=None) == B.SAS_OK              # nothing to summarise
+    assert psum(3, pages=None) == B.SAS_ERR_INVALID_ARGUMENT
+
+
 def test_selector_bwd_validation(lib):
     d = _dims()
     need = B.sas_workspace_bytes(B.SAS_OP_SELECTOR_BWD, d, 16384)

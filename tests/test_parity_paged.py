@@ -1,0 +1,137 @@
+"""GPU parity of the paged-cache decode step (sas_page_summaries,
+sas_decode_step_paged) through the C ABI.
+
+Every sequence's blocks are scattered into a shuffled page pool (plus unused
+pages filled with large values, so a wrong page read shows), and the paged
+step must reproduce the contiguous sas_decode_step bit for bit: idx,
+log_gate, score_lse, o and lse, with and without the fused refresh of the
+newest block, whose page summary must come out with the bits of
+sas_block_summaries.  The contiguous step is itself checked against the CPU
+oracle in test_parity_decode.py; one case here also checks o against the
+oracle directly.  Covered: the batch-1 64K and batch-8 32K-64K workloads
+(both split paths), 512K (256-block selection chunks), fp32 and bf16, d and
+d_sel of 64 and 128, G = 1..8, ragged lengths, k = 0 and T = 1."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_amd import synth
+from oracle import sas_oracle as O
+from tests.gpu_util import TOL_OUT, dev, host, log, needs_gpu
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _sas():
+    from gated_block_sparse_amd import binding
+    return binding
+
+
+def paginate(K, V, seed, spare=5):
+    """Contiguous K/V [B,Hkv,t_max,d] -> page pools [n_pages,Hkv,64,d] and a
+    page table [B,n_blk] over a seeded permutation of the pages."""
+    B, Hkv, t_max, d = K.shape
+    n_blk = -(-t_max // 64)
+    pad = n_blk * 64 - t_max
+    n_pages = B * n_blk + spare
+    gen = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(n_pages, generator=gen)[:B * n_blk].view(B, n_blk).to(torch.int32)
+    pools = []
+    for X in (K, V):
+        Xp = torch.nn.functional.pad(X, (0, 0, 0, pad)) if pad else X
+        blocks = Xp.view(B, Hkv, n_blk, 64, d).permute(0, 2, 1, 3, 4).reshape(B * n_blk, Hkv, 64, d)
+        pool = torch.full((n_pages, Hkv, 64, d), 1e4, dtype=X.dtype, device=X.device)
+        pool[perm.view(-1).long().cuda()] = blocks
+        pools.append(pool)
+    return pools[0], pools[1], perm.cuda().contiguous()
+
+
+def run_paged_case(p, seed=0, label="", check_oracle=False):
+    S = _sas()
+    wl = p.wl
+    B, Hq, Hkv, d, k = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_k
+    t_max = p.K.shape[2]
+    log(f"[paged {label}] B={B} Hq={Hq} Hkv={Hkv} d={d} d_sel={wl.sel_dim} k={k} {wl.dtype} "
+        f"t_max={t_max} lens={p.seq_lens.tolist()[:8]}")
+    q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    lens = torch.from_numpy(p.seq_lens).cuda()
+    Wq, Wk = dev(p.Wq_sel), dev(p.Wk_sel)
+    summ = S.sas_block_summaries(K, lens, Wk)
+    Kp, Vp, table = paginate(K, V, seed)
+
+    # page summaries of every complete block, then compare with the contiguous ones
+    C = [O.n_history_blocks(int(T)) for T in p.seq_lens]
+    pages = torch.cat([table[b, :C[b]] for b in range(B)]) if sum(C) else \
+        torch.zeros(0, dtype=torch.int32, device="cuda")
+    summ_p = S.sas_page_summaries(Kp, pages.contiguous(), Wk)
+    for b in range(B):
+        if C[b]:
+            got = summ_p[table[b, :C[b]].long()]                 # [C, Hkv, ds]
+            assert torch.equal(got.permute(1, 0, 2), summ[b, :, :C[b]]), (label, b)
+
+    ref = S.sas_decode_step(q, K, V, lens, Wq, summ, k)
+    got = S.sas_decode_step_paged(q, Kp, Vp, table, lens, Wq, summ_p, k, t_max)
+    torch.cuda.synchronize()
+    for name, a, g in zip(("idx", "log_gate", "score_lse", "o", "lse"), ref, got):
+        assert torch.equal(a, g), (label, name)
+
+    # fused refresh: spoil every newest complete block's page summary first
+    summ_f = summ_p.clone()
+    for b in range(B):
+        if C[b]:
+            summ_f[table[b, C[b] - 1].long()] = 1e3
+    got = S.sas_decode_step_paged(q, Kp, Vp, table, lens, Wq, summ_f, k, t_max, Wk_sel=Wk)
+    torch.cuda.synchronize()
+    assert torch.equal(summ_f, summ_p), label
+    for name, a, g in zip(("idx", "log_gate", "score_lse", "o", "lse"), ref, got):
+        assert torch.equal(a, g), (label, "refresh", name)
+
+    if check_oracle:
+        # attention of the paged step against the oracle on the step's own selection
+        idx_h = got[0].cpu().numpy().astype(np.int64)
+        lg_h = host(got[1])
+        G = Hq // Hkv
+        scale = 1.0 / math.sqrt(d)
+        o_h = host(got[3])
+        for b in range(B):
+            T = int(p.seq_lens[b])
+            qb = synth.to_f64(p.q[b], wl.dtype)
+            for r in range(Hkv):
+                Kr = synth.to_f64(p.K[b, r:r + 1, :T], wl.dtype)
+                Vr = synth.to_f64(p.V[b, r:r + 1, :T], wl.dtype)
+                o_ref, _ = O.decode_attend(qb[r * G:(r + 1) * G], Kr, Vr, T, idx_h[b, r],
+                                           lg_h[b, r], scale, G, gated=True)
+                err = np.abs(o_h[b, r * G:(r + 1) * G] - o_ref).max()
+                assert err <= TOL_OUT[wl.dtype], (label, b, r, err)
+    return got
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b_decode_64k", "qwen3_4b_decode_b8_32k_64k",
+                                  "qwen3_4b_decode_512k"])
+def test_paged_workloads(name):
+    p = synth.make_problem(synth.WORKLOADS[name], seed=1)
+    run_paged_case(p, seed=3, label=name, check_oracle=(name == "qwen3_4b_decode_64k"))
+
+
+def _edge(T, k, dtype="f32", Hq=4, Hkv=2, d=64, ds=64, batch=1, lens=None, t_max=None, seed=0):
+    wl = synth.custom_workload("decode", batch=batch, n_q_heads=Hq, n_kv_heads=Hkv,
+                               head_dim=d, sel_dim=ds, top_k=k, dtype=dtype, seq_len=T)
+    return synth.make_problem(wl, seed, seq_lens=lens, t_max=t_max)
+
+
+@pytest.mark.parametrize("T,k,dtype,Hq,Hkv,d,ds", [
+    (1, 4, "f32", 4, 2, 64, 64), (65, 0, "f32", 4, 2, 64, 64), (4097, 16, "f32", 4, 1, 64, 64),
+    (3000, 7, "bf16", 32, 8, 128, 128), (2049, 5, "bf16", 8, 8, 64, 128),
+    (5000, 9, "bf16", 16, 2, 128, 64),
+])
+def test_paged_edges(T, k, dtype, Hq, Hkv, d, ds):
+    run_paged_case(_edge(T, k, dtype, Hq, Hkv, d, ds, seed=T), seed=T, label=f"T={T} k={k}",
+                   check_oracle=(T == 4097))
+
+
+def test_paged_varlen_ragged_tmax():
+    lens = [1, 65, 700, 128, 699, 64]
+    p = _edge(700, 5, "bf16", 8, 2, 128, 128, batch=6, lens=lens, t_max=700)
+    run_paged_case(p, seed=11, label="varlen", check_oracle=True)
