@@ -216,6 +216,38 @@ def run_decode(args, wl):
         if st:
             raise S.SasError(st, lib.sas_last_error().decode())
 
+    # the same step on a paged cache: every block in its own page of a
+    # shuffled pool (sas_block_summaries_paged, sas_decode_step_paged)
+    n_blk = -(-t_max // 64)
+    n_pages = B * n_blk
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(0)).view(B, n_blk)
+    table = perm.to(torch.int32).to(dev).contiguous()
+    pools = []
+    for X in (K, V):
+        pad = n_blk * 64 - t_max
+        Xp = torch.nn.functional.pad(X, (0, 0, 0, pad)) if pad else X
+        pool = torch.empty((n_pages, Hkv, 64, d), dtype=X.dtype, device=dev)
+        pool[perm.view(-1).to(dev)] = Xp.view(B, Hkv, n_blk, 64, d).permute(0, 2, 1, 3, 4).reshape(
+            n_pages, Hkv, 64, d)
+        pools.append(pool)
+    Kp, Vp = pools
+    summ_p = S.sas_block_summaries_paged(Kp, table, lens, Wk, t_max)
+    idx3, lg3, slse3 = torch.empty_like(idx), torch.empty_like(lg), torch.empty_like(slse)
+    o3, lse3 = torch.empty_like(o), torch.empty_like(lse)
+    a_paged = (pd, q.data_ptr(), Kp.data_ptr(), Vp.data_ptr(), table.data_ptr(), n_blk,
+               lens.data_ptr(), Wq.data_ptr(), Wk.data_ptr(), summ_p.data_ptr(), 1, scale,
+               idx3.data_ptr(), lg3.data_ptr(), slse3.data_ptr(), o3.data_ptr(), lse3.data_ptr(),
+               ws_step.data_ptr(), ws_step.numel(), sp)
+
+    def step_paged(evs=None):
+        if evs:
+            evs[0].record(stream)
+        st = lib.sas_decode_step_paged(*a_paged)
+        if evs:
+            evs[1].record(stream)
+        if st:
+            raise S.SasError(st, lib.sas_last_error().decode())
+
     def step(evs=None):
         """The same step through the separate entry points (per-op timing)."""
         if evs:
@@ -236,9 +268,12 @@ def run_decode(args, wl):
     for _ in range(args.warmup):
         step()
         step_fused()
+        step_paged()
     torch.cuda.synchronize()
     if not (torch.equal(o, o2) and torch.equal(idx, idx2) and torch.equal(lse, lse2)):
         raise RuntimeError("fused decode step differs from select + decode_fwd")
+    if not (torch.equal(o, o3) and torch.equal(idx, idx3) and torch.equal(lse, lse3)):
+        raise RuntimeError("paged decode step differs from the contiguous one")
 
     K_steps = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
@@ -263,6 +298,13 @@ def run_decode(args, wl):
         step_fused(evf[i])
     torch.cuda.synchronize()
     tot_f = [e[0].elapsed_time(e[1]) * 1e3 for e in evf]
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K_steps)]
+    for i in range(K_steps):
+        if not args.no_flush:
+            flush(i)
+        step_paged(evp[i])
+    torch.cuda.synchronize()
+    tot_p = [e[0].elapsed_time(e[1]) * 1e3 for e in evp]
 
     # hot-cache figures: the same steps with no eviction in between
     evh = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K_steps)]
@@ -335,6 +377,7 @@ def run_decode(args, wl):
             "decode_attention": {"median": round(us_dec, 3), "p10": round(_pct(t_dec, .1), 3), "p90": round(_pct(t_dec, .9), 3)},
             "step": {"median": round(us_step, 3), "p10": round(_pct(tot_f, .1), 3), "p90": round(_pct(tot_f, .9), 3)},
             "step_unfused": {"median": round(med(tot), 3), "p10": round(_pct(tot, .1), 3), "p90": round(_pct(tot, .9), 3)},
+            "step_paged_cache": {"median": round(med(tot_p), 3), "p10": round(_pct(tot_p, .1), 3), "p90": round(_pct(tot_p, .9), 3)},
             "step_hot": round(hot_step, 3),
             "step_unfused_hot": round(hot_step_unfused, 3),
             "decode_attention_hot": round(hot_dec, 3),

@@ -8,7 +8,7 @@ raises if the library has not been built.
 
 _BINDING_NAMES = (
     "sas_block_summaries", "sas_select", "sas_decode_fwd", "sas_decode_step",
-    "sas_decode_step_paged", "sas_page_summaries", "sas_prefill_fwd", "sas_bwd",
+    "sas_decode_step_paged", "sas_block_summaries_paged", "sas_prefill_fwd", "sas_bwd",
     "sas_selector_bwd", "sas_workspace_bytes", "SasError",
 )
 

@@ -46,7 +46,7 @@ _SIGNATURES = {
     "sas_decode_fwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
     "sas_decode_step": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _vp, _vp,
                                _vp, _vp, _vp, _sz, _vp]),
-    "sas_page_summaries": (_i32, [_PD, _vp, _vp, _i32, _vp, _vp, _vp]),
+    "sas_block_summaries_paged": (_i32, [_PD, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp]),
     "sas_decode_step_paged": (_i32, [_PD, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
                                      _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sas_prefill_fwd": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
@@ -240,31 +240,35 @@ def sas_decode_step(q, K, V, seq_lens, Wq_sel, summ, top_k, gated=True, scale=No
     return idx, log_gate, score_lse, o, lse
 
 
-def sas_page_summaries(K_pages, pages, Wk_sel, summ_pages=None):
-    """Summaries of the listed pages of a paged cache.  K_pages
-    [n_pages,Hkv,64,d]; pages int32 [n]; summ_pages fp32 [n_pages,Hkv,d_sel]
-    (allocated if None; rows of unlisted pages are left as they are)."""
-    n_pages, Hkv, _, d = K_pages.shape
+def sas_block_summaries_paged(K_pages, page_table, seq_lens, Wk_sel, t_max, blk_begin=0,
+                              blk_end=None, summ=None):
+    """sas_block_summaries on a paged cache: K_pages [n_pages,Hkv,64,d];
+    page_table int32 [B,max_pages]; summaries [B,Hkv,t_max//64,d_sel]
+    (logical blocks, allocated if None)."""
+    _, Hkv, _, d = K_pages.shape
+    B, max_pages = page_table.shape
     ds = Wk_sel.shape[0]
-    if summ_pages is None:
-        summ_pages = torch.zeros(n_pages, Hkv, ds, dtype=torch.float32, device=K_pages.device)
-    dims = make_dims(1, Hkv, Hkv, d, ds, 0, 64, _dtype_code(K_pages))
-    _check(load_library().sas_page_summaries(ctypes.byref(dims), _ptr(K_pages), _ptr(pages),
-                                             int(pages.numel()), _ptr(Wk_sel), _ptr(summ_pages),
-                                             _stream()))
-    return summ_pages
+    c_max = t_max // BLOCK
+    if summ is None:
+        summ = torch.zeros(B, Hkv, c_max, ds, dtype=torch.float32, device=K_pages.device)
+    blk_end = c_max if blk_end is None else blk_end
+    dims = make_dims(B, Hkv, Hkv, d, ds, 0, t_max, _dtype_code(K_pages))
+    _check(load_library().sas_block_summaries_paged(
+        ctypes.byref(dims), _ptr(K_pages), _ptr(page_table), int(max_pages), _ptr(seq_lens),
+        _ptr(Wk_sel), int(blk_begin), int(blk_end), _ptr(summ), _stream()))
+    return summ
 
 
-def sas_decode_step_paged(q, K_pages, V_pages, page_table, seq_lens, Wq_sel, summ_pages, top_k,
+def sas_decode_step_paged(q, K_pages, V_pages, page_table, seq_lens, Wq_sel, summ, top_k,
                           t_max, Wk_sel=None, gated=True, scale=None, idx=None, log_gate=None,
                           score_lse=None, o=None, lse=None, ws=None):
     """sas_decode_step on a paged cache: q [B,Hq,d]; K_pages/V_pages
-    [n_pages,Hkv,64,d]; page_table int32 [B,max_pages]; summ_pages fp32
-    [n_pages,Hkv,d_sel]; t_max = logical capacity per sequence.
-    Returns (idx, log_gate, score_lse, o, lse)."""
+    [n_pages,Hkv,64,d]; page_table int32 [B,max_pages]; summ fp32
+    [B,Hkv,t_max//64,d_sel] (logical blocks); t_max = logical capacity per
+    sequence.  Returns (idx, log_gate, score_lse, o, lse)."""
     B, Hq, d = q.shape
     _, Hkv, _, _ = K_pages.shape
-    ds = summ_pages.shape[-1]
+    ds = summ.shape[-1]
     max_pages = page_table.shape[1]
     dims = make_dims(B, Hq, Hkv, d, ds, top_k, t_max, _dtype_code(q))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -282,7 +286,7 @@ def sas_decode_step_paged(q, K_pages, V_pages, page_table, seq_lens, Wq_sel, sum
     ws, ws_bytes = _workspace(SAS_OP_DECODE_STEP, dims, 0, ws, dev)
     _check(load_library().sas_decode_step_paged(
         ctypes.byref(dims), _ptr(q), _ptr(K_pages), _ptr(V_pages), _ptr(page_table),
-        int(max_pages), _ptr(seq_lens), _ptr(Wq_sel), _ptr(Wk_sel), _ptr(summ_pages), int(gated),
+        int(max_pages), _ptr(seq_lens), _ptr(Wq_sel), _ptr(Wk_sel), _ptr(summ), int(gated),
         scale, _ptr(idx), _ptr(log_gate), _ptr(score_lse), _ptr(o), _ptr(lse), _ptr(ws),
         ws_bytes, _stream()))
     return idx, log_gate, score_lse, o, lse

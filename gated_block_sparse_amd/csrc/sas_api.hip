@@ -183,23 +183,34 @@ sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, c
                             log_gate, score_lse, o, lse, ws, static_cast<hipStream_t>(stream));
 }
 
-sas_status sas_page_summaries(const sas_dims* dims, const void* K_pages, const int32_t* pages,
-                              int32_t n, const float* Wk_sel, float* summ_pages, void* stream) {
+sas_status sas_block_summaries_paged(const sas_dims* dims, const void* K_pages,
+                                     const int32_t* page_table, int32_t max_pages,
+                                     const int32_t* seq_lens, const float* Wk_sel,
+                                     int32_t blk_begin, int32_t blk_end, float* summ,
+                                     void* stream) {
   SAS_TRY(check_dims(dims, false));
-  if (n < 0) return fail(SAS_ERR_INVALID_ARGUMENT, "page count %d is negative", n);
-  if (n == 0) return SAS_OK;
+  if (max_pages < 1 || static_cast<long>(dims->t_max) > static_cast<long>(max_pages) * kBlock)
+    return fail(SAS_ERR_INVALID_ARGUMENT, "t_max=%d needs at least %d page-table entries per "
+                "sequence, got %d", dims->t_max, cdiv(dims->t_max, kBlock), max_pages);
+  if (blk_begin < 0 || blk_end < blk_begin)
+    return fail(SAS_ERR_INVALID_ARGUMENT, "block range [%d, %d) is invalid", blk_begin, blk_end);
+  const int c_max = dims->t_max / kBlock;
+  if (blk_end > c_max) blk_end = c_max;
+  if (blk_begin >= blk_end) return SAS_OK;
   SAS_NONNULL(K_pages);
-  SAS_NONNULL(pages);
+  SAS_NONNULL(page_table);
+  SAS_NONNULL(seq_lens);
   SAS_NONNULL(Wk_sel);
-  SAS_NONNULL(summ_pages);
-  return launch_page_summaries(*dims, K_pages, pages, n, Wk_sel, summ_pages,
-                               static_cast<hipStream_t>(stream));
+  SAS_NONNULL(summ);
+  return launch_block_summaries_paged(*dims, K_pages, KvPages{page_table, max_pages}, seq_lens,
+                                      Wk_sel, blk_begin, blk_end, summ,
+                                      static_cast<hipStream_t>(stream));
 }
 
 sas_status sas_decode_step_paged(const sas_dims* dims, const void* q, const void* K_pages,
                                  const void* V_pages, const int32_t* page_table,
                                  int32_t max_pages, const int32_t* seq_lens,
-                                 const float* Wq_sel, const float* Wk_sel, float* summ_pages,
+                                 const float* Wq_sel, const float* Wk_sel, float* summ,
                                  int32_t gated, float scale, int32_t* idx, float* log_gate,
                                  float* score_lse, void* o, float* lse, void* ws,
                                  size_t ws_bytes, void* stream) {
@@ -213,7 +224,7 @@ sas_status sas_decode_step_paged(const sas_dims* dims, const void* q, const void
   SAS_NONNULL(page_table);
   SAS_NONNULL(seq_lens);
   SAS_NONNULL(Wq_sel);
-  SAS_NONNULL(summ_pages);
+  if (dims->t_max >= kBlock) SAS_NONNULL(summ);
   if (dims->top_k > 0) {
     SAS_NONNULL(idx);
     SAS_NONNULL(log_gate);
@@ -223,7 +234,7 @@ sas_status sas_decode_step_paged(const sas_dims* dims, const void* q, const void
   if (!(scale > 0.0f))
     return fail(SAS_ERR_INVALID_ARGUMENT, "scale must be a positive number");
   SAS_TRY(check_ws(decode_step_ws_bytes(*dims), ws, ws_bytes));
-  return launch_decode_step(*dims, q, K_pages, V_pages, seq_lens, Wq_sel, summ_pages, Wk_sel,
+  return launch_decode_step(*dims, q, K_pages, V_pages, seq_lens, Wq_sel, summ, Wk_sel,
                             KvPages{page_table, max_pages}, gated != 0, scale, idx, log_gate,
                             score_lse, o, lse, ws, static_cast<hipStream_t>(stream));
 }

@@ -24,10 +24,10 @@ sas_status check_launch(const char* what);
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------ K/V cache layout ---
-// Contiguous (table == nullptr): K/V [B,Hkv,t_max,d], summaries
-// [B,Hkv,t_max/64,d_sel].  Paged: logical block m of sequence b lives in page
-// table[b * max_pages + m] of a pool K/V [n_pages,Hkv,64,d], and its summary
-// in row (page, r) of [n_pages,Hkv,d_sel].
+// Contiguous (table == nullptr): K/V [B,Hkv,t_max,d].  Paged: logical block
+// m of sequence b lives in page table[b * max_pages + m] of a pool K/V
+// [n_pages,Hkv,64,d].  Block summaries are [B,Hkv,t_max/64,d_sel] by logical
+// block in both layouts (a selection reads them without a table lookup).
 struct KvPages {
   const int32_t* table;
   int max_pages;
@@ -39,13 +39,6 @@ __device__ __forceinline__ size_t kv_block_row(const KvPages& pg, int b, int r, 
     return (static_cast<size_t>(pg.table[static_cast<size_t>(b) * pg.max_pages + m]) * Hkv + r) *
            kBlock;
   return (static_cast<size_t>(b) * Hkv + r) * t_max + static_cast<size_t>(m) * kBlock;
-}
-// Summary row of block m of (b, r).
-__device__ __forceinline__ size_t summ_row(const KvPages& pg, int b, int r, int m, int Hkv,
-                                           int c_max) {
-  if (pg.table)
-    return static_cast<size_t>(pg.table[static_cast<size_t>(b) * pg.max_pages + m]) * Hkv + r;
-  return (static_cast<size_t>(b) * Hkv + r) * c_max + m;
 }
 
 // ---------------------------------------------------------------- bf16 ---
@@ -66,8 +59,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
                                   const float* Wk, int blk_begin, int blk_end, float* summ,
                                   hipStream_t st);
-sas_status launch_page_summaries(const sas_dims& d, const void* K, const int32_t* pages, int n,
-                                 const float* Wk, float* summ, hipStream_t st);
+// The same on a paged cache (pg.table non-null); summ stays logical.
+sas_status launch_block_summaries_paged(const sas_dims& d, const void* K, KvPages pg,
+                                        const int32_t* seq_lens, const float* Wk, int blk_begin,
+                                        int blk_end, float* summ, hipStream_t st);
 
 size_t select_decode_ws_bytes(const sas_dims& d);
 sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t* seq_lens,

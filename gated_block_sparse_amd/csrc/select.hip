@@ -104,7 +104,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < PL; ++e) xs[j][e] = 0.f;
     if (i < n) {
-      const float* sp = summ + summ_row(pg, b, r, m0 + i, Hkv, c_max) * DS + l32 * PL;
+      const float* sp = summ + ((row * c_max) + m0 + i) * static_cast<size_t>(DS) + l32 * PL;
       if constexpr (PL == 4) {
         const float4 x = *reinterpret_cast<const float4*>(sp);
         xs[j][0] = x.x; xs[j][1] = x.y; xs[j][2] = x.z; xs[j][3] = x.w;
@@ -130,7 +130,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
     if (tid % WkSlice<D, DS>::SPLIT == 0) {
       const int jo = tid / WkSlice<D, DS>::SPLIT;
       rsumm[jo] = a;
-      summ_out[summ_row(pg, b, r, mnew, Hkv, c_max) * DS + jo] = a;
+      summ_out[(row * c_max + mnew) * static_cast<size_t>(DS) + jo] = a;
     }
     __syncthreads();
     const int i = mnew - m0;

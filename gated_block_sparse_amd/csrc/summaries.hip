@@ -23,7 +23,7 @@ template <typename T, int D, int DS>
 __global__ void __launch_bounds__(kSumThreads)
 block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_lens,
                        const float* __restrict__ Wk, int blk_begin, int blk_end, int Hkv,
-                       int t_max, int c_max, float* __restrict__ summ) {
+                       int t_max, int c_max, KvPages pg, float* __restrict__ summ) {
   using WS = WkSlice<D, DS>;
   __shared__ float mean[kSumBlocks][D];
 
@@ -39,10 +39,9 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   WS ws;
   ws.load(Wk, tid);
 
-  const T* Kr = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   for (int jb = wave; jb < nblk; jb += 4) {
     BlockMean<T, D> bm;
-    bm.load(Kr + static_cast<size_t>(first + jb) * kBlock * D, lane);
+    bm.load(K + kv_block_row(pg, b, r, first + jb, Hkv, t_max) * D, lane);
     bm.reduce(lane, mean[jb]);
   }
   __syncthreads();
@@ -55,84 +54,22 @@ block_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ seq_
   }
 }
 
-// Summaries of listed pages of a paged cache (K [n_pages,Hkv,64,d] ->
-// summ [n_pages,Hkv,d_sel]), each page a complete block: the same arithmetic
-// as block_summaries_kernel (one wave reduces a block, then the same
-// projection), so a page's summary has the bits of its block's.
-template <typename T, int D, int DS>
-__global__ void __launch_bounds__(kSumThreads)
-page_summaries_kernel(const T* __restrict__ K, const int32_t* __restrict__ pages, int n, int Hkv,
-                      const float* __restrict__ Wk, float* __restrict__ summ) {
-  using WS = WkSlice<D, DS>;
-  __shared__ float mean[kSumBlocks][D];
-  const int r = blockIdx.y;
-  const int first = blockIdx.x * kSumBlocks;
-  const int nblk = min(kSumBlocks, n - first);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  WS ws;
-  ws.load(Wk, tid);
-  for (int jb = wave; jb < nblk; jb += 4) {
-    const size_t pg = static_cast<size_t>(pages[first + jb]);
-    BlockMean<T, D> bm;
-    bm.load(K + (pg * Hkv + r) * kBlock * D, lane);
-    bm.reduce(lane, mean[jb]);
-  }
-  __syncthreads();
-  const int j = tid / WS::SPLIT, part = tid % WS::SPLIT;
-  for (int jb = 0; jb < nblk; ++jb) {
-    const float a = ws.project(mean[jb], tid);
-    if (part == 0) summ[(static_cast<size_t>(pages[first + jb]) * Hkv + r) * DS + j] = a;
-  }
-}
-
-template <typename T, int D, int DS>
-static void launch_page_sum(const sas_dims& d, const void* K, const int32_t* pages, int n,
-                            const float* Wk, float* summ, hipStream_t st) {
-  hipLaunchKernelGGL((page_summaries_kernel<T, D, DS>), dim3(cdiv(n, kSumBlocks), d.n_kv_heads),
-                     dim3(kSumThreads), 0, st, static_cast<const T*>(K), pages, n, d.n_kv_heads,
-                     Wk, summ);
-}
-
-sas_status launch_page_summaries(const sas_dims& d, const void* K, const int32_t* pages, int n,
-                                 const float* Wk, float* summ, hipStream_t st) {
-  if (n <= 0) return SAS_OK;
-  const bool bf = d.dtype == SAS_BF16;
-#define SAS_PSUM_CASE(TT, DD, SS)                                                     \
-  if (d.head_dim == DD && d.sel_dim == SS) {                                          \
-    launch_page_sum<TT, DD, SS>(d, K, pages, n, Wk, summ, st);                        \
-    return check_launch("page_summaries");                                            \
-  }
-  if (bf) {
-    SAS_PSUM_CASE(uint16_t, 64, 64)
-    SAS_PSUM_CASE(uint16_t, 64, 128)
-    SAS_PSUM_CASE(uint16_t, 128, 64)
-    SAS_PSUM_CASE(uint16_t, 128, 128)
-  } else {
-    SAS_PSUM_CASE(float, 64, 64)
-    SAS_PSUM_CASE(float, 64, 128)
-    SAS_PSUM_CASE(float, 128, 64)
-    SAS_PSUM_CASE(float, 128, 128)
-  }
-#undef SAS_PSUM_CASE
-  return fail(SAS_ERR_UNSUPPORTED, "page_summaries: d=%d d_sel=%d", d.head_dim, d.sel_dim);
-}
-
 template <typename T, int D, int DS>
 static void launch_sum(const sas_dims& d, const void* K, const int32_t* seq_lens, const float* Wk,
-                       int blk_begin, int blk_end, float* summ, hipStream_t st) {
+                       int blk_begin, int blk_end, float* summ, hipStream_t st, KvPages pg) {
   dim3 grid(cdiv(blk_end - blk_begin, kSumBlocks), d.n_kv_heads, d.batch);
   hipLaunchKernelGGL((block_summaries_kernel<T, D, DS>), grid, dim3(kSumThreads), 0, st,
                      static_cast<const T*>(K), seq_lens, Wk, blk_begin, blk_end, d.n_kv_heads,
-                     d.t_max, d.t_max / kBlock, summ);
+                     d.t_max, d.t_max / kBlock, pg, summ);
 }
 
-sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
-                                  const float* Wk, int blk_begin, int blk_end, float* summ,
-                                  hipStream_t st) {
+static sas_status sum_any(const sas_dims& d, const void* K, KvPages pg, const int32_t* seq_lens,
+                          const float* Wk, int blk_begin, int blk_end, float* summ,
+                          hipStream_t st) {
   const bool bf = d.dtype == SAS_BF16;
 #define SAS_SUM_CASE(TT, DD, SS)                                                      \
   if (d.head_dim == DD && d.sel_dim == SS) {                                          \
-    launch_sum<TT, DD, SS>(d, K, seq_lens, Wk, blk_begin, blk_end, summ, st);         \
+    launch_sum<TT, DD, SS>(d, K, seq_lens, Wk, blk_begin, blk_end, summ, st, pg);     \
     return check_launch("block_summaries");                                           \
   }
   if (bf) {
@@ -148,6 +85,18 @@ sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_
   }
 #undef SAS_SUM_CASE
   return fail(SAS_ERR_UNSUPPORTED, "block_summaries: d=%d d_sel=%d", d.head_dim, d.sel_dim);
+}
+
+sas_status launch_block_summaries(const sas_dims& d, const void* K, const int32_t* seq_lens,
+                                  const float* Wk, int blk_begin, int blk_end, float* summ,
+                                  hipStream_t st) {
+  return sum_any(d, K, KvPages{nullptr, 0}, seq_lens, Wk, blk_begin, blk_end, summ, st);
+}
+
+sas_status launch_block_summaries_paged(const sas_dims& d, const void* K, KvPages pg,
+                                        const int32_t* seq_lens, const float* Wk, int blk_begin,
+                                        int blk_end, float* summ, hipStream_t st) {
+  return sum_any(d, K, pg, seq_lens, Wk, blk_begin, blk_end, summ, st);
 }
 
 }  // namespace sas

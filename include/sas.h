@@ -169,30 +169,33 @@ sas_status sas_decode_step(const sas_dims* dims, const void* q, const void* K, c
 
 /* Paged K/V cache (SAS close reading 2.4, closing paragraph on serving: the
  * served system keeps K/V in a paged cache).  A page is one 64-token block of
- * every KV head of one sequence: K_pages/V_pages dtype [n_pages,Hkv,64,d];
- * summ_pages fp32 [n_pages,Hkv,d_sel] holds each page's block summary.
+ * every KV head of one sequence: K_pages/V_pages dtype [n_pages,Hkv,64,d].
  * page_table int32 [B,max_pages]: logical block m of sequence b (tokens
  * 64m..64m+63) is page page_table[b*max_pages+m]; entries m <= C_b =
  * (seq_lens[b]-1)/64 must name valid pages (the caller owns the pool and the
- * table; pages may be shared between sequences).
+ * table; pages may be shared between sequences).  dims->t_max is the logical
+ * capacity per sequence, at most 64*max_pages.  Summaries stay logical, fp32
+ * [B,Hkv,t_max/64,d_sel] as for a contiguous cache, so the selection reads
+ * them without a table lookup.
  *
- * sas_page_summaries: the summaries of the n pages listed in pages (int32,
- * each a complete block), with the bits sas_block_summaries gives the same
- * block in a contiguous cache.  n = 0 does nothing. */
-sas_status sas_page_summaries(const sas_dims* dims, const void* K_pages, const int32_t* pages,
-                              int32_t n, const float* Wk_sel, float* summ_pages, void* stream);
+ * sas_block_summaries_paged: sas_block_summaries on a paged cache (same
+ * block range rules, same bits for the same block contents). */
+sas_status sas_block_summaries_paged(const sas_dims* dims, const void* K_pages,
+                                     const int32_t* page_table, int32_t max_pages,
+                                     const int32_t* seq_lens, const float* Wk_sel,
+                                     int32_t blk_begin, int32_t blk_end, float* summ,
+                                     void* stream);
 
 /* sas_decode_step on a paged cache: the same computation and outputs, bit
  * for bit, as sas_decode_step on the contiguous cache holding the same
- * blocks (idx holds logical block numbers).  dims->t_max is the logical
- * capacity per sequence, at most 64*max_pages.  With Wk_sel, the summary of
- * each sequence's newest complete block is refreshed into its page's row of
- * summ_pages.  Invalid sizes or NULL required pointers return an error and
- * enqueue nothing.  ws: at least sas_workspace_bytes(SAS_OP_DECODE_STEP, dims, 0). */
+ * blocks (idx holds logical block numbers; with Wk_sel the newest complete
+ * block's summary is refreshed into summ first).  Invalid sizes or NULL
+ * required pointers return an error and enqueue nothing.
+ * ws: at least sas_workspace_bytes(SAS_OP_DECODE_STEP, dims, 0). */
 sas_status sas_decode_step_paged(const sas_dims* dims, const void* q, const void* K_pages,
                                  const void* V_pages, const int32_t* page_table,
                                  int32_t max_pages, const int32_t* seq_lens,
-                                 const float* Wq_sel, const float* Wk_sel, float* summ_pages,
+                                 const float* Wq_sel, const float* Wk_sel, float* summ,
                                  int32_t gated, float scale, int32_t* idx, float* log_gate,
                                  float* score_lse, void* o, float* lse, void* ws,
                                  size_t ws_bytes, void* stream);

@@ -119,11 +119,13 @@ def test_paged_validation(lib):
     assert step(d, 1024, table=None) == B.SAS_ERR_INVALID_ARGUMENT
     assert step(d, 1024, summ=None) == B.SAS_ERR_INVALID_ARGUMENT
     assert step(_dims(head_dim=96), 1 << 20) == B.SAS_ERR_UNSUPPORTED
-    psum = lambda n, pages=FAKE: lib.sas_page_summaries(ctypes.byref(d), FAKE, pages, n, FAKE,
-                                                        FAKE, None)
-    assert psum(-1) == B.SAS_ERR_INVALID_ARGUMENT
-    assert psum(0, pages=None) == B.SAS_OK              # nothing to summarise
-    assert psum(3, pages=None) == B.SAS_ERR_INVALID_ARGUMENT
+    psum = lambda b0, b1, table=FAKE, mp=1024: lib.sas_block_summaries_paged(
+        ctypes.byref(d), FAKE, table, mp, FAKE, FAKE, b0, b1, FAKE, None)
+    assert psum(-1, 4) == B.SAS_ERR_INVALID_ARGUMENT
+    assert psum(5, 4) == B.SAS_ERR_INVALID_ARGUMENT
+    assert psum(0, 4, mp=1000) == B.SAS_ERR_INVALID_ARGUMENT
+    assert psum(0, 4, table=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert psum(2000, 3000, table=None) == B.SAS_OK       # beyond t_max/64: nothing to do
 
 
 def test_selector_bwd_validation(lib):

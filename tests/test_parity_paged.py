@@ -1,14 +1,15 @@
-"""GPU parity of the paged-cache decode step (sas_page_summaries,
+"""GPU parity of the paged-cache decode step (sas_block_summaries_paged,
 sas_decode_step_paged) through the C ABI.
 
 Every sequence's blocks are scattered into a shuffled page pool (plus unused
-pages filled with large values, so a wrong page read shows), and the paged
-step must reproduce the contiguous sas_decode_step bit for bit: idx,
-log_gate, score_lse, o and lse, with and without the fused refresh of the
-newest block, whose page summary must come out with the bits of
-sas_block_summaries.  The contiguous step is itself checked against the CPU
-oracle in test_parity_decode.py; one case here also checks o against the
-oracle directly.  Covered: the batch-1 64K and batch-8 32K-64K workloads
+pages filled with large values, so a wrong page read shows).  The paged
+summaries must equal the contiguous ones bit for bit, and the paged step
+must reproduce the contiguous sas_decode_step bit for bit: idx, log_gate,
+score_lse, o and lse, with and without the fused refresh of the newest
+block, whose summary must come out with the bits of sas_block_summaries.
+The contiguous step is itself checked against the CPU oracle in
+test_parity_decode.py; three cases here also check o against the oracle
+directly.  Covered: the batch-1 64K and batch-8 32K-64K workloads
 (both split paths), 512K (256-block selection chunks), fp32 and bf16, d and
 d_sel of 64 and 128, G = 1..8, ragged lengths, k = 0 and T = 1."""
 import math
@@ -61,15 +62,11 @@ def run_paged_case(p, seed=0, label="", check_oracle=False):
     summ = S.sas_block_summaries(K, lens, Wk)
     Kp, Vp, table = paginate(K, V, seed)
 
-    # page summaries of every complete block, then compare with the contiguous ones
+    # summaries of every complete block from the pages, against the contiguous ones
     C = [O.n_history_blocks(int(T)) for T in p.seq_lens]
-    pages = torch.cat([table[b, :C[b]] for b in range(B)]) if sum(C) else \
-        torch.zeros(0, dtype=torch.int32, device="cuda")
-    summ_p = S.sas_page_summaries(Kp, pages.contiguous(), Wk)
+    summ_p = S.sas_block_summaries_paged(Kp, table, lens, Wk, t_max)
     for b in range(B):
-        if C[b]:
-            got = summ_p[table[b, :C[b]].long()]                 # [C, Hkv, ds]
-            assert torch.equal(got.permute(1, 0, 2), summ[b, :, :C[b]]), (label, b)
+        assert torch.equal(summ_p[b, :, :C[b]], summ[b, :, :C[b]]), (label, b)
 
     ref = S.sas_decode_step(q, K, V, lens, Wq, summ, k)
     got = S.sas_decode_step_paged(q, Kp, Vp, table, lens, Wq, summ_p, k, t_max)
@@ -77,11 +74,11 @@ def run_paged_case(p, seed=0, label="", check_oracle=False):
     for name, a, g in zip(("idx", "log_gate", "score_lse", "o", "lse"), ref, got):
         assert torch.equal(a, g), (label, name)
 
-    # fused refresh: spoil every newest complete block's page summary first
+    # fused refresh: spoil every newest complete block's summary first
     summ_f = summ_p.clone()
     for b in range(B):
         if C[b]:
-            summ_f[table[b, C[b] - 1].long()] = 1e3
+            summ_f[b, :, C[b] - 1] = 1e3
     got = S.sas_decode_step_paged(q, Kp, Vp, table, lens, Wq, summ_f, k, t_max, Wk_sel=Wk)
     torch.cuda.synchronize()
     assert torch.equal(summ_f, summ_p), label
