@@ -480,6 +480,32 @@ def run_prefill(args, wl):
     t_bwd = [e[2].elapsed_time(e[3]) * 1e3 for e in evs]
     t_sb = [e[3].elapsed_time(e[4]) * 1e3 for e in evs]
     tot = [e[0].elapsed_time(e[4]) * 1e3 for e in evs]
+
+    # the backward once more with a sink-heavy selection (every tile also
+    # selects blocks 0 and 1, which every tile then reads): the case the
+    # dK/dV pass splits hot blocks for
+    rng = np.random.default_rng(7)
+    sidx = idx.cpu().numpy().copy()
+    n_tiles = sidx.shape[2]
+    for r in range(Hkv):
+        for t in range(2, n_tiles):
+            row = [int(x) for x in sidx[0, r, t] if x >= 0]
+            keep = [x for x in row if x not in (0, 1)]
+            rng.shuffle(keep)
+            row = sorted([0, 1] + keep[:max(0, len(row) - 2)])
+            sidx[0, r, t, :len(row)] = row
+    sidx_d = torch.from_numpy(sidx).to(dev)
+    Os, lses = Sb.sas_prefill_fwd(Q, K, V, sidx_d, lg)
+    t_sink = []
+    for i in range(n):
+        if not args.no_flush:
+            flush(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        Sb.sas_bwd(Q, K, V, Os, dO, lses, sidx_d, lg, dQ=dQ, dK=dK, dV=dV, dlog_gate=dlg, ws=ws_bwd)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_sink.append(e0.elapsed_time(e1) * 1e3)
     med = statistics.median
     us_fwd, us_bwd, us_step = med(t_fwd), med(t_bwd), med(tot)
     fwd_tf = fwd_flop / (us_fwd * 1e-6) / 1e12
@@ -501,6 +527,7 @@ def run_prefill(args, wl):
             "prefill_fwd": {"median": round(us_fwd, 2), "p10": round(_pct(t_fwd, .1), 2), "p90": round(_pct(t_fwd, .9), 2)},
             "bwd": {"median": round(us_bwd, 2), "p10": round(_pct(t_bwd, .1), 2), "p90": round(_pct(t_bwd, .9), 2)},
             "selector_bwd": {"median": round(med(t_sb), 2), "p10": round(_pct(t_sb, .1), 2), "p90": round(_pct(t_sb, .9), 2)},
+            "bwd_sink_heavy_selection": {"median": round(med(t_sink), 2), "p10": round(_pct(t_sink, .1), 2), "p90": round(_pct(t_sink, .9), 2)},
         },
         "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
         "bwd_TFLOPs": round(bwd_tf, 1),

@@ -523,7 +523,8 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv,
                    int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
-                   const float* __restrict__ log_gate, float scale2, float scale,
+                   const float* __restrict__ log_gate, float scale2, float scale, int n_hot,
+                   int max_chunks, float* __restrict__ hot_part, int* __restrict__ hot_cnt,
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
   constexpr int D = 128, NWV = 4, KS = D / 32, CT = D / 16;
   __shared__ __attribute__((aligned(16))) unsigned char ring[kTsSlots * kTsSlot];
@@ -534,7 +535,21 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   __shared__ int s_count;
   __shared__ int s_wcount[NWV];
 
-  const int m = static_cast<int>(blockIdx.x) / Hkv, r = static_cast<int>(blockIdx.x) % Hkv;
+  // Grid: first the hot blocks m < n_hot, max_chunks workgroups each (block,
+  // then chunk, then group), then every other block with one workgroup.
+  int m, r, chunk;
+  {
+    const int x = static_cast<int>(blockIdx.x), hot = n_hot * max_chunks * Hkv;
+    if (x < hot) {
+      m = x / (max_chunks * Hkv);
+      chunk = (x / Hkv) % max_chunks;
+      r = x % Hkv;
+    } else {
+      m = n_hot + (x - hot) / Hkv;
+      chunk = 0;
+      r = (x - hot) % Hkv;
+    }
+  }
   const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, i4 = lane >> 4;
@@ -544,7 +559,20 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
                                         log_gate ? log_gate + grow * n_tiles * k : nullptr,
                                         list_t, list_slot, list_beta, &s_count, s_wcount);
-  const int n_steps = n_list * G * 2;
+  // Hot-block chunking: a hot block read by more than kHotCap tiles is split
+  // over ceil(n_list / kHotCap) workgroups, chunk c taking entries c, c + nc,
+  // c + 2nc, ... (interleaved, so the chunks sweep the tiles together and
+  // share them in the L2, as one workgroup's sweep would); each chunk leaves
+  // an fp32 partial of dK^T/dV^T that the reduction kernel sums in chunk
+  // order.  Other blocks (and hot blocks with few readers) are done by chunk
+  // 0 alone.
+  const bool split = m < n_hot && n_list > kHotCap;
+  const int n_chunks = split ? (n_list + kHotCap - 1) / kHotCap : 1;
+  const size_t hot_slot = (grow * n_hot + m) * static_cast<size_t>(max_chunks) + chunk;
+  if (m < n_hot && chunk == 0 && tid == 0) hot_cnt[grow * n_hot + m] = split ? n_chunks : 0;
+  if (chunk >= n_chunks) return;   // workgroup-uniform: no barrier follows for anyone
+  const int n_mine = (n_list - chunk + n_chunks - 1) / n_chunks;   // entries chunk + j nc
+  const int n_steps = n_mine * G * 2;
   const uint32_t ring_lds = lds_addr_of(ring);
 
   // ---- LDS DMA of step s2 into slot s2 % kTsSlots.  Every wave copies rows
@@ -555,7 +583,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // the sequence end repeat its last row (finite values; masked below).
   auto issue = [&](int s2) {
     const int sc = min(s2, n_steps - 1);
-    const int qt2 = sc & 1, g2 = (sc >> 1) % G, e2 = (sc >> 1) / G;
+    const int qt2 = sc & 1, g2 = (sc >> 1) % G, e2 = chunk + ((sc >> 1) / G) * n_chunks;
     const int qbase = 64 * list_t[e2] + 32 * qt2;
     const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g2) * S;
     const uint32_t slot = ring_lds + (s2 % kTsSlots) * kTsSlot;
@@ -612,7 +640,8 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int tr_x = ft >> 1;
 
   float dsum = 0.f;
-  int pending = -1;   // entry whose per-wave dlog_gate partials sit in red[]
+  int pending = -1;   // entry whose per-wave dlog_gate partials sit in red[pslot]
+  int pslot = 0;
   for (int s = 0; s < n_steps; ++s) {
     // this wave's copies for step s are done once at most the copies of
     // kTsSlots - 2 later steps remain; the barrier makes every wave's copies
@@ -623,12 +652,13 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (pending >= 1 && tid == 0) {
       float tot = 0.f;
 #pragma unroll
-      for (int w = 0; w < NWV; ++w) tot += red[pending & 1][w];
+      for (int w = 0; w < NWV; ++w) tot += red[pslot][w];
       dlg[(grow * n_tiles + list_t[pending]) * k + list_slot[pending]] = tot;
     }
     if (pending >= 0) pending = -1;
 
-    const int qt = s & 1, g = (s >> 1) % G, e = (s >> 1) / G;
+    const int jl = (s >> 1) / G;   // the chunk's local entry number
+    const int qt = s & 1, g = (s >> 1) % G, e = chunk + jl * n_chunks;
     const bool diag = e == 0;
     const float beta2 = list_beta[e];
     const int nq = min(64, S - 64 * list_t[e]);
@@ -692,20 +722,29 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // last step of the entry: the wave's dlog_gate partial
     if (qt == 1 && g == G - 1) {
       const float w = wave_sum_from(dsum, 1);
-      if (lane == 0) red[e & 1][wave] = w;
+      if (lane == 0) red[jl & 1][wave] = w;
       dsum = 0.f;
       pending = e;
+      pslot = jl & 1;
     }
   }
   dma_sync<0>();
   if (pending >= 1 && tid == 0) {
     float tot = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) tot += red[pending & 1][w];
+    for (int w = 0; w < NWV; ++w) tot += red[pslot][w];
     dlg[(grow * n_tiles + list_t[pending]) * k + list_slot[pending]] = tot;
   }
   // ---- store: lane holds channels 16 ct + 4 i4 + v of token tok
-  if (tok_ok) {
+  if (split) {   // fp32 partial, dK^T unscaled: [dK | dV][64 tokens][D]
+    float* dst = hot_part + hot_slot * (2 * 64 * D) + tok * D + 4 * i4;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      *reinterpret_cast<float4*>(dst + 16 * ct) = make_float4(dk[ct][0], dk[ct][1], dk[ct][2], dk[ct][3]);
+      *reinterpret_cast<float4*>(dst + 64 * D + 16 * ct) =
+          make_float4(dv[ct][0], dv[ct][1], dv[ct][2], dv[ct][3]);
+    }
+  } else if (tok_ok) {
     const size_t orow = (grow * t_max + tok0 + tok) * D + 4 * i4;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -720,9 +759,55 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 }
 
+// Sum of the chunk partials of the split hot blocks, in chunk order (one
+// workgroup per (hot block, group, sequence); blocks that were not split
+// have a count of 0 and were stored by their single workgroup).
+__global__ void __launch_bounds__(256)
+bwd_hot_reduce_kernel(const float* __restrict__ hot_part, const int* __restrict__ hot_cnt,
+                      int S, int Hkv, int t_max, int n_hot, int max_chunks, float scale,
+                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV) {
+  constexpr int D = 128;
+  const int m = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const size_t grow = static_cast<size_t>(b) * Hkv + r;
+  const int nc = hot_cnt[grow * n_hot + m];
+  if (nc == 0) return;
+  const float* base = hot_part + (grow * n_hot + m) * static_cast<size_t>(max_chunks) * (2 * 64 * D);
+  for (int i = threadIdx.x; i < 2 * 64 * D / 4; i += 256) {
+    const int which = i / (64 * D / 4), rem = i % (64 * D / 4);
+    const int tok = rem / (D / 4), c4 = (rem % (D / 4)) * 4;
+    if (64 * m + tok >= S) continue;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < nc; ++c) {
+      const float4 x = *reinterpret_cast<const float4*>(base + static_cast<size_t>(c) * (2 * 64 * D) + 4 * static_cast<size_t>(i));
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+    }
+    const float mul = which ? 1.f : scale;
+    uint2 pk;
+    pk.x = bf16_rne(a.x * mul) | (bf16_rne(a.y * mul) << 16);
+    pk.y = bf16_rne(a.z * mul) | (bf16_rne(a.w * mul) << 16);
+    uint16_t* dst = which ? dV : dK;
+    *reinterpret_cast<uint2*>(dst + (grow * t_max + 64 * m + tok) * D + c4) = pk;
+  }
+}
+
 // ------------------------------------------------------------ launcher ---
+// dK/dV hot-block chunking (d = 128): blocks m < n_hot may be split into up
+// to max_chunks workgroups; their fp32 partials and chunk counts follow D.
+static int hot_blocks(int n_tiles) { return n_tiles < kHotBlocks ? n_tiles : kHotBlocks; }
+static int hot_max_chunks(int n_tiles) { return cdiv(n_tiles, kHotCap); }
+static size_t hot_part_floats(const sas_dims& d, int n_tiles) {
+  return static_cast<size_t>(d.batch) * d.n_kv_heads * hot_blocks(n_tiles) *
+         hot_max_chunks(n_tiles) * (2 * 64 * 128);
+}
+static size_t align_up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// workspace: D [B,Hq,S] fp32 | (d = 128) hot partials | hot chunk counts
 size_t bwd_ws_bytes(const sas_dims& d, int seq_len) {
-  return static_cast<size_t>(d.batch) * d.n_q_heads * seq_len * sizeof(float);
+  const size_t dq = static_cast<size_t>(d.batch) * d.n_q_heads * seq_len * sizeof(float);
+  if (d.head_dim != 128) return dq;
+  const int n_tiles = cdiv(seq_len, kBlock);
+  return align_up256(dq) + align_up256(hot_part_floats(d, n_tiles) * sizeof(float)) +
+         static_cast<size_t>(d.batch) * d.n_kv_heads * hot_blocks(n_tiles) * sizeof(int);
 }
 
 template <int D>
@@ -761,11 +846,16 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   s = check_launch("bwd_dq");
   if (s != SAS_OK) return s;
   if constexpr (D == 128) {
+    const int n_hot = hot_blocks(n_tiles), max_chunks = hot_max_chunks(n_tiles);
+    char* wsb = static_cast<char*>(ws) + align_up256(n_rows * sizeof(float));
+    float* hot_part = reinterpret_cast<float*>(wsb);
+    int* hot_cnt = reinterpret_cast<int*>(wsb + align_up256(hot_part_floats(d, n_tiles) * sizeof(float)));
+    const int grid_x = (n_hot * max_chunks + (n_tiles - n_hot)) * d.n_kv_heads;
 #define SAS_DKDV_TS(GG)                                                                          \
-  hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),          \
-                     dim3(256), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, \
-                     d.top_k, idx, log_gate, scale2, scale, static_cast<uint16_t*>(dK),          \
-                     static_cast<uint16_t*>(dV), dlg)
+  hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG>), dim3(grid_x, 1, d.batch), dim3(256), 0, st, q, kk,  \
+                     v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, d.top_k, idx, log_gate,  \
+                     scale2, scale, n_hot, max_chunks, hot_part, hot_cnt,                        \
+                     static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
     switch (G) {
       case 1: SAS_DKDV_TS(1); break;
       case 2: SAS_DKDV_TS(2); break;
@@ -773,7 +863,12 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
       default: SAS_DKDV_TS(8); break;
     }
 #undef SAS_DKDV_TS
-    return check_launch("bwd_dkdv_ts");
+    s = check_launch("bwd_dkdv_ts");
+    if (s != SAS_OK || max_chunks == 1) return s;
+    hipLaunchKernelGGL(bwd_hot_reduce_kernel, dim3(n_hot, d.n_kv_heads, d.batch), dim3(256), 0,
+                       st, hot_part, hot_cnt, S, d.n_kv_heads, d.t_max, n_hot, max_chunks, scale,
+                       static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV));
+    return check_launch("bwd_hot_reduce");
   }
 #define SAS_DKDV_CASE(NWV)                                                                     \
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),         \

@@ -15,6 +15,8 @@ constexpr int kChunkGridCap = 256;   // decode select: at most this many chunk w
 constexpr int kChunkKeysCap = 512;   // ... and merged candidate keys per row for chunks < 256 blocks
 constexpr int kMaxTileRows = 1024;  // prefill tiles supported by the tile selector
 constexpr int kMaxMergeKeys = 2048; // chunk candidates one decode row may merge
+constexpr int kHotBlocks = 16;      // dK/dV: the first blocks may be split across workgroups ...
+constexpr int kHotCap = 96;         // ... into chunks of this many reading tiles
 
 // Set the thread-local error text (printf-style) and return `st`.
 sas_status fail(sas_status st, const char* fmt, ...);

@@ -46,6 +46,23 @@ def random_selection(rng, Hkv, n_tiles, k):
     return idx, lg
 
 
+def sink_selection(rng, Hkv, n_tiles, k):
+    """Like random_selection, but every tile that can selects blocks 0 and 1
+    (sink-heavy: those blocks are read by every tile)."""
+    idx = np.full((Hkv, n_tiles, k), -1, np.int64)
+    lg = np.full((Hkv, n_tiles, k), -np.inf)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            n = min(k, t)
+            if n:
+                sinks = [m for m in (0, 1) if m < t][:n]
+                rest = rng.choice(np.arange(len(sinks), t), size=n - len(sinks), replace=False)
+                ch = np.sort(np.concatenate([sinks, rest]).astype(np.int64))
+                idx[r, t, :n] = ch
+                lg[r, t, :n] = -rng.uniform(0.5, 8.0, size=n)
+    return idx, lg
+
+
 def check_select_tiles(p, summ_g, tiles):
     """GPU per-tile selection vs the oracle on the given tiles."""
     S_ = _sas()
@@ -92,6 +109,8 @@ def run_prefill_case(p, tiles=None, selection="oracle", gated=True, label=""):
     if selection == "oracle":
         sel = O.prefill_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
         idx, lg = sel["idx"], sel["log_gate"]
+    elif selection == "sink":
+        idx, lg = sink_selection(np.random.default_rng(4321), Hkv, n_tiles, k)
     else:
         idx, lg = random_selection(np.random.default_rng(1234), Hkv, n_tiles, k)
     scale = 1.0 / math.sqrt(d)
@@ -201,6 +220,15 @@ def test_bwd_full_workload_sampled_tiles():
     ctx = run_prefill_case(p, tiles=[0, 1, 2, 15, 16, 17, 100, 200, 253, 254, 255],
                            selection="random", label="qwen3_4b_prefill_16k")
     run_bwd_case(p, ctx, exact_blocks=[253, 254, 255], label="qwen3_4b_prefill_16k")
+
+
+def test_bwd_hot_blocks_split():
+    """Sink-heavy selection: blocks 0 and 1 are read by all 200 tiles, so for
+    d = 128 the dK/dV pass splits them into chunks of reading tiles whose
+    fp32 partials are summed by the reduction kernel; everything is compared."""
+    p = _problem(64 * 200, 8, 2, 128, 128, 8, seed=77)
+    ctx = run_prefill_case(p, selection="sink", label="sink")
+    run_bwd_case(p, ctx, label="sink")
 
 
 def test_bwd_deterministic():
