@@ -5,7 +5,9 @@ Small shapes are checked on every tile; the full training-style workload
 (S=16384, Qwen3-4B head shape, per-tile k=16) is checked on sampled tiles
 (first, last, around the k boundary and in the middle).  The attention stage
 gets a selection that does not come from the GPU: the oracle's own Top-K on
-small shapes, a seeded random valid selection at full size."""
+small shapes, a seeded random valid selection at full size.  Also covered: a
+sink-heavy selection (hot-block chunking of the dK/dV pass), two sequences in
+one call, the largest k (64) and the largest sequence (1024 tiles, sampled)."""
 import math
 
 import numpy as np
@@ -242,3 +244,55 @@ def test_bwd_deterministic():
         outs.append([x.clone() for x in r])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_prefill_batch2_fwd_bwd():
+    """Two sequences in one call (grid z): each checked against the oracle run
+    on its own, with the oracle's selection of that sequence."""
+    S_ = _sas()
+    S, Hq, Hkv, d, k = 700, 8, 2, 128, 5
+    wl = synth.custom_workload("prefill", batch=2, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                               sel_dim=128, top_k=k, dtype="bf16", seq_len=S)
+    p = synth.make_problem(wl, 31)
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    Qd, Kd, Vd, dOd = dev(p.q), dev(p.K), dev(p.V), dev(p.dO)
+    sels, refs = [], []
+    for b in range(2):
+        Qf, Kf, Vf, dOf = (synth.to_f64(x[b], "bf16") for x in (p.q, p.K, p.V, p.dO))
+        sel = O.prefill_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        sels.append(sel)
+        Or, lser = O.prefill_attend(Qf, Kf, Vf, S, sel["idx"], sel["log_gate"], scale, G)
+        gr = O.prefill_backward(Qf, Kf, Vf, dOf, S, sel["idx"], sel["log_gate"], scale, G)
+        refs.append((Or, lser, gr))
+    idx = idx_dev(np.stack([s["idx"] for s in sels]))
+    lg = lg_dev(np.stack([s["log_gate"] for s in sels]))
+    O_g, lse_g = S_.sas_prefill_fwd(Qd, Kd, Vd, idx, lg)
+    dQ, dK, dV, dlg = S_.sas_bwd(Qd, Kd, Vd, O_g, dOd, lse_g, idx, lg)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Or, lser, (rQ, rK, rV, rlg) = refs[b]
+        assert np.abs(host(O_g)[b] - Or).max() <= TOL_OUT["bf16"]
+        for g, r in ((dQ, rQ), (dK, rK), (dV, rV)):
+            x = host(g)[b][:, :S]
+            assert np.linalg.norm(x - r) <= TOL_GRAD_REL * np.linalg.norm(r), b
+        valid = sels[b]["idx"] >= 0
+        e = np.linalg.norm(host(dlg)[b][valid] - rlg[valid]) / np.linalg.norm(rlg[valid])
+        assert e <= TOL_GRAD_REL, (b, e)
+
+
+def test_prefill_k64_fwd_bwd():
+    """The largest k built (64): tiles past the 64th select 64 history blocks."""
+    p = _problem(64 * 70 + 17, 4, 1, 128, 128, 64, seed=64)
+    ctx = run_prefill_case(p, selection="random", label="k=64")
+    run_bwd_case(p, ctx, label="k=64")
+
+
+@pytest.mark.timeout(900)
+def test_prefill_max_tiles_sampled():
+    """The largest sequence the tile selector supports (1024 tiles, S = 65536),
+    forward and backward on sampled tiles / exact blocks."""
+    p = _problem(65536, 4, 1, 128, 128, 16, seed=65)
+    ctx = run_prefill_case(p, tiles=[0, 1, 511, 1021, 1022, 1023], selection="random",
+                           label="S=65536")
+    run_bwd_case(p, ctx, exact_blocks=[1021, 1022, 1023], label="S=65536")
