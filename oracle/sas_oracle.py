@@ -55,6 +55,11 @@ Sources are cited by page and section; the short names are:
    carries ``ds`` to ``Wq_sel`` and ``Wk_sel``.  The selector's own chain into
    the backbone's Q and K is not formed: the backbone is held fixed while the
    selector trains.
+9. Per-query selection (a next row, oracle only; SAS close reading 2.4: the
+   training kernel masks unselected blocks by each query's own gate
+   threshold): query i of a prefill has its own scores over its C_i = i // b
+   history blocks (step 3 with the query alone), its own gate and Top-K, and
+   attends like a decode query at position i.
 
 Every stage is its own function so a test can feed one stage's inputs
 independently of the others.  All arithmetic is float64 NumPy; loops are kept
@@ -454,6 +459,62 @@ def prefill_select(Q, K, S, Wq_sel, Wk_sel, k, G, b=BLOCK):
         idx[r], lg[r], lse[r], gap[r] = i_r, lg_r, lse_r, gap_r
     return {"idx": idx, "log_gate": lg, "score_lse": lse, "gap": gap, "scores": rows,
             "summ": summ}
+
+
+# --------------------------------------------------------------------------
+# 9. Per-query selection in prefill (a next row: oracle only, no kernel yet)
+# --------------------------------------------------------------------------
+def query_scores(Q, S, Wq_sel, summ, G, b=BLOCK, queries=None):
+    """Per-query, per-group scores for a prefill with one selection per query
+    (SAS close reading 2.4: the training kernel masks the unselected blocks by
+    each query's own gate threshold).  Query i has the C_i = i // b complete
+    blocks before its own block as history, and its score of block m is step 3
+    with the query alone in place of a tile: the mean over its group's heads
+    of (Wq_sel q_{h,i}) . summ_m / sqrt(d_sel), i.e. the decode score of a
+    query at position i.  Q: [Hq, >=S, d]; summ: [Hkv, >=C, d_sel].
+    Returns {i: array [Hkv, C_i]} for the queries asked for (all by default).
+    """
+    out = {}
+    for i in (range(S) if queries is None else queries):
+        C = i // b
+        out[i] = decode_scores(Q[:, i], Wq_sel, summ[:, :C], G)
+    return out
+
+
+def query_select(Q, K, S, Wq_sel, Wk_sel, k, G, b=BLOCK, queries=None):
+    """Summaries -> per-query scores -> gate -> Top-K for one sequence (the
+    threshold of query i is its k-th largest score, ties to the lower block).
+
+    Returns idx/log_gate [Hkv, S, k] (-1 / -inf padded), score_lse and gap
+    [Hkv, S]; with ``queries`` only those rows are filled in."""
+    Hkv = K.shape[0]
+    summ = block_summaries(K, S, Wk_sel, b)
+    rows = query_scores(Q, S, Wq_sel, summ, G, b, queries)
+    idx = np.full((Hkv, S, k), -1, np.int64)
+    lg = np.full((Hkv, S, k), NEG_INF)
+    lse = np.zeros((Hkv, S))
+    gap = np.zeros((Hkv, S))
+    for i, s in rows.items():
+        i_r, lg_r, lse_r, gap_r = select_rows([s[r] for r in range(Hkv)], k)
+        idx[:, i], lg[:, i], lse[:, i], gap[:, i] = i_r, lg_r, lse_r, gap_r
+    return {"idx": idx, "log_gate": lg, "score_lse": lse, "gap": gap, "scores": rows,
+            "summ": summ}
+
+
+def query_attend(Q, K, V, S, idx, log_gate, scale, G, b=BLOCK, gated=True, queries=None):
+    """Causal gated block-sparse attention with one selection per query: query
+    i attends to the blocks idx[r, i] (bias log g) and to tokens b*(i//b)..i of
+    its own block (bias 0) -- a decode step at T = i + 1.
+
+    Q: [Hq, >=S, d]; K, V: [Hkv, >=S, d]; idx, log_gate: [Hkv, S, k].
+    Returns O [Hq, S, d] and lse [Hq, S] (only the requested queries)."""
+    Hq, _, d = Q.shape
+    O = np.zeros((Hq, S, d))
+    lse = np.zeros((Hq, S))
+    for i in (range(S) if queries is None else queries):
+        o, l = decode_attend(Q[:, i], K, V, i + 1, idx[:, i], log_gate[:, i], scale, G, b, gated)
+        O[:, i], lse[:, i] = o, l
+    return O, lse
 
 
 # --------------------------------------------------------------------------

@@ -13,6 +13,9 @@
 * the selector backward: dL/ds of the attention loss by central differences on
   the scores (eq. 8's sparse-scope term for unselected blocks, sum ds = 0), and
   dWq_sel / dWk_sel by central differences on the weights;
+* per-query selection: dense causal attention with a per-query log-gate bias
+  when k covers the history, local causal attention at k = 0, and the tile
+  scores when the queries of each tile are equal;
 * planted mistakes: each mutation of the oracle must make some pin fail.
 """
 import itertools
@@ -542,10 +545,97 @@ def test_selector_weight_gradients_match_finite_differences():
 
 
 # --------------------------------------------------------------------------
+# per-query selection (a next row): dense causal attention with a per-query
+# bias, k = 0, and consistency with the tile selection
+def _query_problem(seed, S=150, b=16, Hq=4, Hkv=2, d=8, d_sel=6):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((Hq, S, d))
+    K = rng.standard_normal((Hkv, S, d))
+    V = rng.standard_normal((Hkv, S, d))
+    Wq = rng.standard_normal((d_sel, d)) / math.sqrt(d_sel)
+    Wk = rng.standard_normal((d_sel, d)) / math.sqrt(d_sel)
+    return Q, K, V, Wq, Wk
+
+
+def check_query_selection_dense(seed=31):
+    """k >= every C_i: each query selects all its history blocks, so the
+    attention is dense causal attention whose logits carry, per query row, the
+    log-gate of the key's block (0 in the query's own block)."""
+    S, b, Hq, Hkv, d = 150, 16, 4, 2, 8
+    G = Hq // Hkv
+    Q, K, V, Wq, Wk = _query_problem(seed, S, b, Hq, Hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    sel = O.query_select(Q, K, S, Wq, Wk, 100, G, b)
+    Oq, _ = O.query_attend(Q, K, V, S, sel["idx"], sel["log_gate"], scale, G, b)
+    for h in range(Hq):
+        r = h // G
+        bias = np.full((S, S), -np.inf)
+        for i in range(S):
+            C = i // b
+            assert list(sel["idx"][r, i, :C]) == list(range(C))
+            lg = sel["log_gate"][r, i, :C]
+            if C:
+                assert abs(np.exp(lg).sum() - 1.0) < 1e-12     # the gate is a softmax
+            for j in range(i + 1):
+                bias[i, j] = lg[j // b] if j // b < C else 0.0
+        Z = Q[h, :S] @ K[r, :S].T * scale + bias
+        P = np.exp(Z - Z.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        assert np.abs(P @ V[r, :S] - Oq[h]).max() < 1e-12
+
+
+def check_query_k0_local(seed=32):
+    """k = 0: every query attends to its own block only, causally."""
+    S, b, Hq, Hkv, d = 100, 16, 4, 2, 8
+    G = Hq // Hkv
+    Q, K, V, Wq, Wk = _query_problem(seed, S, b, Hq, Hkv, d)
+    scale = 1.0 / math.sqrt(d)
+    sel = O.query_select(Q, K, S, Wq, Wk, 0, G, b)
+    Oq, lse = O.query_attend(Q, K, V, S, sel["idx"], sel["log_gate"], scale, G, b)
+    for h in range(Hq):
+        r = h // G
+        for i in range(S):
+            j0 = b * (i // b)
+            z = K[r, j0:i + 1] @ Q[h, i] * scale
+            p = np.exp(z - z.max())
+            assert np.abs(p @ V[r, j0:i + 1] / p.sum() - Oq[h, i]).max() < 1e-12
+            assert abs(lse[h, i] - (z.max() + math.log(p.sum()))) < 1e-12
+
+
+def check_query_scores_vs_tiles(seed=33):
+    """Queries that are equal within each tile give the tile's scores: the
+    tile's pooling then averages identical rows."""
+    S, b, Hq, Hkv, d = 96, 16, 4, 2, 8
+    G = Hq // Hkv
+    Q, K, V, Wq, Wk = _query_problem(seed, S, b, Hq, Hkv, d)
+    for t in range(S // b):
+        Q[:, b * t:b * t + b] = Q[:, b * t:b * t + 1]
+    summ = O.block_summaries(K, S, Wk, b)
+    rows_q = O.query_scores(Q, S, Wq, summ, G, b)
+    rows_t = O.tile_scores(Q, S, Wq, summ, G, b)
+    for i in range(S):
+        assert rows_q[i].shape == rows_t[i // b].shape
+        assert np.abs(rows_q[i] - rows_t[i // b]).max(initial=0.0) < 1e-12
+
+
+def test_query_selection_is_dense_when_k_covers_history():
+    check_query_selection_dense()
+
+
+def test_query_selection_k0_is_local_causal():
+    check_query_k0_local()
+
+
+def test_query_scores_match_tile_scores_on_tile_constant_queries():
+    check_query_scores_vs_tiles()
+
+
+# --------------------------------------------------------------------------
 PINS = [check_hand_worked, check_topk_lexsort, check_topk_exhaustive, check_gather_vs_dense,
         check_uniform_gate_is_dense_with_bias, check_k0_is_local_causal, check_dlog_gate_fd,
         check_qkv_grads_fd, check_summaries, check_selector_score_grad_fd,
-        check_selector_weights_fd]
+        check_selector_weights_fd, check_query_selection_dense, check_query_k0_local,
+        check_query_scores_vs_tiles]
 
 
 def _some_pin_fails():
@@ -574,7 +664,17 @@ def _summaries_sum_not_mean(K, T, Wk, b=O.BLOCK):
 
 
 _ORIG = {"gate": O.gate, "topk": O.topk, "block_summaries": O.block_summaries,
-         "_selected_tokens": O._selected_tokens, "score_grad": O.score_grad}
+         "_selected_tokens": O._selected_tokens, "score_grad": O.score_grad,
+         "query_scores": O.query_scores}
+
+
+def _query_history_includes_own_block(Q, S, Wq, summ, G, b=O.BLOCK, queries=None):
+    """Lets query i score its own (incomplete) block as history."""
+    out = {}
+    for i in (range(S) if queries is None else queries):
+        C = min(i // b + 1, summ.shape[1])
+        out[i] = O.decode_scores(Q[:, i], Wq, summ[:, :C], G)
+    return out
 
 
 def _score_grad_no_normaliser(s, idx_row, dlg_row):
@@ -602,6 +702,7 @@ def _off_by_one_block(idx_row, lg_row, b, gated):
     ("_selected_tokens", _drop_gate_bias),
     ("_selected_tokens", _off_by_one_block),
     ("score_grad", _score_grad_no_normaliser),
+    ("query_scores", _query_history_includes_own_block),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
