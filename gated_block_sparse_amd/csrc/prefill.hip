@@ -26,35 +26,54 @@
 
 namespace sas {
 
-// Per-thread share of staging one 64-token block: K and V rows, as 16-byte
-// chunks copied row-major into LDS (V, at the transpose-read stride, is read
-// back transposed by the LDS transpose read, so no shuffling on the way in).
-template <int D, int NT>
-struct BlockStage {
-  static constexpr int TOT = 64 * (D / 8);           // 16-byte chunks per tensor
-  static constexpr int CH = (TOT + NT - 1) / NT;     // per thread
-  uint4 k[CH], v[CH];
+// Staging of one 64-token block by LDS DMA (global_load_lds_dwordx4): the K
+// tile at the row-read stride and the V tile at the transpose-read stride.
+// One copy instruction fills 64 consecutive 16-byte positions of a tile, so
+// a padded row of RB bytes spans RB / 16 positions and a tile 64 * RB / 16
+// positions, i.e. RB / 16 instructions.  Lane L of instruction n takes
+// position 64 n + L: row p / (RB / 16), chunk p % (RB / 16); a lane whose
+// position falls in the row padding fetches the row's first chunk again
+// (its bytes land in the padding, which nobody reads).  Rows at or past the
+// sequence end repeat its last row: finite values whose probabilities are
+// masked to zero.  Each wave issues the same number of copies per tile
+// (instructions past the last repeat it), so per-wave wait counts are exact.
+template <int D, int NW>
+struct DmaStage {
+  static constexpr int KRB = kRowStride<D> * 2, VRB = kTrStride<D> * 2;   // bytes per row
+  static constexpr int KPOS = KRB / 16, VPOS = VRB / 16;                  // positions per row
+  static constexpr int KINS = KPOS, VINS = VPOS;                          // copies per tile
+  static constexpr int KPW = (KINS + NW - 1) / NW, VPW = (VINS + NW - 1) / NW;   // per wave
+  static constexpr int KTILE = 64 * KRB, VTILE = 64 * VRB;                // bytes per tile
+  int koff[KPW], voff[VPW];   // row * D + channel of the lane's chunk (row before clamping)
+  int krow[KPW], vrow[VPW];
 
-  __device__ __forceinline__ void load(const uint16_t* Kb, const uint16_t* Vb, int valid, int tid) {
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
-      const bool ok = c < TOT && row < valid;
-      k[i] = ok ? *reinterpret_cast<const uint4*>(Kb + static_cast<size_t>(row) * D + cc * 8)
-                : make_uint4(0, 0, 0, 0);
-      v[i] = ok ? *reinterpret_cast<const uint4*>(Vb + static_cast<size_t>(row) * D + cc * 8)
-                : make_uint4(0, 0, 0, 0);
+    for (int n = 0; n < KPW; ++n) {
+      const int p = 64 * min(wave + NW * n, KINS - 1) + lane, c = p % KPOS;
+      krow[n] = p / KPOS;
+      koff[n] = 8 * (c < D / 8 ? c : 0);
+    }
+#pragma unroll
+    for (int n = 0; n < VPW; ++n) {
+      const int p = 64 * min(wave + NW * n, VINS - 1) + lane, c = p % VPOS;
+      vrow[n] = p / VPOS;
+      voff[n] = 8 * (c < D / 8 ? c : 0);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* Ks, uint16_t* Vs, int tid) const {
+  // K (or V) rows tok.. of the block, `valid` of them inside the sequence,
+  // into the tile at LDS byte address `dst`.
+  __device__ __forceinline__ void k(const uint16_t* Kb, int valid, uint32_t dst, int wave) const {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NT, row = c / (D / 8), cc = c % (D / 8);
-      if (c < TOT) {
-        lds_store_row8<kRowStride<D>>(Ks, row, cc * 8, k[i]);
-        lds_store_row8<kTrStride<D>>(Vs, row, cc * 8, v[i]);
-      }
-    }
+    for (int n = 0; n < KPW; ++n)
+      lds_dma<16>(Kb + static_cast<size_t>(min(krow[n], valid - 1)) * D + koff[n],
+                  dst + 1024 * min(wave + NW * n, KINS - 1));
+  }
+  __device__ __forceinline__ void v(const uint16_t* Vb, int valid, uint32_t dst, int wave) const {
+#pragma unroll
+    for (int n = 0; n < VPW; ++n)
+      lds_dma<16>(Vb + static_cast<size_t>(min(vrow[n], valid - 1)) * D + voff[n],
+                  dst + 1024 * min(wave + NW * n, VINS - 1));
   }
 };
 
@@ -88,9 +107,12 @@ __device__ __forceinline__ void block_pv(const uint16_t* Vc, const bf16x8_t* pb,
 //   A: adds block i-1's P V into O^T (MFMA) while it takes block i's max (VALU),
 //   B: computes block i+1's scores (MFMA) while it exponentiates block i (VALU),
 // so the matrix cores and the vector ALUs of a wave have independent work at
-// every point.  Staged blocks live in a ring of four LDS buffers (block i in
-// buffer i % 4); block i+2 is written while blocks i-1 and i+1 are read, so
-// one barrier per iteration suffices.
+// every point.  K and V tiles live in two rings of four LDS buffers (block j
+// in buffer j % 4).  Iteration i reads K of block i+1 and V of block i-1 and
+// starts the copies of K of block i+3 and V of block i+2: each goes into the
+// buffer whose last reader ran in iteration i-2 or i-1, before the barrier
+// that ends iteration i-1, and has two iterations to land.  One wait + barrier
+// per iteration suffices.
 template <int D, int HPW>
 __global__ void __launch_bounds__(128 * HPW)
 prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -162,19 +184,29 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // buffer nobody reads again), and the first iteration's P V runs on a
   // zeroed buffer with P = 0.
   const int nh = nblk - 1;
-  BlockStage<D, NT> stg;
-  auto load_block = [&](int i) {
+  using Stage = DmaStage<D, NT / 64>;
+  Stage stg;
+  stg.init(wave, lane);
+  const uint32_t ks_lds = lds_addr_of(&Ks[0][0]), vs_lds = lds_addr_of(&Vs[0][0]);
+  auto copy_k = [&](int i) {
     const int tok = s_blk[min(i, nh)] * 64;
-    stg.load(Kg + static_cast<size_t>(tok) * D, Vg + static_cast<size_t>(tok) * D, S - tok, tid);
+    stg.k(Kg + static_cast<size_t>(tok) * D, S - tok, ks_lds + (i & 3) * Stage::KTILE, wave);
   };
-  load_block(0);
-  stg.store(Ks[0], Vs[0], tid);
-  load_block(1);
-  stg.store(Ks[1], Vs[1], tid);
+  auto copy_v = [&](int i) {
+    const int tok = s_blk[min(i, nh)] * 64;
+    stg.v(Vg + static_cast<size_t>(tok) * D, S - tok, vs_lds + (i & 3) * Stage::VTILE, wave);
+  };
   for (int c = tid; c < 64 * kTrStride<D> / 8; c += NT)
     *reinterpret_cast<uint4*>(&Vs[3][8 * c]) = make_uint4(0, 0, 0, 0);
-  load_block(2);
-  __syncthreads();
+  // in this order the wait below leaves exactly K of block 2 and V of block 1
+  // in flight; every later wait leaves the copies of the last one and a half
+  // iterations (V of block i+1, K of block i+3, V of block i+2)
+  copy_k(0);
+  copy_v(0);
+  copy_k(1);
+  copy_k(2);
+  copy_v(1);
+  dma_sync<Stage::KPW + Stage::VPW>();
 
   f32x16_t s_cur[2];
   block_scores<D>(Ks[0], qb, s_cur, l32, hi);
@@ -222,6 +254,8 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   for (int it = 0; it < nh; ++it) {
     const float beta2 = s_beta[it];
+    copy_k(it + 3);
+    copy_v(it + 2);
     // A: the previous block's P V, this block's max
     block_pv<D>(Vs[(it + 3) & 3], p_prev, acc, hi);
     update_max(beta2);
@@ -230,12 +264,14 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     f32x16_t s_next[2];
     block_scores<D>(Ks[(it + 1) & 3], qb, s_next, l32, hi);
     probabilities(beta2);
-    stg.store(Ks[(it + 2) & 3], Vs[(it + 2) & 3], tid);
-    load_block(it + 3);
-    __syncthreads();
+    // K of block it+2 (read next) and V of block it (read next) have landed
+    dma_sync<2 * Stage::VPW + Stage::KPW>();
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) s_cur[tt] = s_next[tt];
   }
+  // V of the diagonal block (and the copies past the list) have landed;
+  // nothing is left in flight when the workgroup ends
+  dma_sync<0>();
   // the diagonal block: causal mask j > i
   block_pv<D>(Vs[(nh + 3) & 3], p_prev, acc, hi);
 #pragma unroll
