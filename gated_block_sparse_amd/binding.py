@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID_ARGUMENT, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE_TOO_SMALL, SAS_ERR_HIP = range(5)
 SAS_F32, SAS_BF16 = 0, 1
-SAS_SELECT_DECODE, SAS_SELECT_TILES = 0, 1
+SAS_SELECT_DECODE, SAS_SELECT_TILES, SAS_SELECT_QUERIES = 0, 1, 2
 (SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD,
- SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD) = range(7)
+ SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD, SAS_OP_SELECT_QUERIES,
+ SAS_OP_PREFILL_FWD_QUERIES) = range(9)
 BLOCK = 64
 SIZE_MAX = 2 ** 64 - 1
 
@@ -50,6 +51,8 @@ _SIGNATURES = {
     "sas_decode_step_paged": (_i32, [_PD, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
                                      _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sas_prefill_fwd": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp]),
+    "sas_prefill_fwd_queries": (_i32, [_PD, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
+                                       _sz, _vp]),
     "sas_bwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
                        _vp, _vp, _sz, _vp]),
     "sas_selector_bwd": (_i32, [_PD, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -155,7 +158,8 @@ def sas_select(mode, Q, seq_lens, Wq_sel, summ, top_k, t_max=None, q_len=None,
                ws=None):
     """Selector scores, gate and Top-K.  Returns (idx, log_gate, score_lse, scores|None).
 
-    mode SAS_SELECT_DECODE: Q is q [B,Hq,d]; SAS_SELECT_TILES: Q is [B,Hq,S,d].
+    mode SAS_SELECT_DECODE: Q is q [B,Hq,d]; SAS_SELECT_TILES and
+    SAS_SELECT_QUERIES: Q is [B,Hq,S,d] (rows: ceil(S/64) tiles, or S queries).
     t_max: K/V row capacity (default: the largest one whose summary buffer has
     summ.shape[2] rows, so no sequence length that fits the buffer is clipped)."""
     B, Hkv, c_max, ds = summ.shape
@@ -165,6 +169,9 @@ def sas_select(mode, Q, seq_lens, Wq_sel, summ, top_k, t_max=None, q_len=None,
     if mode == SAS_SELECT_TILES:
         q_len = Q.shape[2] if q_len is None else q_len
         rows = -(-q_len // BLOCK)
+    elif mode == SAS_SELECT_QUERIES:
+        q_len = Q.shape[2] if q_len is None else q_len
+        rows = q_len
     else:
         q_len, rows = 0, 1
     dims = make_dims(B, Hq, Hkv, d, ds, top_k, t_max, _dtype_code(Q))
@@ -177,7 +184,8 @@ def sas_select(mode, Q, seq_lens, Wq_sel, summ, top_k, t_max=None, q_len=None,
         score_lse = torch.empty(B, Hkv, rows, dtype=torch.float32, device=dev)
     if want_scores and scores is None:
         scores = torch.full((B, Hkv, rows, c_max), float("nan"), dtype=torch.float32, device=dev)
-    op = SAS_OP_SELECT_TILES if mode == SAS_SELECT_TILES else SAS_OP_SELECT_DECODE
+    op = {SAS_SELECT_TILES: SAS_OP_SELECT_TILES,
+          SAS_SELECT_QUERIES: SAS_OP_SELECT_QUERIES}.get(mode, SAS_OP_SELECT_DECODE)
     ws, ws_bytes = _workspace(op, dims, q_len, ws, dev)
     _check(load_library().sas_select(ctypes.byref(dims), mode, _ptr(Q), q_len, _ptr(seq_lens),
                                      _ptr(Wq_sel), _ptr(summ), _ptr(idx), _ptr(log_gate),
@@ -309,6 +317,28 @@ def sas_prefill_fwd(Q, K, V, idx, log_gate, scale=None, seq_len=None, O=None, ls
     _check(load_library().sas_prefill_fwd(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), seq_len,
                                           _ptr(idx), _ptr(log_gate), scale, _ptr(O), _ptr(lse),
                                           _ptr(ws), ws_bytes, _stream()))
+    return O, lse
+
+
+def sas_prefill_fwd_queries(Q, K, V, idx, log_gate, scale=None, seq_len=None, O=None,
+                            lse=None, ws=None):
+    """Causal prefill forward with one selection per query (bf16).  Q
+    [B,Hq,S,d]; K,V [B,Hkv,t_max,d]; idx/log_gate [B,Hkv,S,k].  Returns (O, lse)."""
+    B, Hq, S, d = Q.shape
+    _, Hkv, t_max, _ = K.shape
+    seq_len = S if seq_len is None else seq_len
+    k = idx.shape[-1]
+    dims = make_dims(B, Hq, Hkv, d, 64, k, t_max, _dtype_code(Q))
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if O is None:
+        O = torch.empty_like(Q)
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=Q.device)
+    ws, ws_bytes = _workspace(SAS_OP_PREFILL_FWD_QUERIES, dims, seq_len, ws, Q.device)
+    _check(load_library().sas_prefill_fwd_queries(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V),
+                                                  seq_len, _ptr(idx), _ptr(log_gate), scale,
+                                                  _ptr(O), _ptr(lse), _ptr(ws), ws_bytes,
+                                                  _stream()))
     return O, lse
 
 

@@ -20,6 +20,8 @@
 //  * the log-gate is added per block; the diagonal block is masked j > i;
 //  * the block loop is software-pipelined (see the kernel) so each wave always
 //    has matrix and vector work that do not depend on each other.
+#include <climits>
+
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_mfma.h"
@@ -113,7 +115,17 @@ __device__ __forceinline__ void block_pv(const uint16_t* Vc, const bf16x8_t* pb,
 // buffer whose last reader ran in iteration i-2 or i-1, before the barrier
 // that ends iteration i-1, and has two iterations to land.  One wait + barrier
 // per iteration suffices.
-template <int D, int HPW>
+//
+// PQ (one selection per query, idx/log_gate [B,Hkv,S,k]): the workgroup walks
+// the union of its queries' selected blocks in ascending order (built from a
+// bitmap in LDS), and each lane, which owns one query column, takes the bias
+// of its own query for the block: log g if its query selected the block, -inf
+// otherwise (the per-query mask of the pages' training kernel), found by a
+// cursor into its query's ascending idx row.  Blocks no query of the tile
+// selected are never visited.  The running max starts at a finite floor so
+// that a query whose first visited blocks are all masked keeps l = 0 and
+// O = 0 until its first selected block.
+template <int D, int HPW, bool PQ>
 __global__ void __launch_bounds__(128 * HPW)
 prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, int S, int Hkv, int G, int t_max,
@@ -126,8 +138,9 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int NBUF = 4;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][64 * kRowStride<D>];  // row reads
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][64 * kTrStride<D>];   // transpose reads
-  __shared__ int s_blk[kMaxTopK + 1];
-  __shared__ float s_beta[kMaxTopK + 1];
+  __shared__ int s_blk[PQ ? kMaxTileRows + 1 : kMaxTopK + 1];
+  __shared__ float s_beta[PQ ? 1 : kMaxTopK + 1];
+  __shared__ uint32_t s_bits[PQ ? kMaxTileRows / 32 : 1];
   __shared__ int s_nblk;
 
   const int nhc = G / HPW;                       // head chunks per group
@@ -143,7 +156,39 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   // block list: the valid selected blocks (in slot order), then the diagonal
   const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
-  if (wave == 0) {
+  if constexpr (PQ) {
+    // union of the tile's per-query selections: bitmap, then a compaction by
+    // wave 0 (lane w owns blocks 32w .. 32w+31) into ascending order
+    for (int w = tid; w < kMaxTileRows / 32; w += NT) s_bits[w] = 0u;
+    __syncthreads();
+    const size_t qrow0 = (static_cast<size_t>(b) * Hkv + r) * S + static_cast<size_t>(t) * 64;
+    const int n_ent = min(64, S - t * 64) * k;
+    for (int e = tid; e < n_ent; e += NT) {
+      const int m = idx[qrow0 * k + e];
+      if (m >= 0) atomicOr(&s_bits[m >> 5], 1u << (m & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t w = lane < kMaxTileRows / 32 ? s_bits[lane] : 0u;
+      const int cnt = __popc(w);
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      int pos = incl - cnt;
+      while (w) {
+        s_blk[pos++] = 32 * lane + (__ffs(w) - 1);
+        w &= w - 1u;
+      }
+      const int total = __shfl(incl, 63, 64);
+      if (lane == 0) {
+        s_blk[total] = t;
+        s_nblk = total + 1;
+      }
+    }
+  } else if (wave == 0) {
     const bool ok = lane < k && idx[srow * k + lane] >= 0;
     const unsigned long long mask = __ballot(ok);
     if (ok) {
@@ -170,7 +215,24 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   f32x16_t acc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) zero16(acc[ct]);
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = PQ ? -1e30f : -INFINITY, l_run = 0.f;
+
+  // PQ: cursor into the lane's query's ascending selection (next selected
+  // block and its log2-scaled gate; INT_MAX once the row is exhausted)
+  const size_t qsel = PQ ? ((static_cast<size_t>(b) * Hkv + r) * S + (qvalid ? qi : 0)) * k : 0;
+  int cur = 0, nxt = INT_MAX;
+  float nxt_beta = 0.f;
+  auto fetch = [&]() {
+    nxt = INT_MAX;
+    if (qvalid && cur < k) {
+      const int v = idx[qsel + cur];
+      if (v >= 0) {
+        nxt = v;
+        nxt_beta = log_gate ? log_gate[qsel + cur] * kLog2eF : 0.f;
+      }
+    }
+  };
+  if constexpr (PQ) fetch();
 
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
@@ -253,7 +315,17 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   };
 
   for (int it = 0; it < nh; ++it) {
-    const float beta2 = s_beta[it];
+    float beta2;
+    if constexpr (PQ) {
+      const bool hit = nxt == s_blk[it];
+      beta2 = hit ? nxt_beta : -INFINITY;
+      if (hit) {
+        ++cur;
+        fetch();
+      }
+    } else {
+      beta2 = s_beta[it];
+    }
     copy_k(it + 3);
     copy_v(it + 2);
     // A: the previous block's P V, this block's max
@@ -291,7 +363,7 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
 size_t prefill_ws_bytes(const sas_dims&, int) { return 0; }
 
-template <int D>
+template <int D, bool PQ>
 static sas_status launch_pf(const sas_dims& d, const void* Q, const void* K, const void* V,
                             int S, const int32_t* idx, const float* log_gate, float scale,
                             void* O, float* lse, hipStream_t st) {
@@ -299,18 +371,18 @@ static sas_status launch_pf(const sas_dims& d, const void* Q, const void* K, con
   const int n_tiles = cdiv(S, kBlock);
   const float scale2 = scale * kLog2eF;
 #define SAS_PF_CASE(HPW)                                                                   \
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, HPW>), dim3(n_tiles * (G / HPW), d.n_kv_heads, \
-                     d.batch), dim3(128 * HPW), 0, st, static_cast<const uint16_t*>(Q),   \
-                     static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), S,   \
-                     d.n_kv_heads, G, d.t_max, n_tiles, d.top_k, idx, log_gate, scale2,     \
-                     static_cast<uint16_t*>(O), lse)
+  hipLaunchKernelGGL((prefill_fwd_kernel<D, HPW, PQ>), dim3(n_tiles * (G / HPW),           \
+                     d.n_kv_heads, d.batch), dim3(128 * HPW), 0, st,                        \
+                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),      \
+                     static_cast<const uint16_t*>(V), S, d.n_kv_heads, G, d.t_max, n_tiles, \
+                     d.top_k, idx, log_gate, scale2, static_cast<uint16_t*>(O), lse)
   switch (G) {
     case 1: SAS_PF_CASE(1); break;
     case 2: SAS_PF_CASE(2); break;
     default: SAS_PF_CASE(4); break;  // G = 4 or 8 (two head chunks)
   }
 #undef SAS_PF_CASE
-  return check_launch("prefill_fwd");
+  return check_launch(PQ ? "prefill_fwd_queries" : "prefill_fwd");
 }
 
 sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,
@@ -318,8 +390,17 @@ sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, c
                               float scale, void* O, float* lse, void* ws, hipStream_t st) {
   (void)ws;
   if (d.head_dim == 128)
-    return launch_pf<128>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
-  return launch_pf<64>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
+    return launch_pf<128, false>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
+  return launch_pf<64, false>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
+}
+
+sas_status launch_prefill_fwd_queries(const sas_dims& d, const void* Q, const void* K,
+                                      const void* V, int seq_len, const int32_t* idx,
+                                      const float* log_gate, float scale, void* O, float* lse,
+                                      hipStream_t st) {
+  if (d.head_dim == 128)
+    return launch_pf<128, true>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
+  return launch_pf<64, true>(d, Q, K, V, seq_len, idx, log_gate, scale, O, lse, st);
 }
 
 }  // namespace sas

@@ -135,6 +135,14 @@ sas_status sas_select(const sas_dims* dims, int32_t mode, const void* Q, int32_t
     return launch_select_tiles(*dims, Q, q_len, Wq_sel, summ, idx, log_gate, score_lse,
                                scores, st);
   }
+  if (mode == SAS_SELECT_QUERIES) {
+    SAS_TRY(check_len(dims, q_len, "q_len"));
+    if (cdiv(q_len, kBlock) > kMaxTileRows)
+      return fail(SAS_ERR_UNSUPPORTED, "q_len=%d gives more than %d tiles", q_len,
+                  kMaxTileRows);
+    return launch_select_queries(*dims, Q, q_len, Wq_sel, summ, idx, log_gate, score_lse,
+                                 scores, st);
+  }
   return fail(SAS_ERR_INVALID_ARGUMENT, "mode=%d is not a sas_select_mode", mode);
 }
 
@@ -257,6 +265,28 @@ sas_status sas_prefill_fwd(const sas_dims* dims, const void* Q, const void* K, c
                             static_cast<hipStream_t>(stream));
 }
 
+sas_status sas_prefill_fwd_queries(const sas_dims* dims, const void* Q, const void* K,
+                                   const void* V, int32_t seq_len, const int32_t* idx,
+                                   const float* log_gate, float scale, void* O, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;   // no workspace
+  SAS_TRY(check_dims(dims, true));
+  SAS_TRY(check_len(dims, seq_len, "seq_len"));
+  SAS_NONNULL(Q);
+  SAS_NONNULL(K);
+  SAS_NONNULL(V);
+  SAS_NONNULL(O);
+  SAS_NONNULL(lse);
+  if (dims->top_k > 0) SAS_NONNULL(idx);
+  if (!(scale > 0.0f)) return fail(SAS_ERR_INVALID_ARGUMENT, "scale must be a positive number");
+  if (cdiv(seq_len, kBlock) > kMaxTileRows)
+    return fail(SAS_ERR_UNSUPPORTED, "seq_len=%d gives more than %d tiles", seq_len,
+                kMaxTileRows);
+  return launch_prefill_fwd_queries(*dims, Q, K, V, seq_len, idx, log_gate, scale, O, lse,
+                                    static_cast<hipStream_t>(stream));
+}
+
 sas_status sas_bwd(const sas_dims* dims, const void* Q, const void* K, const void* V,
                    const void* O, const void* dO, const float* lse, int32_t seq_len,
                    const int32_t* idx, const float* log_gate, float scale, void* dQ, void* dK,
@@ -308,11 +338,16 @@ sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, 
 }
 
 size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
-  const bool bf16_only = (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD);
+  const bool bf16_only =
+      (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD || op == SAS_OP_PREFILL_FWD_QUERIES);
   if (check_dims(dims, bf16_only) != SAS_OK) return SIZE_MAX;
   switch (op) {
     case SAS_OP_SELECT_DECODE: return select_decode_ws_bytes(*dims);
     case SAS_OP_SELECT_TILES: return 0;
+    case SAS_OP_SELECT_QUERIES: return 0;
+    case SAS_OP_PREFILL_FWD_QUERIES:
+      if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
+      return 0;
     case SAS_OP_DECODE_FWD: return decode_ws_bytes(*dims);
     case SAS_OP_DECODE_STEP: return decode_step_ws_bytes(*dims);
     case SAS_OP_SELECTOR_BWD:

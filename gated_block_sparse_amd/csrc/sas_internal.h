@@ -70,6 +70,10 @@ size_t select_decode_ws_bytes(const sas_dims& d);
 sas_status launch_select_decode(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                 const float* Wq, const float* summ, int32_t* idx, float* log_gate,
                                 float* score_lse, float* scores, void* ws, hipStream_t st);
+// One selection row per query (rows = q_len; row i has C = i / 64).
+sas_status launch_select_queries(const sas_dims& d, const void* Q, int q_len, const float* Wq,
+                                 const float* summ, int32_t* idx, float* log_gate,
+                                 float* score_lse, float* scores, hipStream_t st);
 sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, const float* Wq,
                                const float* summ, int32_t* idx, float* log_gate,
                                float* score_lse, float* scores, hipStream_t st);
@@ -119,6 +123,11 @@ size_t prefill_ws_bytes(const sas_dims& d, int seq_len);
 sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,
                               int seq_len, const int32_t* idx, const float* log_gate,
                               float scale, void* O, float* lse, void* ws, hipStream_t st);
+// The same with one selection per query: idx/log_gate [B,Hkv,seq_len,k].
+sas_status launch_prefill_fwd_queries(const sas_dims& d, const void* Q, const void* K,
+                                      const void* V, int seq_len, const int32_t* idx,
+                                      const float* log_gate, float scale, void* O, float* lse,
+                                      hipStream_t st);
 
 size_t bwd_ws_bytes(const sas_dims& d, int seq_len);
 sas_status launch_bwd(const sas_dims& d, const void* Q, const void* K, const void* V,

@@ -384,6 +384,211 @@ select_tiles_kernel(const T* __restrict__ Q, int q_len, const float* __restrict_
   if (tid == 0) score_lse[row] = lse;
 }
 
+// ------------------------------------------------------------ queries ---
+// One selection per query (SAS close reading 2.4: the training kernel masks
+// every query by its own gate threshold).  Query i has the C = i / 64
+// complete blocks before its own block as history, and its score of block m
+// is the decode score of a query at position i: the mean over the group's G
+// heads of (Wq_sel q_h) . summ_m / sqrt(d_sel).  The GPU pools the G heads
+// first and projects once (linear; fp32 rounding only).
+//
+// One workgroup per 32 queries (half a tile), group and sequence; all its
+// queries share C.  The pooled queries and then their projections u (32 x
+// d_sel) sit in LDS; the summaries are scored in chunks of 64 blocks staged
+// in LDS (rows padded by 4 floats: the 16-byte reads of 16 consecutive rows
+// hit distinct banks), each thread forming 2 queries x 4 blocks.  Each wave
+// then keeps, for 8 queries, a running (max, sum-exp) and a running Top-K
+// list (descending composite keys, as in the decode selection): it sorts the
+// chunk's 64 keys across its lanes and merges them with the list by rank (a
+// key's place in the merged list is its own position plus the number of
+// larger keys in the other list).
+constexpr int kQsRows = 32;   // queries per workgroup
+constexpr int kQsChunk = 64;  // blocks scored per pass
+
+template <typename T, int D, int DS, int G>
+__global__ void __launch_bounds__(kSelThreads)
+select_queries_kernel(const T* __restrict__ Q, int q_len, const float* __restrict__ Wq,
+                      const float* __restrict__ summ, int Hkv, int c_max, int k,
+                      int32_t* __restrict__ idx, float* __restrict__ log_gate,
+                      float* __restrict__ score_lse, float* __restrict__ scores) {
+  constexpr int NW = kSelThreads / 64;          // waves
+  constexpr int QPW = kQsRows / NW;             // queries per wave in the Top-K phase
+  constexpr int QS = D + 4, US = DS + 4;        // padded LDS row strides (floats)
+  constexpr int BUF = (kQsRows * QS > kQsChunk * US) ? kQsRows * QS : kQsChunk * US;
+  __shared__ __attribute__((aligned(16))) float buf[BUF];        // pooled queries, then summaries
+  __shared__ __attribute__((aligned(16))) float u[kQsRows * US];  // projected queries
+  __shared__ float sc[kQsRows][kQsChunk + 1];
+  __shared__ uint64_t top[kQsRows][kMaxTopK];
+  __shared__ uint64_t wk[NW][2][kQsChunk];
+
+  const int t = blockIdx.x >> 1, r = blockIdx.y, b = blockIdx.z;
+  const int i0 = t * kBlock + (blockIdx.x & 1) * kQsRows;
+  const int nq = min(kQsRows, q_len - i0);
+  if (nq <= 0) return;   // second half of a short last tile (workgroup-uniform)
+  const int C = t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // ---- pooled queries qbar[q] = (1/G) sum_h Q[b, rG+h, i0+q, :]
+  {
+    constexpr int EPL = Vec16<T>::N, LPR = D / EPL;
+    for (int x = tid; x < kQsRows * LPR; x += kSelThreads) {
+      const int q = x / LPR, col = x % LPR;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      if (q < nq) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const T* src = Q + ((static_cast<size_t>(b) * Hkv * G + r * G + h) * q_len + i0 + q) * D +
+                         col * EPL;
+          float f[EPL];
+          Vec16<T>::unpack(*reinterpret_cast<const uint4*>(src), f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += f[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) buf[q * QS + col * EPL + e] = acc[e] * (1.0f / G);
+    }
+  }
+  __syncthreads();
+  // ---- u[q][c] = (Wq[c,:] . qbar[q]) / sqrt(DS); thread: channel c, every
+  // NQG-th query (a wave shares its query rows: broadcast LDS reads)
+  {
+    constexpr int NQG = kSelThreads / DS, NE = kQsRows / NQG;
+    const int c = tid % DS, qg = tid / DS;
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    const float4* w = reinterpret_cast<const float4*>(Wq + static_cast<size_t>(c) * D);
+#pragma unroll 4
+    for (int j4 = 0; j4 < D / 4; ++j4) {
+      const float4 x = w[j4];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float4 a = *reinterpret_cast<const float4*>(&buf[(qg + NQG * e) * QS + 4 * j4]);
+        acc[e] += x.x * a.x + x.y * a.y + x.z * a.z + x.w * a.w;
+      }
+    }
+    const float inv = 1.0f / sqrtf(static_cast<float>(DS));
+#pragma unroll
+    for (int e = 0; e < NE; ++e) u[(qg + NQG * e) * US + c] = acc[e] * inv;
+  }
+
+  float run_m[QPW], run_s[QPW];
+#pragma unroll
+  for (int e = 0; e < QPW; ++e) {
+    run_m[e] = -INFINITY;
+    run_s[e] = 0.f;
+  }
+  const float* srow = summ + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(c_max) * DS;
+  const size_t row0 = (static_cast<size_t>(b) * Hkv + r) * q_len + i0;   // row of query i0
+
+  for (int c0 = 0; c0 < C; c0 += kQsChunk) {
+    const int nb = min(kQsChunk, C - c0);
+    __syncthreads();   // the previous chunk's readers of buf/sc are done (and u is written)
+    // ---- stage the chunk's summaries
+    for (int x = tid; x < kQsChunk * (DS / 4); x += kSelThreads) {
+      const int m = x / (DS / 4), c4 = x % (DS / 4);
+      const float4 v = m < nb ? *reinterpret_cast<const float4*>(srow + static_cast<size_t>(c0 + m) * DS + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&buf[m * US + 4 * c4]) = v;
+    }
+    __syncthreads();
+    // ---- scores: thread (tq, tm) takes queries 2tq, 2tq+1 and blocks tm + 16x
+    {
+      const int tq = tid >> 4, tm = tid & 15;
+      float acc[2][4];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[a][x] = 0.f;
+#pragma unroll 4
+      for (int j4 = 0; j4 < DS / 4; ++j4) {
+        float4 uq[2], sv[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) uq[a] = *reinterpret_cast<const float4*>(&u[(2 * tq + a) * US + 4 * j4]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sv[x] = *reinterpret_cast<const float4*>(&buf[(tm + 16 * x) * US + 4 * j4]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            acc[a][x] += uq[a].x * sv[x].x + uq[a].y * sv[x].y + uq[a].z * sv[x].z + uq[a].w * sv[x].w;
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int q = 2 * tq + a, m = tm + 16 * x;
+          sc[q][m] = acc[a][x];
+          if (scores && q < nq && m < nb)
+            scores[(row0 + q) * c_max + c0 + m] = acc[a][x];
+        }
+    }
+    __syncthreads();
+    // ---- per query: softmax state and Top-K list
+#pragma unroll
+    for (int e = 0; e < QPW; ++e) {
+      const int q = wave * QPW + e;
+      if (q >= nq) continue;   // wave-uniform
+      const bool ok = lane < nb;
+      const float s = sc[q][lane];
+      const float cm = wave_max_from(ok ? s : -INFINITY, 1);
+      const float m_new = fmaxf(run_m[e], cm);
+      const float cs = wave_sum_from(ok ? expf(s - m_new) : 0.f, 1);
+      run_s[e] = run_s[e] * expf(run_m[e] - m_new) + cs;
+      run_m[e] = m_new;
+      if (k == 0) continue;
+      const uint64_t key = wave_sort_desc(ok ? topk_key(s, c0 + lane) : 0ull);
+      const int n_old = min(k, c0);            // kept so far (every earlier block is a candidate)
+      const int n_new = min(k, c0 + nb);
+      if (c0 == 0) {
+        if (lane < n_new) top[q][lane] = key;
+      } else {
+        uint64_t* chunk = wk[wave][0];
+        uint64_t* merged = wk[wave][1];
+        chunk[lane] = key;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // place of the chunk key and of the list key held by this lane
+        const int pc = ok ? lane + count_greater_desc(top[q], n_old, key) : kMaxTopK;
+        const uint64_t lk = lane < n_old ? top[q][lane] : 0ull;
+        const int pl = lane < n_old ? lane + count_greater_desc(chunk, nb, lk) : kMaxTopK;
+        if (pc < n_new) merged[pc] = key;
+        if (pl < n_new) merged[pl] = lk;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < n_new) top[q][lane] = merged[lane];
+      }
+    }
+  }
+  // ---- outputs: ascending idx, log g = s - LSE(s), LSE
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < QPW; ++e) {
+    const int q = wave * QPW + e;
+    if (q >= nq) continue;
+    const float lse = C > 0 ? run_m[e] + logf(run_s[e]) : -INFINITY;
+    const int kk = min(k, C);
+    const size_t row = row0 + q;
+    if (lane < kk) {
+      const uint64_t key = top[q][lane];
+      const int mb = key_block(key);
+      int rank = 0;
+      for (int j = 0; j < kk; ++j) rank += key_block(top[q][j]) < mb;
+      idx[row * k + rank] = mb;
+      log_gate[row * k + rank] = key_score(key) - lse;
+    } else if (lane < k) {
+      idx[row * k + lane] = -1;
+      log_gate[row * k + lane] = -INFINITY;
+    }
+    if (lane == 0) score_lse[row] = lse;
+  }
+}
+
 // ---------------------------------------------------------- dispatch ---
 template <typename T, int D, int DS, int G>
 struct SelDecode {
@@ -417,6 +622,20 @@ struct SelTiles {
                        d.n_kv_heads, d.t_max / kBlock, rows, d.top_k, idx, log_gate, score_lse,
                        scores);
     return check_launch("select_tiles");
+  }
+};
+
+template <typename T, int D, int DS, int G>
+struct SelQueries {
+  static sas_status run(const sas_dims& d, const void* Q, int q_len, const float* Wq,
+                        const float* summ, int32_t* idx, float* log_gate, float* score_lse,
+                        float* scores, hipStream_t st) {
+    const int n_tiles = cdiv(q_len, kBlock);
+    hipLaunchKernelGGL((select_queries_kernel<T, D, DS, G>), dim3(2 * n_tiles, d.n_kv_heads,
+                       d.batch), dim3(kSelThreads), 0, st, static_cast<const T*>(Q), q_len, Wq,
+                       summ, d.n_kv_heads, d.t_max / kBlock, d.top_k, idx, log_gate, score_lse,
+                       scores);
+    return check_launch("select_queries");
   }
 };
 
@@ -465,6 +684,12 @@ sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, cons
                                const float* summ, int32_t* idx, float* log_gate,
                                float* score_lse, float* scores, hipStream_t st) {
   return by_type<SelTiles>(d, Q, q_len, Wq, summ, idx, log_gate, score_lse, scores, st);
+}
+
+sas_status launch_select_queries(const sas_dims& d, const void* Q, int q_len, const float* Wq,
+                                 const float* summ, int32_t* idx, float* log_gate,
+                                 float* score_lse, float* scores, hipStream_t st) {
+  return by_type<SelQueries>(d, Q, q_len, Wq, summ, idx, log_gate, score_lse, scores, st);
 }
 
 }  // namespace sas

@@ -69,7 +69,7 @@ typedef enum {
 
 typedef enum { SAS_F32 = 0, SAS_BF16 = 1 } sas_dtype;
 
-typedef enum { SAS_SELECT_DECODE = 0, SAS_SELECT_TILES = 1 } sas_select_mode;
+typedef enum { SAS_SELECT_DECODE = 0, SAS_SELECT_TILES = 1, SAS_SELECT_QUERIES = 2 } sas_select_mode;
 
 typedef enum {
   SAS_OP_SELECT_DECODE = 0,
@@ -78,7 +78,9 @@ typedef enum {
   SAS_OP_PREFILL_FWD = 3,
   SAS_OP_BWD = 4,
   SAS_OP_DECODE_STEP = 5,
-  SAS_OP_SELECTOR_BWD = 6
+  SAS_OP_SELECTOR_BWD = 6,
+  SAS_OP_SELECT_QUERIES = 7,
+  SAS_OP_PREFILL_FWD_QUERIES = 8
 } sas_op;
 
 /* Problem sizes.  Supported: block_size 64; head_dim and sel_dim 64 or 128;
@@ -119,9 +121,16 @@ sas_status sas_block_summaries(const sas_dims* dims, const void* K, const int32_
  * mode SAS_SELECT_TILES:  Q is [B,Hq,q_len,d], rows = ceil(q_len/64), row t has
  *   C = t history blocks and averages over its min(64, q_len-64t) queries;
  *   seq_lens may be NULL; q_len <= t_max and rows <= 1024.
+ * mode SAS_SELECT_QUERIES: Q is [B,Hq,q_len,d], rows = q_len, one row per
+ *   query (SAS close reading 2.4: the training kernel masks each query by its
+ *   own gate threshold); row i has C = i/64 history blocks (those before the
+ *   query's own block) and averages over the G heads of query i only, i.e.
+ *   the decode selection of a query at position i; seq_lens may be NULL;
+ *   q_len <= t_max and ceil(q_len/64) <= 1024.
  * scores (nullable): fp32 [B,Hkv,rows,t_max/64]; entry m < C of a row gets s_m.
  * summ must hold the summaries of every block the rows read.
- * ws: at least sas_workspace_bytes(SAS_OP_SELECT_DECODE or _TILES, dims, q_len). */
+ * ws: at least sas_workspace_bytes(SAS_OP_SELECT_DECODE, _TILES or _QUERIES,
+ * dims, q_len). */
 sas_status sas_select(const sas_dims* dims, int32_t mode, const void* Q, int32_t q_len,
                       const int32_t* seq_lens, const float* Wq_sel, const float* summ,
                       int32_t* idx, float* log_gate, float* score_lse, float* scores,
@@ -213,6 +222,23 @@ sas_status sas_prefill_fwd(const sas_dims* dims, const void* Q, const void* K, c
                            int32_t seq_len, const int32_t* idx, const float* log_gate,
                            float scale, void* O, float* lse, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* Causal prefill / training forward with one selection per query (SAS close
+ * reading 2.4: the fused kernel adds log g to the selected blocks' logits
+ * and masks the others by each query's own gate threshold, skipping blocks
+ * that no query of a tile selected): query i attends to the blocks
+ * idx[b,r,i,:] with bias log_gate and to tokens 64*(i/64)..i of its own block
+ * with bias 0, i.e. a decode step at T = i+1.  bf16 only.
+ * Q, O: bf16 [B,Hq,seq_len,d]; K, V: bf16 [B,Hkv,t_max,d] (seq_len <= t_max);
+ * idx/log_gate [B,Hkv,seq_len,k] as written by sas_select(SAS_SELECT_QUERIES)
+ * (ascending, -1 padded, every entry < i/64; log_gate NULL = ungated);
+ * lse: fp32 [B,Hq,seq_len] (natural log); ceil(seq_len/64) <= 1024.
+ * ws: at least sas_workspace_bytes(SAS_OP_PREFILL_FWD_QUERIES, dims, seq_len)
+ * (0 today).  Errors as sas_prefill_fwd. */
+sas_status sas_prefill_fwd_queries(const sas_dims* dims, const void* Q, const void* K,
+                                   const void* V, int32_t seq_len, const int32_t* idx,
+                                   const float* log_gate, float scale, void* O, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of sas_prefill_fwd for L with upstream gradient dO (SAS close
  * reading 2.4 and 2.2 eq. 5; SAS summary, Method): recompute P from lse;

@@ -1,0 +1,180 @@
+"""GPU parity of the per-query selection path against the CPU oracle, through
+the C ABI: sas_block_summaries -> sas_select(QUERIES) -> sas_prefill_fwd_queries.
+
+Per-query selection is the training kernel's own masking rule (SAS close
+reading 2.4: every query is masked by its own gate threshold): query i keeps
+the Top-k of its own scores over the i // 64 blocks before its block, which
+is the decode selection of a query at position i.
+
+The selection is checked row by row against the oracle's query_select (the
+index rule with the near-tie band, log-gate, LSE and the raw scores).  The
+forward gets a selection that does not come from the GPU (the oracle's own
+per-query Top-K on small shapes, a seeded random valid per-query selection at
+full size) and is compared with the oracle's query_attend.  A property that
+holds at any size: when every query carries its tile's selection, the
+per-query forward equals sas_prefill_fwd bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_block_sparse_amd import synth
+from oracle import sas_oracle as O
+from tests.gpu_util import (TOL_F32_OUT, TOL_OUT, check_selection_row, dev, host, idx_dev,
+                            lg_dev, log, needs_gpu)
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+TOL_LSE = 1e-3
+
+
+def _sas():
+    from gated_block_sparse_amd import binding
+    return binding
+
+
+def _problem(S, Hq=4, Hkv=1, d=128, ds=128, k=4, dtype="bf16", seed=0):
+    wl = synth.custom_workload("prefill", n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, sel_dim=ds,
+                               top_k=k, dtype=dtype, seq_len=S)
+    return synth.make_problem(wl, seed)
+
+
+def random_query_selection(rng, Hkv, S, k):
+    """A seeded valid per-query selection: row i holds min(k, i // 64) distinct
+    blocks below i // 64, ascending, -1 padded, with log g < 0."""
+    idx = np.full((Hkv, S, k), -1, np.int64)
+    lg = np.full((Hkv, S, k), -np.inf)
+    for r in range(Hkv):
+        for i in range(S):
+            C = i // 64
+            n = min(k, C)
+            if n:
+                idx[r, i, :n] = np.sort(rng.choice(C, size=n, replace=False))
+                lg[r, i, :n] = -rng.uniform(0.5, 8.0, size=n)
+    return idx, lg
+
+
+def check_select_queries(p, summ_g, queries):
+    """GPU per-query selection vs the oracle on the given queries."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hkv, G, k, dt = int(p.seq_lens[0]), wl.n_kv_heads, wl.group, wl.top_k, wl.dtype
+    idx_g, lg_g, slse_g, sc_g = S_.sas_select(S_.SAS_SELECT_QUERIES, dev(p.q), None,
+                                              dev(p.Wq_sel), summ_g, k, t_max=p.K.shape[2],
+                                              want_scores=True)
+    idx_h, lg_h, slse_h, sc_h = idx_g.cpu().numpy(), host(lg_g), host(slse_g), host(sc_g)
+    Qf, Kf = synth.to_f64(p.q[0], dt), synth.to_f64(p.K[0], dt)
+    ref = O.query_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G, queries=queries)
+    tol = TOL_F32_OUT[dt]
+    n_exact = n_rows = 0
+    for i in queries:
+        C = i // 64
+        for r in range(Hkv):
+            s = ref["scores"][i][r]
+            if C:
+                err = np.abs(sc_h[0, r, i, :C] - s).max()
+                assert err <= tol, (i, r, err)
+                assert abs(slse_h[0, r, i] - ref["score_lse"][r, i]) <= tol, (i, r)
+            else:
+                assert np.isneginf(slse_h[0, r, i])
+            n_exact += check_selection_row(idx_h[0, r, i], lg_h[0, r, i], s, ref["idx"][r, i],
+                                           ref["gap"][r, i], k, ref["score_lse"][r, i], tol)
+            n_rows += 1
+    return idx_g, lg_g, n_exact, n_rows
+
+
+def run_queries_case(p, queries=None, selection="oracle", gated=True, label=""):
+    S_ = _sas()
+    wl = p.wl
+    S, Hq, Hkv, d, k, G = int(p.seq_lens[0]), wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_k, wl.group
+    queries = list(range(S)) if queries is None else sorted(queries)
+    log(f"[queries {label}] S={S} Hq={Hq} Hkv={Hkv} d={d} k={k} {len(queries)} queries checked")
+    Q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    lens = torch.tensor([S], dtype=torch.int32).cuda()
+    summ_g = S_.sas_block_summaries(K, lens, dev(p.Wk_sel))
+    _, _, n_exact, n_rows = check_select_queries(p, summ_g, queries)
+    log(f"[queries {label}] per-query selection exact on {n_exact}/{n_rows} rows")
+
+    Qf, Kf, Vf = (synth.to_f64(x[0], "bf16") for x in (p.q, p.K, p.V))
+    if selection == "oracle":
+        sel = O.query_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        idx, lg = sel["idx"], sel["log_gate"]
+    else:
+        idx, lg = random_query_selection(np.random.default_rng(2024), Hkv, S, k)
+    scale = 1.0 / math.sqrt(d)
+    O_g, lse_g = S_.sas_prefill_fwd_queries(Q, K, V, idx_dev(idx[None]),
+                                            lg_dev(lg[None]) if gated else None)
+    Or, lser = O.query_attend(Qf, Kf, Vf, S, idx, lg, scale, G, gated=gated, queries=queries)
+    O_h, lse_h = host(O_g)[0], host(lse_g)[0]
+    err_o = np.abs(O_h[:, queries] - Or[:, queries]).max()
+    err_l = np.abs(lse_h[:, queries] - lser[:, queries]).max()
+    log(f"[queries {label}] max|O-O_ref|={err_o:.3g} max|lse-lse_ref|={err_l:.3g}")
+    assert err_o <= TOL_OUT["bf16"], err_o
+    assert err_l <= TOL_LSE, err_l
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,ds,k", [
+    (64, 4, 1, 128, 128, 4), (100, 4, 1, 128, 128, 4), (1000, 8, 2, 128, 128, 3),
+    (2048, 8, 2, 128, 128, 16), (777, 2, 2, 64, 128, 5), (640, 8, 1, 128, 64, 4),
+    (700, 16, 2, 64, 64, 6), (1, 4, 1, 128, 128, 2), (1300, 4, 4, 128, 128, 64),
+])
+def test_queries_small(S, Hq, Hkv, d, ds, k):
+    run_queries_case(_problem(S, Hq, Hkv, d, ds, k, seed=S + Hq + 7), label=f"S={S}")
+
+
+def test_queries_ungated_and_k0():
+    run_queries_case(_problem(500, 8, 2, 128, 128, 4, seed=5), gated=False, label="ungated")
+    run_queries_case(_problem(333, 8, 2, 128, 128, 0, seed=6), label="k=0")
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,ds,k", [(900, 4, 1, 64, 64, 8), (300, 8, 2, 128, 128, 5)])
+def test_select_queries_fp32(S, Hq, Hkv, d, ds, k):
+    """The per-query selection on fp32 queries and keys (fp32 tolerances)."""
+    p = _problem(S, Hq, Hkv, d, ds, k, dtype="f32", seed=S)
+    K = dev(p.K)
+    summ_g = _sas().sas_block_summaries(K, torch.tensor([S], dtype=torch.int32).cuda(),
+                                        dev(p.Wk_sel))
+    _, _, n_exact, n_rows = check_select_queries(p, summ_g, list(range(S)))
+    log(f"[queries fp32 S={S}] exact on {n_exact}/{n_rows} rows")
+
+
+def _tile_vs_query_bitwise(p, label):
+    S_ = _sas()
+    wl = p.wl
+    S, Hkv, k = int(p.seq_lens[0]), wl.n_kv_heads, wl.top_k
+    n_tiles = -(-S // 64)
+    rng = np.random.default_rng(99)
+    idx_t = np.full((Hkv, n_tiles, k), -1, np.int64)
+    lg_t = np.full((Hkv, n_tiles, k), -np.inf)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            n = min(k, t)
+            if n:
+                idx_t[r, t, :n] = np.sort(rng.choice(t, size=n, replace=False))
+                lg_t[r, t, :n] = -rng.uniform(0.5, 8.0, size=n)
+    tile_of = np.arange(S) // 64
+    idx_q, lg_q = idx_t[:, tile_of], lg_t[:, tile_of]
+    Q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    O_t, lse_t = S_.sas_prefill_fwd(Q, K, V, idx_dev(idx_t[None]), lg_dev(lg_t[None]))
+    O_q, lse_q = S_.sas_prefill_fwd_queries(Q, K, V, idx_dev(idx_q[None]), lg_dev(lg_q[None]))
+    torch.cuda.synchronize()
+    log(f"[queries {label}] tile-selection broadcast: O equal={torch.equal(O_t, O_q)} "
+        f"lse equal={torch.equal(lse_t, lse_q)}")
+    assert torch.equal(O_t, O_q) and torch.equal(lse_t, lse_q)
+
+
+def test_queries_equal_tile_forward_small():
+    _tile_vs_query_bitwise(_problem(1024, 8, 2, 128, 128, 5, seed=11), "S=1024")
+    _tile_vs_query_bitwise(_problem(640, 4, 1, 64, 64, 3, seed=12), "S=640 d=64")
+
+
+@pytest.mark.timeout(900)
+def test_queries_full_workload():
+    """The training-style workload (S=16384, Qwen3-4B head shape, k=16): the
+    per-query selection on sampled queries (first, tile edges, last), the
+    forward with a random per-query selection on those queries, and the
+    bitwise equality with the tile forward under a broadcast tile selection."""
+    p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
+    queries = [0, 1, 63, 64, 65, 1023, 1024, 1087, 4095, 8200, 12345, 16320, 16383]
+    run_queries_case(p, queries=queries, selection="random", label="qwen3_4b_prefill_16k")
+    _tile_vs_query_bitwise(p, "qwen3_4b_prefill_16k")
