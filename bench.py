@@ -412,6 +412,25 @@ def prefill_pairs(S, G_heads, idx_h):
     return total
 
 
+def query_pairs(S, G_heads, qidx):
+    """Per-query selection: causally visible selected (query, key) pairs and
+    the pairs the forward visits (each tile's queries against the union of
+    their selected blocks, plus the causal diagonal), summed over query heads."""
+    Hkv = qidx.shape[1]
+    sel = vis = 0
+    for r in range(Hkv):
+        rows = qidx[0, r]
+        nsel = (rows >= 0).sum(axis=1)
+        for t in range(-(-S // 64)):
+            i0, i1 = 64 * t, min(64 * t + 64, S)
+            nq = i1 - i0
+            diag = nq * (nq + 1) // 2
+            u = np.unique(rows[i0:i1][rows[i0:i1] >= 0]).size
+            sel += G_heads * (int(nsel[i0:i1].sum()) * 64 + diag)
+            vis += G_heads * (u * 64 * nq + diag)
+    return sel, vis
+
+
 def run_prefill(args, wl):
     import torch
     from gated_block_sparse_amd import binding as Sb
@@ -506,8 +525,30 @@ def run_prefill(args, wl):
         e1.record(stream)
         torch.cuda.synchronize()
         t_sink.append(e0.elapsed_time(e1) * 1e3)
+    # one selection per query (the training kernel's own masking rule): the
+    # per-query selection, then the forward over the union of each tile's
+    # per-query selections with a per-query mask
+    qidx, qlg, qlse, _ = Sb.sas_select(Sb.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S)
+    Oq, lseq = Sb.sas_prefill_fwd_queries(Q, K, V, qidx, qlg)
+    t_qsel, t_qfwd = [], []
+    for i in range(n):
+        if not args.no_flush:
+            flush(i)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        Sb.sas_select(Sb.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S, idx=qidx,
+                      log_gate=qlg, score_lse=qlse)
+        e1.record(stream)
+        Sb.sas_prefill_fwd_queries(Q, K, V, qidx, qlg, O=Oq, lse=lseq)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        t_qsel.append(e0.elapsed_time(e1) * 1e3)
+        t_qfwd.append(e1.elapsed_time(e2) * 1e3)
+    qsel_pairs, qvis_pairs = query_pairs(S, Hq // Hkv, qidx.cpu().numpy())
+
     med = statistics.median
     us_fwd, us_bwd, us_step = med(t_fwd), med(t_bwd), med(tot)
+    us_qfwd = med(t_qfwd)
     fwd_tf = fwd_flop / (us_fwd * 1e-6) / 1e12
     bwd_tf = bwd_flop / (us_bwd * 1e-6) / 1e12
     res = {
@@ -528,6 +569,16 @@ def run_prefill(args, wl):
             "bwd": {"median": round(us_bwd, 2), "p10": round(_pct(t_bwd, .1), 2), "p90": round(_pct(t_bwd, .9), 2)},
             "selector_bwd": {"median": round(med(t_sb), 2), "p10": round(_pct(t_sb, .1), 2), "p90": round(_pct(t_sb, .9), 2)},
             "bwd_sink_heavy_selection": {"median": round(med(t_sink), 2), "p10": round(_pct(t_sink, .1), 2), "p90": round(_pct(t_sink, .9), 2)},
+            "per_query_select": {"median": round(med(t_qsel), 2), "p10": round(_pct(t_qsel, .1), 2), "p90": round(_pct(t_qsel, .9), 2)},
+            "per_query_fwd": {"median": round(us_qfwd, 2), "p10": round(_pct(t_qfwd, .1), 2), "p90": round(_pct(t_qfwd, .9), 2)},
+        },
+        "per_query": {
+            "selected_pairs": qsel_pairs, "visited_pairs": qvis_pairs,
+            "fwd_TFLOPs_selected": round(4.0 * d * qsel_pairs / (us_qfwd * 1e-6) / 1e12, 1),
+            "fwd_TFLOPs_visited": round(4.0 * d * qvis_pairs / (us_qfwd * 1e-6) / 1e12, 1),
+            "note": "selected = the causally visible (query, key) pairs each query selected "
+                    "(algorithmic); visited = the pairs the kernel multiplies: every query "
+                    "of a tile against the union of the tile's selections",
         },
         "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
         "bwd_TFLOPs": round(bwd_tf, 1),

@@ -55,11 +55,12 @@ Sources are cited by page and section; the short names are:
    carries ``ds`` to ``Wq_sel`` and ``Wk_sel``.  The selector's own chain into
    the backbone's Q and K is not formed: the backbone is held fixed while the
    selector trains.
-9. Per-query selection (a next row, oracle only; SAS close reading 2.4: the
-   training kernel masks unselected blocks by each query's own gate
-   threshold): query i of a prefill has its own scores over its C_i = i // b
-   history blocks (step 3 with the query alone), its own gate and Top-K, and
-   attends like a decode query at position i.
+9. Per-query selection (a next row; SAS close reading 2.4: the training
+   kernel masks unselected blocks by each query's own gate threshold): query
+   i of a prefill has its own scores over its C_i = i // b history blocks
+   (step 3 with the query alone), its own gate and Top-K, and attends like a
+   decode query at position i.  Its backward is step 7 on the query's own
+   token set, with one log-gate gradient per (query, slot).
 
 Every stage is its own function so a test can feed one stage's inputs
 independently of the others.  All arithmetic is float64 NumPy; loops are kept
@@ -515,6 +516,68 @@ def query_attend(Q, K, V, S, idx, log_gate, scale, G, b=BLOCK, gated=True, queri
         o, l = decode_attend(Q[:, i], K, V, i + 1, idx[:, i], log_gate[:, i], scale, G, b, gated)
         O[:, i], lse[:, i] = o, l
     return O, lse
+
+
+def _query_tokens(i, idx_row, lg_row, b):
+    """Token set of query i under per-query selection: its own block up to i
+    (bias 0, slot -1), then the tokens of its selected blocks (bias log g,
+    the block's slot)."""
+    j0 = b * (i // b)
+    toks = list(range(j0, i + 1))
+    bias = [0.0] * len(toks)
+    slots = [-1] * len(toks)
+    for slot, (m, lgm) in enumerate(zip(idx_row, lg_row)):
+        if m >= 0:
+            toks.extend(range(b * int(m), b * int(m) + b))
+            bias.extend([float(lgm)] * b)
+            slots.extend([slot] * b)
+    return toks, np.asarray(bias), np.asarray(slots)
+
+
+def _slot_sums(dz, slots, k):
+    """Sum of the logit gradients over the tokens of each selected slot (the
+    query's own block, slot -1, has no gate)."""
+    out = np.zeros(k)
+    for slot in range(k):
+        out[slot] = dz[slots == slot].sum()
+    return out
+
+
+def query_backward(Q, K, V, dO, S, idx, log_gate, scale, G, b=BLOCK, queries=None):
+    """Gradients of L = <dO, O> for query_attend (gated): step 7 on each
+    query's own token set.  With p the softmax row of query i and head h,
+    D = do . o, dz = p (do . v_j - D), dq = scale dz K_S, dk_j += scale dz_j q,
+    dv_j += p_j do, and the log-gate gradient of query i's slot is the sum of
+    dz over that block's tokens and the group's heads (the gates are per
+    query, so the sum runs over one query only).
+
+    Q, dO: [Hq, >=S, d]; K, V: [Hkv, >=S, d]; idx, log_gate: [Hkv, S, k].
+    Returns dQ [Hq,S,d], dK [Hkv,S,d], dV [Hkv,S,d], dlog_gate [Hkv,S,k]
+    (zero on empty slots).  With ``queries``, only the terms of those queries
+    are accumulated."""
+    Hq, _, d = Q.shape
+    Hkv = K.shape[0]
+    k = idx.shape[2]
+    dQ = np.zeros((Hq, S, d))
+    dK = np.zeros((Hkv, S, d))
+    dV = np.zeros((Hkv, S, d))
+    dlg = np.zeros((Hkv, S, k))
+    for i in (range(S) if queries is None else queries):
+        for h in range(Hq):
+            r = h // G
+            toks, bias, slots = _query_tokens(i, idx[r, i], log_gate[r, i], b)
+            Ks, Vs = K[r, toks], V[r, toks]
+            z = Ks @ Q[h, i] * scale + bias
+            e = np.exp(z - z.max())
+            p = e / e.sum()
+            o = p @ Vs
+            D = float(dO[h, i] @ o)
+            dz = p * (Vs @ dO[h, i] - D)
+            dQ[h, i] += scale * dz @ Ks
+            np.add.at(dK[r], toks, scale * np.outer(dz, Q[h, i]))
+            np.add.at(dV[r], toks, np.outer(p, dO[h, i]))
+            dlg[r, i] += _slot_sums(dz, slots, k)
+    return dQ, dK, dV, dlg
 
 
 # --------------------------------------------------------------------------

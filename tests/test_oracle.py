@@ -618,6 +618,89 @@ def check_query_scores_vs_tiles(seed=33):
         assert np.abs(rows_q[i] - rows_t[i // b]).max(initial=0.0) < 1e-12
 
 
+def _random_query_selection(rng, Hkv, S, b, k):
+    idx = np.full((Hkv, S, k), -1, np.int64)
+    lg = np.full((Hkv, S, k), -np.inf)
+    for r in range(Hkv):
+        for i in range(S):
+            n = min(k, i // b)
+            if n:
+                idx[r, i, :n] = np.sort(rng.choice(i // b, size=n, replace=False))
+                lg[r, i, :n] = -rng.uniform(0.2, 3.0, size=n)
+    return idx, lg
+
+
+def _query_loss(Q, K, V, dO, S, idx, lg, scale, G, b):
+    Oq, _ = O.query_attend(Q, K, V, S, idx, lg, scale, G, b)
+    return float(np.sum(Oq[:, :S] * dO[:, :S]))
+
+
+def check_query_backward_fd(seed=34):
+    """Per-query backward against central differences of L = <dO, O>: every
+    log-gate entry of every query, and sampled entries of Q, K and V."""
+    S, b, Hq, Hkv, d, k, scale = 22, 4, 4, 2, 3, 2, 0.43
+    G = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal(sh) for sh in ((Hq, S, d), (Hkv, S, d), (Hkv, S, d)))
+    dO = rng.standard_normal((Hq, S, d))
+    idx, lg = _random_query_selection(rng, Hkv, S, b, k)
+    dQ, dK, dV, dlg = O.query_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    h = 1e-6
+    fd = np.zeros_like(dlg)
+    for r, i, sl in zip(*np.nonzero(idx >= 0)):
+        lp, lm = lg.copy(), lg.copy()
+        lp[r, i, sl] += h
+        lm[r, i, sl] -= h
+        fd[r, i, sl] = (_query_loss(Q, K, V, dO, S, idx, lp, scale, G, b) -
+                        _query_loss(Q, K, V, dO, S, idx, lm, scale, G, b)) / (2 * h)
+    assert np.abs(fd).max() > 1e-3
+    np.testing.assert_allclose(dlg, fd, atol=1e-6 * np.abs(fd).max(), rtol=1e-6)
+    assert (dlg[idx < 0] == 0).all()
+    for name, X, grad in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+        for _ in range(12):
+            pos = tuple(int(rng.integers(0, n)) for n in X.shape)
+            Xp, Xm = X.copy(), X.copy()
+            Xp[pos] += h
+            Xm[pos] -= h
+            args_p = {"Q": Q, "K": K, "V": V}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = Xp, Xm
+            fdx = (_query_loss(args_p["Q"], args_p["K"], args_p["V"], dO, S, idx, lg, scale, G, b) -
+                   _query_loss(args_m["Q"], args_m["K"], args_m["V"], dO, S, idx, lg, scale, G, b)) / (2 * h)
+            assert abs(fdx - grad[pos]) <= 1e-6 * max(1.0, abs(fdx)), (name, pos, fdx, grad[pos])
+
+
+def check_query_backward_vs_tiles(seed=35):
+    """Queries that carry their tile's selection: the per-query backward gives
+    the tile backward's dQ, dK and dV, and its per-query log-gate gradients
+    sum over each tile's queries to the tile's."""
+    S, b, Hq, Hkv, d, k, scale = 45, 8, 4, 2, 5, 3, 0.31
+    G = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal(sh) for sh in ((Hq, S, d), (Hkv, S, d), (Hkv, S, d)))
+    dO = rng.standard_normal((Hq, S, d))
+    n_tiles = -(-S // b)
+    idx_t, lg_t = _random_selection(rng, Hkv, n_tiles, k)
+    tile_of = np.arange(S) // b
+    qQ, qK, qV, qlg = O.query_backward(Q, K, V, dO, S, idx_t[:, tile_of], lg_t[:, tile_of],
+                                       scale, G, b)
+    tQ, tK, tV, tlg = O.prefill_backward(Q, K, V, dO, S, idx_t, lg_t, scale, G, b)
+    for a, c in ((qQ, tQ), (qK, tK), (qV, tV)):
+        assert np.abs(a - c).max() < 1e-12
+    summed = np.zeros_like(tlg)
+    for i in range(S):
+        summed[:, i // b] += qlg[:, i]
+    assert np.abs(summed - tlg).max() < 1e-12
+
+
+def test_query_backward_matches_finite_differences():
+    check_query_backward_fd()
+
+
+def test_query_backward_reduces_to_tile_backward():
+    check_query_backward_vs_tiles()
+
+
 def test_query_selection_is_dense_when_k_covers_history():
     check_query_selection_dense()
 
@@ -635,7 +718,7 @@ PINS = [check_hand_worked, check_topk_lexsort, check_topk_exhaustive, check_gath
         check_uniform_gate_is_dense_with_bias, check_k0_is_local_causal, check_dlog_gate_fd,
         check_qkv_grads_fd, check_summaries, check_selector_score_grad_fd,
         check_selector_weights_fd, check_query_selection_dense, check_query_k0_local,
-        check_query_scores_vs_tiles]
+        check_query_scores_vs_tiles, check_query_backward_fd, check_query_backward_vs_tiles]
 
 
 def _some_pin_fails():
@@ -665,7 +748,7 @@ def _summaries_sum_not_mean(K, T, Wk, b=O.BLOCK):
 
 _ORIG = {"gate": O.gate, "topk": O.topk, "block_summaries": O.block_summaries,
          "_selected_tokens": O._selected_tokens, "score_grad": O.score_grad,
-         "query_scores": O.query_scores}
+         "query_scores": O.query_scores, "_slot_sums": O._slot_sums}
 
 
 def _query_history_includes_own_block(Q, S, Wq, summ, G, b=O.BLOCK, queries=None):
@@ -686,6 +769,14 @@ def _score_grad_no_normaliser(s, idx_row, dlg_row):
     return out
 
 
+def _slot_sums_with_own_block(dz, slots, k):
+    """Credits the query's own block (no gate) to its first slot as well."""
+    out = _ORIG["_slot_sums"](dz, slots, k)
+    if k:
+        out[0] += dz[slots == -1].sum()
+    return out
+
+
 def _drop_gate_bias(idx_row, lg_row, b, gated):
     return _ORIG["_selected_tokens"](idx_row, lg_row, b, False)
 
@@ -703,6 +794,7 @@ def _off_by_one_block(idx_row, lg_row, b, gated):
     ("_selected_tokens", _off_by_one_block),
     ("score_grad", _score_grad_no_normaliser),
     ("query_scores", _query_history_includes_own_block),
+    ("_slot_sums", _slot_sums_with_own_block),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
