@@ -21,8 +21,8 @@ SAS_OK, SAS_ERR_INVALID_ARGUMENT, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE_TOO_SMA
 SAS_F32, SAS_BF16 = 0, 1
 SAS_SELECT_DECODE, SAS_SELECT_TILES, SAS_SELECT_QUERIES = 0, 1, 2
 (SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD,
- SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD, SAS_OP_SELECT_QUERIES,
- SAS_OP_PREFILL_FWD_QUERIES) = range(9)
+ SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD, SAS_OP_SELECT_QUERIES, SAS_OP_PREFILL_FWD_QUERIES,
+ SAS_OP_BWD_QUERIES) = range(10)
 BLOCK = 64
 SIZE_MAX = 2 ** 64 - 1
 
@@ -55,6 +55,8 @@ _SIGNATURES = {
                                        _sz, _vp]),
     "sas_bwd": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
                        _vp, _vp, _sz, _vp]),
+    "sas_bwd_queries": (_i32, [_PD, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
+                               _vp, _vp, _vp, _sz, _vp]),
     "sas_selector_bwd": (_i32, [_PD, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _sz, _vp]),
     "sas_workspace_bytes": (_sz, [_i32, _PD, _i32]),
@@ -361,6 +363,29 @@ def sas_bwd(Q, K, V, O, dO, lse, idx, log_gate, scale=None, seq_len=None, dQ=Non
                                   _ptr(lse), seq_len, _ptr(idx), _ptr(log_gate), scale, _ptr(dQ),
                                   _ptr(dK), _ptr(dV), _ptr(dlog_gate), _ptr(ws), ws_bytes,
                                   _stream()))
+    return dQ, dK, dV, dlog_gate
+
+
+def sas_bwd_queries(Q, K, V, O, dO, lse, idx, log_gate, scale=None, seq_len=None, dQ=None,
+                    dK=None, dV=None, dlog_gate=None, ws=None):
+    """Backward of sas_prefill_fwd_queries (idx/log_gate [B,Hkv,S,k]).
+    Returns (dQ, dK, dV, dlog_gate [B,Hkv,S,k])."""
+    B, Hq, S, d = Q.shape
+    _, Hkv, t_max, _ = K.shape
+    seq_len = S if seq_len is None else seq_len
+    k = idx.shape[-1]
+    dims = make_dims(B, Hq, Hkv, d, 64, k, t_max, _dtype_code(Q))
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.zeros_like(K) if dK is None else dK
+    dV = torch.zeros_like(V) if dV is None else dV
+    if dlog_gate is None:
+        dlog_gate = torch.empty(idx.shape, dtype=torch.float32, device=Q.device)
+    ws, ws_bytes = _workspace(SAS_OP_BWD_QUERIES, dims, seq_len, ws, Q.device)
+    _check(load_library().sas_bwd_queries(ctypes.byref(dims), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                          _ptr(dO), _ptr(lse), seq_len, _ptr(idx),
+                                          _ptr(log_gate), scale, _ptr(dQ), _ptr(dK), _ptr(dV),
+                                          _ptr(dlog_gate), _ptr(ws), ws_bytes, _stream()))
     return dQ, dK, dV, dlog_gate
 
 

@@ -22,11 +22,20 @@
 //     d = 64 one wave per head owns all 64 tokens (bwd_dkdv_kernel).  It is
 //     the only writer of dK/dV for its block and of the dlog_gate entries
 //     that point at it, which it sums in a fixed order.
+#include <climits>
+
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_mfma.h"
 
 namespace sas {
+
+// Per-query selection: union bitmaps of 32 words (blocks < 1024) and the
+// number of gate rows per (sequence, group) (see bwd_qsel_prep_kernel).
+constexpr int kUnionWords = kMaxTileRows / 32;
+__host__ __device__ inline size_t qsel_rows(int n_tiles) {
+  return 1 + static_cast<size_t>(n_tiles) * (n_tiles - 1) / 2;
+}
 
 // ------------------------------------------------------------ pre-pass ---
 template <int D>
@@ -51,13 +60,20 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, 
 }
 
 // ------------------------------------------------------------ dQ pass ---
-template <int D, int HPW>
+// PQ (one selection per query): the workgroup walks the union of its tile's
+// per-query selections (from the prep bitmap), each lane takes its own
+// query's gate for the block (-inf where the query did not select it) from a
+// cursor into the query's ascending idx row, and at a block its query selected
+// it stores the sum of dS over the block's 64 tokens for its head:
+// part[b,h,i,slot], which bwd_qsel_dlg_kernel sums over the group's heads.
+template <int D, int HPW, bool PQ>
 __global__ void __launch_bounds__(128 * HPW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
               const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv, int G,
               int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
               const float* __restrict__ log_gate, float scale2, float scale,
+              const uint32_t* __restrict__ ubits, float* __restrict__ part,
               uint16_t* __restrict__ dQ) {
   constexpr int NT = 128 * HPW;
   constexpr int KS = D / 16, CT = D / 32;
@@ -65,8 +81,8 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * kRowStride<D>];  // K, row reads
   __shared__ __attribute__((aligned(16))) uint16_t Kt[2][64 * kTrStride<D>];   // K, transpose reads
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * kRowStride<D>];
-  __shared__ int s_blk[kMaxTopK + 1];
-  __shared__ float s_beta[kMaxTopK + 1];
+  __shared__ int s_blk[PQ ? kMaxTileRows + 1 : kMaxTopK + 1];
+  __shared__ float s_beta[PQ ? 1 : kMaxTopK + 1];
   __shared__ int s_nblk;
 
   const int nhc = G / HPW;
@@ -99,8 +115,45 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
 
-  // block list: the valid selected blocks (in slot order), then the diagonal
-  if (wave == 0) {
+  // PQ: cursor into the lane's query's ascending selection (next selected
+  // block, its slot and log2-scaled gate; INT_MAX once the row is exhausted)
+  const size_t qsel = PQ ? ((static_cast<size_t>(b) * Hkv + r) * S + (qvalid ? qi : 0)) * k : 0;
+  int cur = 0, nxt = INT_MAX;
+  float nxt_beta = 0.f;
+  auto fetch = [&]() {
+    nxt = INT_MAX;
+    if (qvalid && cur < k) {
+      const int v = idx[qsel + cur];
+      if (v >= 0) {
+        nxt = v;
+        nxt_beta = log_gate ? log_gate[qsel + cur] * kLog2eF : 0.f;
+      }
+    }
+  };
+  if constexpr (PQ) fetch();
+
+  // block list: the valid selected blocks (in slot order), then the diagonal;
+  // PQ: the union of the tile's selections in ascending order
+  if (PQ && wave == 0) {
+    uint32_t w = lane < kUnionWords ? ubits[srow * kUnionWords + lane] : 0u;
+    const int cnt = __popc(w);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int pos = incl - cnt;
+    while (w) {
+      s_blk[pos++] = 32 * lane + (__ffs(w) - 1);
+      w &= w - 1u;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (lane == 0) {
+      s_blk[total] = t;
+      s_nblk = total + 1;
+    }
+  } else if (!PQ && wave == 0) {
     const bool ok = lane < k && idx[srow * k + lane] >= 0;
     const unsigned long long mask = __ballot(ok);
     if (ok) {
@@ -150,7 +203,19 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   for (int it = 0; it < nblk; ++it) {
     const bool diag = it == nblk - 1;
-    const float beta2 = s_beta[it];
+    float beta2;
+    int hit_slot = -1;
+    if constexpr (PQ) {
+      const bool hit = nxt == s_blk[it];
+      beta2 = hit ? nxt_beta : (diag ? 0.f : -INFINITY);
+      if (hit) {
+        hit_slot = cur++;
+        fetch();
+      }
+    } else {
+      beta2 = s_beta[it];
+    }
+    float dsq = 0.f;   // PQ: sum of dS over the block's tokens (this lane's rows)
     const int buf = it & 1;
     if (it + 1 < nblk) load_block(it + 1);   // in flight while this block computes
     const float off = beta2 - lse2;
@@ -178,6 +243,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int v = 0; v < 16; ++v) st[v] = fast_exp2(fmaf(st[v], scale2, off)) * (dp[v] - Dv);
       }
+      if constexpr (PQ) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dsq += st[v];
+      }
       // dQ^T (D x 32 queries) += K^T dS^T over this half's k-steps j = 2tt, 2tt+1
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
@@ -187,6 +256,11 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           dq[ct] = mfma32x32x16(lds_aop_tr_perm<kTrStride<D>>(Kt[buf], 32 * ct, 2 * tt + jj, hi),
                                 bop, dq[ct]);
       }
+    }
+    if constexpr (PQ) {
+      dsq += __shfl_xor(dsq, 32, 64);   // the other 32 token rows of the query
+      if (hit_slot >= 0 && hi == 0)
+        part[((static_cast<size_t>(b) * Hq + h) * S + qi) * k + hit_slot] = dsq;
     }
     if (it + 1 < nblk) store_block(buf ^ 1);
     __syncthreads();
@@ -247,6 +321,126 @@ __device__ int reading_tiles(int m, int n_tiles, int k, const int32_t* __restric
   return *s_count;
 }
 
+// ------------------------------------------- per-query selection prep ---
+// With one selection per query (idx/log_gate [B,Hkv,S,k]) the backward needs,
+// per (sequence, group, tile t): the union of the tile's per-query selections
+// as a bitmap (32 words: blocks < 1024), the exclusive prefix counts of its
+// words (the rank of a block in the union), and one row of 64 base-2 gates
+// per union block: row[q] = log g of query 64t+q for that block, or -inf if
+// the query did not select it.  Rows of tile t start at 1 + t(t-1)/2 (a tile
+// has at most t union blocks); row 0 is all zeros (the diagonal block).
+
+__global__ void __launch_bounds__(256)
+bwd_qsel_prep_kernel(int S, int Hkv, int n_tiles, int k, const int32_t* __restrict__ idx,
+                     const float* __restrict__ log_gate, uint32_t* __restrict__ ubits,
+                     int* __restrict__ ucnt, float* __restrict__ table) {
+  __shared__ uint32_t bits[kUnionWords];
+  __shared__ int cnt[kUnionWords];
+  const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const size_t grow = static_cast<size_t>(b) * Hkv + r;
+  const size_t qrow0 = grow * S + static_cast<size_t>(t) * 64;
+  const int n_ent = min(64, S - 64 * t) * k;
+  float* tab = table + grow * qsel_rows(n_tiles) * 64;
+  if (tid < kUnionWords) bits[tid] = 0u;
+  if (t == 0 && tid < 64) tab[tid] = 0.f;   // row 0: the diagonal block's zero gates
+  __syncthreads();
+  for (int e = tid; e < n_ent; e += 256) {
+    const int m = idx[qrow0 * k + e];
+    if (m >= 0) atomicOr(&bits[m >> 5], 1u << (m & 31));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const uint32_t w = tid < kUnionWords ? bits[tid] : 0u;
+    int incl = __popc(w);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += v;
+    }
+    if (tid < kUnionWords) {
+      cnt[tid] = incl - __popc(w);
+      ubits[(grow * n_tiles + t) * kUnionWords + tid] = w;
+      ucnt[(grow * n_tiles + t) * kUnionWords + tid] = incl - __popc(w);
+    }
+  }
+  __syncthreads();
+  const int n_union = cnt[kUnionWords - 1] + __popc(bits[kUnionWords - 1]);
+  float* rows = tab + (1 + static_cast<size_t>(t) * (t - 1) / 2) * 64;
+  for (int i = tid; i < n_union * 64; i += 256) rows[i] = -INFINITY;
+  __syncthreads();
+  for (int e = tid; e < n_ent; e += 256) {
+    const int m = idx[qrow0 * k + e];
+    if (m >= 0) {
+      const int rank = cnt[m >> 5] + __popc(bits[m >> 5] & ((1u << (m & 31)) - 1u));
+      rows[rank * 64 + e / k] = log_gate ? log_gate[qrow0 * k + e] * kLog2eF : 0.f;
+    }
+  }
+}
+
+// dlog_gate[b,r,i,slot] = sum over the G heads of the group, in head order,
+// of the dQ pass's per-(query, head, slot) partials; 0 on empty slots.
+__global__ void __launch_bounds__(256)
+bwd_qsel_dlg_kernel(int S, int Hkv, int G, int k, const int32_t* __restrict__ idx,
+                    const float* __restrict__ part, float* __restrict__ dlg, size_t n) {
+  const size_t x = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (x >= n) return;
+  const int slot = static_cast<int>(x % k);
+  const size_t qi = (x / k) % S, grow = x / (static_cast<size_t>(k) * S);
+  const size_t b = grow / Hkv, r = grow % Hkv;
+  float tot = 0.f;
+  if (idx[x] >= 0)
+    for (int g = 0; g < G; ++g)
+      tot += part[(((b * Hkv + r) * G + g) * S + qi) * k + slot];
+  dlg[x] = tot;
+}
+
+// The readers of key block m under per-query selection: the diagonal tile
+// (gate row 0) first, then every later tile whose union contains m, in
+// ascending order, with the index of the gate row of (tile, m).
+template <int NWV>
+__device__ int reading_tiles_pq(int m, int n_tiles, const uint32_t* __restrict__ ubits,
+                                const int* __restrict__ ucnt, int* list_t, int* list_row,
+                                int* s_count, int* s_wcount) {
+  constexpr int NT = 64 * NWV;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wd = m >> 5;
+  const uint32_t below = (1u << (m & 31)) - 1u;
+  if (tid == 0) {
+    list_t[0] = m;
+    list_row[0] = 0;
+    *s_count = 1;
+  }
+  __syncthreads();
+  for (int base = m + 1; base < n_tiles; base += NT) {
+    const int t = base + tid;
+    int row = -1;
+    if (t < n_tiles) {
+      const uint32_t w = ubits[static_cast<size_t>(t) * kUnionWords + wd];
+      if ((w >> (m & 31)) & 1u)
+        row = 1 + t * (t - 1) / 2 + ucnt[static_cast<size_t>(t) * kUnionWords + wd] +
+              __popc(w & below);
+    }
+    const unsigned long long mask = __ballot(row >= 0);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) s_wcount[wave] = __popcll(mask);
+    __syncthreads();
+    int off = *s_count;
+    for (int w = 0; w < wave; ++w) off += s_wcount[w];
+    if (row >= 0) {
+      list_t[off + before] = t;
+      list_row[off + before] = row;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int add = 0;
+      for (int w = 0; w < NWV; ++w) add += s_wcount[w];
+      *s_count += add;
+    }
+    __syncthreads();
+  }
+  return *s_count;
+}
+
 // --------------------------------------------------------- dK/dV pass ---
 // One workgroup per (key block m, group r, sequence) with up to 4 waves; wave
 // w handles heads w, w + 4, ... of the group and all 64 tokens of the block,
@@ -258,14 +452,18 @@ __device__ int reading_tiles(int m, int n_tiles, int k, const int32_t* __restric
 // yields the A operands of dK^T += Q^T dS and dV^T += dO^T P; the waves never
 // wait for each other between tiles.  dlog_gate partials are summed over
 // waves at the end.
-template <int D, int NWV>
+// PQ (one selection per query): readers from the prep bitmaps, per-query gates
+// from the prep's gate rows (loaded with lse and D), no dlog_gate here.
+template <int D, int NWV, bool PQ>
 __global__ void __launch_bounds__(64 * NWV)
 bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                 const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv,
                 int G, int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
                 const float* __restrict__ log_gate, float scale2, float scale,
-                uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
+                const uint32_t* __restrict__ ubits, const int* __restrict__ ucnt,
+                const float* __restrict__ gtab, uint16_t* __restrict__ dK,
+                uint16_t* __restrict__ dV, float* __restrict__ dlg) {
   constexpr int NT = 64 * NWV;
   constexpr int KS = D / 16, CT = D / 32;
   // One LDS arena: K rows and V rows (row reads), then per wave the 32 query
@@ -282,6 +480,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   __shared__ float dsum_s[NWV][kMaxTileRows];
   __shared__ float lse_w[NWV][64];   // per wave: lse (base 2) and D of the tile's queries
   __shared__ float dq_w[NWV][64];
+  __shared__ float bq_w[PQ ? NWV : 1][64];     // PQ: the queries' base-2 gates
   __shared__ float list_beta[kMaxTileRows];   // log-gate (base 2) of each entry
   __shared__ int s_count;
   __shared__ int s_wcount[NWV];
@@ -296,9 +495,16 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int Hq = Hkv * G;
   const size_t grow = static_cast<size_t>(b) * Hkv + r;
 
-  const int n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
-                                        log_gate ? log_gate + grow * n_tiles * k : nullptr,
-                                        list_t, list_slot, list_beta, &s_count, s_wcount);
+  int n_list;
+  if constexpr (PQ)
+    n_list = reading_tiles_pq<NWV>(m, n_tiles, ubits + grow * n_tiles * kUnionWords,
+                                   ucnt + grow * n_tiles * kUnionWords, list_t, list_slot,
+                                   &s_count, s_wcount);
+  else
+    n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
+                                log_gate ? log_gate + grow * n_tiles * k : nullptr, list_t,
+                                list_slot, list_beta, &s_count, s_wcount);
+  const float* gt = PQ ? gtab + grow * qsel_rows(n_tiles) * 64 : nullptr;
 
   // ---- stage the block's K and V rows (B operands, shared by the waves)
   const int tok0 = 64 * m;
@@ -319,20 +525,21 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // lse and D of the wave's next (entry, head) pair are loaded one pair
   // ahead, so their memory latency overlaps the current pair's work
-  float pre_l = 0.f, pre_d = 0.f;
+  float pre_l = 0.f, pre_d = 0.f, pre_b = 0.f;
   auto fetch_rows = [&](int e2, int g2) {
     const int q2 = 64 * list_t[e2];
     const size_t hrow2 = (static_cast<size_t>(b) * Hq + r * G + g2) * S + q2;
     const bool ok = lane < min(64, S - q2);
     pre_l = ok ? lse[hrow2 + lane] * kLog2eF : 0.f;
     pre_d = ok ? Dq[hrow2 + lane] : 0.f;
+    if constexpr (PQ) pre_b = gt[static_cast<size_t>(list_slot[e2]) * 64 + lane];
   };
   if (wave < G) fetch_rows(0, wave);
 
   for (int e = 0; e < n_list; ++e) {
     const int t = list_t[e];
     const bool diag = e == 0;
-    const float beta2 = list_beta[e];
+    const float beta2 = PQ ? 0.f : list_beta[e];
     const int q0 = 64 * t;
     const int nq = min(64, S - q0);
     float dsum = 0.f;
@@ -340,6 +547,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g) * S + q0;
       lse_w[wave][lane] = pre_l;
       dq_w[wave][lane] = pre_d;
+      if constexpr (PQ) bq_w[wave][lane] = pre_b;
       if (g + NWV < G) fetch_rows(e, g + NWV);
       else if (e + 1 < n_list) fetch_rows(e + 1, wave);
       __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -387,7 +595,8 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
             for (int v = 0; v < 16; ++v) {
               const int q = 32 * qt + acc_row(v, hi);
               const bool ok = tok_ok && q < nq && !(diag && tok > q);
-              const float p = ok ? fast_exp2(fmaf(s[tt][v], scale2, beta2 - lse_w[wave][q])) : 0.f;
+              const float bb = PQ ? bq_w[PQ ? wave : 0][q] : beta2;
+              const float p = ok ? fast_exp2(fmaf(s[tt][v], scale2, bb - lse_w[wave][q])) : 0.f;
               const float ds = p * (dp[tt][v] - dq_w[wave][q]);
               s[tt][v] = p;
               dp[tt][v] = ds;
@@ -399,7 +608,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int q = 32 * qt + acc_row(v, hi);
-            lo[v] = beta2 - lse_w[wave][q];
+            lo[v] = (PQ ? bq_w[PQ ? wave : 0][q] : beta2) - lse_w[wave][q];
             dd[v] = dq_w[wave][q];
           }
 #pragma unroll
@@ -438,7 +647,7 @@ bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   __syncthreads();
   // dlog_gate: one writer per (tile, slot) entry, heads summed in wave order
-  for (int e = 1 + tid; e < n_list; e += NT) {
+  for (int e = 1 + tid; !PQ && e < n_list; e += NT) {
     float tot = 0.f;
     for (int w = 0; w < NWV; ++w) tot += dsum_s[w][e];
     dlg[(grow * n_tiles + list_t[e]) * k + list_slot[e]] = tot;
@@ -520,7 +729,11 @@ constexpr int kTsSlot = 2 * kTsTensor + 64 * 4;      // Q, dO, lse[32], D[32]
 __device__ __forceinline__ int ts_swz(int q) { return 2 * (q & 7) + ((q >> 2) & 1); }
 
 
-template <int G>
+// PQ (one selection per query): the readers come from the prep bitmaps, the
+// gates are per query: wave 1 also copies the step's 32 base-2 gates from the
+// prep's gate row of (tile, block) into the slot (row 0, zeros, for the
+// diagonal tile), and no dlog_gate is formed here (the dQ pass does it).
+template <int G, bool PQ>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -528,9 +741,12 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
                    const float* __restrict__ log_gate, float scale2, float scale, int n_hot,
                    int max_chunks, float* __restrict__ hot_part, int* __restrict__ hot_cnt,
-                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, float* __restrict__ dlg) {
+                   const uint32_t* __restrict__ ubits, const int* __restrict__ ucnt,
+                   const float* __restrict__ gtab, uint16_t* __restrict__ dK,
+                   uint16_t* __restrict__ dV, float* __restrict__ dlg) {
   constexpr int D = 128, NWV = 4, KS = D / 32, CT = D / 16;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kTsSlots * kTsSlot];
+  constexpr int SLOT = kTsSlot + (PQ ? 64 * 4 : 0);   // + the step's gates (PQ)
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kTsSlots * SLOT];
   __shared__ int list_t[kMaxTileRows];
   __shared__ int list_slot[kMaxTileRows];
   __shared__ float list_beta[kMaxTileRows];
@@ -559,9 +775,16 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int Hq = Hkv * G;
   const size_t grow = static_cast<size_t>(b) * Hkv + r;
 
-  const int n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
-                                        log_gate ? log_gate + grow * n_tiles * k : nullptr,
-                                        list_t, list_slot, list_beta, &s_count, s_wcount);
+  int n_list;
+  if constexpr (PQ)
+    n_list = reading_tiles_pq<NWV>(m, n_tiles, ubits + grow * n_tiles * kUnionWords,
+                                   ucnt + grow * n_tiles * kUnionWords, list_t, list_slot,
+                                   &s_count, s_wcount);
+  else
+    n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
+                                log_gate ? log_gate + grow * n_tiles * k : nullptr, list_t,
+                                list_slot, list_beta, &s_count, s_wcount);
+  const float* gt = PQ ? gtab + grow * qsel_rows(n_tiles) * 64 : nullptr;
   // Hot-block chunking: a hot block read by more than kHotCap tiles is split
   // over ceil(n_list / kHotCap) workgroups, chunk c taking entries c, c + nc,
   // c + 2nc, ... (interleaved, so the chunks sweep the tiles together and
@@ -589,7 +812,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int qt2 = sc & 1, g2 = (sc >> 1) % G, e2 = chunk + ((sc >> 1) / G) * n_chunks;
     const int qbase = 64 * list_t[e2] + 32 * qt2;
     const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g2) * S;
-    const uint32_t slot = ring_lds + (s2 % kTsSlots) * kTsSlot;
+    const uint32_t slot = ring_lds + (s2 % kTsSlots) * SLOT;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int row0 = 8 * wave + 4 * n;
@@ -602,6 +825,9 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const float* src = (lane < 32 ? lse : Dq) + hrow + min(qbase + (lane & 31), S - 1);
       lds_dma<4>(src, slot + 2 * kTsTensor);
     }
+    if (PQ && wave == 1)   // gates of the 32 queries (lanes 32..63 repeat them)
+      lds_dma<4>(gt + static_cast<size_t>(list_slot[e2]) * 64 + 32 * qt2 + (lane & 31),
+                 slot + 2 * kTsTensor + 256);
   };
   // ---- K and V rows of the wave's tokens: B operands, k-step ks holds
   // channels 32ks + 8 i4 .. +7 of token 16w + l16 (zero past the sequence)
@@ -649,10 +875,10 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     // this wave's copies for step s are done once at most the copies of
     // kTsSlots - 2 later steps remain; the barrier makes every wave's copies
     // visible and frees the slot read in step s - 1 for the next copy
-    if (wave == 0) dma_sync<5 * (kTsSlots - 2)>();
+    if (wave == 0 || (PQ && wave == 1)) dma_sync<5 * (kTsSlots - 2)>();
     else dma_sync<4 * (kTsSlots - 2)>();
     issue(s + kTsSlots - 1);
-    if (pending >= 1 && tid == 0) {
+    if (!PQ && pending >= 1 && tid == 0) {
       float tot = 0.f;
 #pragma unroll
       for (int w = 0; w < NWV; ++w) tot += red[pslot][w];
@@ -663,9 +889,10 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int jl = (s >> 1) / G;   // the chunk's local entry number
     const int qt = s & 1, g = (s >> 1) % G, e = chunk + jl * n_chunks;
     const bool diag = e == 0;
-    const float beta2 = list_beta[e];
+    const float beta2 = PQ ? 0.f : list_beta[e];
     const int nq = min(64, S - 64 * list_t[e]);
-    const unsigned char* slot = ring + (s % kTsSlots) * kTsSlot;
+    const unsigned char* slot = ring + (s % kTsSlots) * SLOT;
+    const float* bq = reinterpret_cast<const float*>(slot + 2 * kTsTensor + 256);   // PQ gates
     const unsigned char* Qs = slot;
     const unsigned char* Os = slot + kTsTensor;
     const float* ls = reinterpret_cast<const float*>(slot + 2 * kTsTensor);
@@ -697,7 +924,8 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         const int qq = 32 * qt + q;
         const bool ok = tok_ok && qq < nq && !(diag && tok > qq);
         const float p =
-            ok ? fast_exp2(fmaf(sa[qtile][v], scale2, beta2 - ls[q] * kLog2eF)) : 0.f;
+            ok ? fast_exp2(fmaf(sa[qtile][v], scale2, (PQ ? bq[q] : beta2) - ls[q] * kLog2eF))
+               : 0.f;
         const float ds = p * (pa[qtile][v] - ls[32 + q]);
         sa[qtile][v] = p;
         pa[qtile][v] = ds;
@@ -723,7 +951,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       dk[ct] = mfma16x16x32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), sb, dk[ct]);
     }
     // last step of the entry: the wave's dlog_gate partial
-    if (qt == 1 && g == G - 1) {
+    if (!PQ && qt == 1 && g == G - 1) {
       const float w = wave_sum_from(dsum, 1);
       if (lane == 0) red[jl & 1][wave] = w;
       dsum = 0.f;
@@ -732,7 +960,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   }
   dma_sync<0>();
-  if (pending >= 1 && tid == 0) {
+  if (!PQ && pending >= 1 && tid == 0) {
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) tot += red[pslot][w];
@@ -804,16 +1032,52 @@ static size_t hot_part_floats(const sas_dims& d, int n_tiles) {
 }
 static size_t align_up256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// workspace: D [B,Hq,S] fp32 | (d = 128) hot partials | hot chunk counts
-size_t bwd_ws_bytes(const sas_dims& d, int seq_len) {
-  const size_t dq = static_cast<size_t>(d.batch) * d.n_q_heads * seq_len * sizeof(float);
-  if (d.head_dim != 128) return dq;
+// workspace: D [B,Hq,S] fp32 | (d = 128) hot partials | hot chunk counts;
+// per-query selection adds: dlog_gate partials [B,Hq,S,k] fp32 | union bitmaps
+// [B,Hkv,n_tiles,32] | their word prefix counts | gate rows
+// [B,Hkv,1 + n_tiles(n_tiles-1)/2,64] fp32.
+struct BwdWs {
+  size_t dq, hot_part, hot_cnt, part, ubits, ucnt, gtab, total;
+};
+static BwdWs bwd_ws_layout(const sas_dims& d, int seq_len, bool pq) {
+  BwdWs w{};
   const int n_tiles = cdiv(seq_len, kBlock);
-  return align_up256(dq) + align_up256(hot_part_floats(d, n_tiles) * sizeof(float)) +
-         static_cast<size_t>(d.batch) * d.n_kv_heads * hot_blocks(n_tiles) * sizeof(int);
+  const size_t rows = static_cast<size_t>(d.batch) * d.n_q_heads * seq_len;
+  const size_t groups = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  size_t off = 0;
+  w.dq = off;
+  off += rows * sizeof(float);
+  if (d.head_dim == 128) {
+    off = align_up256(off);
+    w.hot_part = off;
+    off += hot_part_floats(d, n_tiles) * sizeof(float);
+    off = align_up256(off);
+    w.hot_cnt = off;
+    off += groups * hot_blocks(n_tiles) * sizeof(int);
+  }
+  if (pq) {
+    off = align_up256(off);
+    w.part = off;
+    off += rows * static_cast<size_t>(d.top_k) * sizeof(float);
+    off = align_up256(off);
+    w.ubits = off;
+    off += groups * n_tiles * kUnionWords * sizeof(uint32_t);
+    off = align_up256(off);
+    w.ucnt = off;
+    off += groups * n_tiles * kUnionWords * sizeof(int);
+    off = align_up256(off);
+    w.gtab = off;
+    off += groups * qsel_rows(n_tiles) * 64 * sizeof(float);
+  }
+  w.total = off;
+  return w;
+}
+size_t bwd_ws_bytes(const sas_dims& d, int seq_len) { return bwd_ws_layout(d, seq_len, false).total; }
+size_t bwd_queries_ws_bytes(const sas_dims& d, int seq_len) {
+  return bwd_ws_layout(d, seq_len, true).total;
 }
 
-template <int D>
+template <int D, bool PQ>
 static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, const void* V,
                                const void* O, const void* dO, const float* lse, int S,
                                const int32_t* idx, const float* log_gate, float scale, void* dQ,
@@ -821,9 +1085,18 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   const int G = d.n_q_heads / d.n_kv_heads;
   const int n_tiles = cdiv(S, kBlock);
   const float scale2 = scale * kLog2eF;
-  float* Dq = static_cast<float*>(ws);
+  const BwdWs lay = bwd_ws_layout(d, S, PQ);
+  char* wsb = static_cast<char*>(ws);
+  float* Dq = reinterpret_cast<float*>(wsb + lay.dq);
+  float* part = PQ ? reinterpret_cast<float*>(wsb + lay.part) : nullptr;
+  uint32_t* ubits = PQ ? reinterpret_cast<uint32_t*>(wsb + lay.ubits) : nullptr;
+  int* ucnt = PQ ? reinterpret_cast<int*>(wsb + lay.ucnt) : nullptr;
+  float* gtab = PQ ? reinterpret_cast<float*>(wsb + lay.gtab) : nullptr;
   const size_t n_rows = static_cast<size_t>(d.batch) * d.n_q_heads * S;
-  const size_t n_dlg = (d.top_k > 0 && dlg) ? static_cast<size_t>(d.batch) * d.n_kv_heads * n_tiles * d.top_k : 0;
+  // the tile backward's dlog_gate entries are zeroed here and written by the
+  // dK/dV pass; the per-query one is written whole by its reduction kernel
+  const size_t n_dlg = (!PQ && d.top_k > 0 && dlg)
+                           ? static_cast<size_t>(d.batch) * d.n_kv_heads * n_tiles * d.top_k : 0;
   const size_t thr = n_rows * (D / 8);
   const int pre_blocks = static_cast<int>((thr + 255) / 256);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_blocks), dim3(256), 0, st,
@@ -831,14 +1104,20 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
                      Dq, dlg, n_dlg);
   sas_status s = check_launch("bwd_pre");
   if (s != SAS_OK) return s;
+  if constexpr (PQ) {
+    hipLaunchKernelGGL(bwd_qsel_prep_kernel, dim3(n_tiles, d.n_kv_heads, d.batch), dim3(256), 0,
+                       st, S, d.n_kv_heads, n_tiles, d.top_k, idx, log_gate, ubits, ucnt, gtab);
+    s = check_launch("bwd_qsel_prep");
+    if (s != SAS_OK) return s;
+  }
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* kk = static_cast<const uint16_t*>(K);
   const uint16_t* v = static_cast<const uint16_t*>(V);
   const uint16_t* dop = static_cast<const uint16_t*>(dO);
-#define SAS_DQ_CASE(HPW)                                                                        \
-  hipLaunchKernelGGL((bwd_dq_kernel<D, HPW>), dim3(n_tiles * (G / HPW), d.n_kv_heads, d.batch), \
-                     dim3(128 * HPW), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G,        \
-                     d.t_max, n_tiles, d.top_k, idx, log_gate, scale2, scale,                   \
+#define SAS_DQ_CASE(HPW)                                                                       \
+  hipLaunchKernelGGL((bwd_dq_kernel<D, HPW, PQ>), dim3(n_tiles * (G / HPW), d.n_kv_heads,       \
+                     d.batch), dim3(128 * HPW), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, \
+                     G, d.t_max, n_tiles, d.top_k, idx, log_gate, scale2, scale, ubits, part,   \
                      static_cast<uint16_t*>(dQ))
   switch (G) {
     case 1: SAS_DQ_CASE(1); break;
@@ -848,17 +1127,23 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
 #undef SAS_DQ_CASE
   s = check_launch("bwd_dq");
   if (s != SAS_OK) return s;
+  if (PQ && d.top_k > 0 && dlg) {
+    const size_t n = static_cast<size_t>(d.batch) * d.n_kv_heads * S * d.top_k;
+    hipLaunchKernelGGL(bwd_qsel_dlg_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
+                       dim3(256), 0, st, S, d.n_kv_heads, G, d.top_k, idx, part, dlg, n);
+    s = check_launch("bwd_qsel_dlg");
+    if (s != SAS_OK) return s;
+  }
   if constexpr (D == 128) {
     const int n_hot = hot_blocks(n_tiles), max_chunks = hot_max_chunks(n_tiles);
-    char* wsb = static_cast<char*>(ws) + align_up256(n_rows * sizeof(float));
-    float* hot_part = reinterpret_cast<float*>(wsb);
-    int* hot_cnt = reinterpret_cast<int*>(wsb + align_up256(hot_part_floats(d, n_tiles) * sizeof(float)));
+    float* hot_part = reinterpret_cast<float*>(wsb + lay.hot_part);
+    int* hot_cnt = reinterpret_cast<int*>(wsb + lay.hot_cnt);
     const int grid_x = (n_hot * max_chunks + (n_tiles - n_hot)) * d.n_kv_heads;
 #define SAS_DKDV_TS(GG)                                                                          \
-  hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG>), dim3(grid_x, 1, d.batch), dim3(256), 0, st, q, kk,  \
-                     v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, d.top_k, idx, log_gate,  \
-                     scale2, scale, n_hot, max_chunks, hot_part, hot_cnt,                        \
-                     static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
+  hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG, PQ>), dim3(grid_x, 1, d.batch), dim3(256), 0, st, q, \
+                     kk, v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, d.top_k, idx,        \
+                     log_gate, scale2, scale, n_hot, max_chunks, hot_part, hot_cnt, ubits, ucnt,  \
+                     gtab, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
     switch (G) {
       case 1: SAS_DKDV_TS(1); break;
       case 2: SAS_DKDV_TS(2); break;
@@ -874,9 +1159,9 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
     return check_launch("bwd_hot_reduce");
   }
 #define SAS_DKDV_CASE(NWV)                                                                     \
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),         \
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, NWV, PQ>), dim3(n_tiles * d.n_kv_heads, 1, d.batch),     \
                      dim3(64 * NWV), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, \
-                     n_tiles, d.top_k, idx, log_gate, scale2, scale,                              \
+                     n_tiles, d.top_k, idx, log_gate, scale2, scale, ubits, ucnt, gtab,           \
                      static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
   switch (G) {
     case 1: SAS_DKDV_CASE(1); break;
@@ -895,10 +1180,24 @@ sas_status launch_bwd(const sas_dims& d, const void* Q, const void* K, const voi
     return fail(SAS_ERR_UNSUPPORTED, "backward: seq_len=%d gives more than %d tiles", seq_len,
                 kMaxTileRows);
   if (d.head_dim == 128)
-    return launch_bwd_d<128>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ, dK, dV,
-                             dlog_gate, ws, st);
-  return launch_bwd_d<64>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ, dK, dV,
-                          dlog_gate, ws, st);
+    return launch_bwd_d<128, false>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ,
+                                    dK, dV, dlog_gate, ws, st);
+  return launch_bwd_d<64, false>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ, dK,
+                                 dV, dlog_gate, ws, st);
+}
+
+sas_status launch_bwd_queries(const sas_dims& d, const void* Q, const void* K, const void* V,
+                              const void* O, const void* dO, const float* lse, int seq_len,
+                              const int32_t* idx, const float* log_gate, float scale, void* dQ,
+                              void* dK, void* dV, float* dlog_gate, void* ws, hipStream_t st) {
+  if (cdiv(seq_len, kBlock) > kMaxTileRows)
+    return fail(SAS_ERR_UNSUPPORTED, "backward: seq_len=%d gives more than %d tiles", seq_len,
+                kMaxTileRows);
+  if (d.head_dim == 128)
+    return launch_bwd_d<128, true>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ,
+                                   dK, dV, dlog_gate, ws, st);
+  return launch_bwd_d<64, true>(d, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ, dK,
+                                dV, dlog_gate, ws, st);
 }
 
 }  // namespace sas

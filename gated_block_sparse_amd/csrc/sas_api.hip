@@ -312,6 +312,32 @@ sas_status sas_bwd(const sas_dims* dims, const void* Q, const void* K, const voi
                     dlog_gate, ws, static_cast<hipStream_t>(stream));
 }
 
+sas_status sas_bwd_queries(const sas_dims* dims, const void* Q, const void* K, const void* V,
+                           const void* O, const void* dO, const float* lse, int32_t seq_len,
+                           const int32_t* idx, const float* log_gate, float scale, void* dQ,
+                           void* dK, void* dV, float* dlog_gate, void* ws, size_t ws_bytes,
+                           void* stream) {
+  SAS_TRY(check_dims(dims, true));
+  SAS_TRY(check_len(dims, seq_len, "seq_len"));
+  SAS_NONNULL(Q);
+  SAS_NONNULL(K);
+  SAS_NONNULL(V);
+  SAS_NONNULL(O);
+  SAS_NONNULL(dO);
+  SAS_NONNULL(lse);
+  SAS_NONNULL(dQ);
+  SAS_NONNULL(dK);
+  SAS_NONNULL(dV);
+  if (dims->top_k > 0) {
+    SAS_NONNULL(idx);
+    SAS_NONNULL(dlog_gate);
+  }
+  if (!(scale > 0.0f)) return fail(SAS_ERR_INVALID_ARGUMENT, "scale must be a positive number");
+  SAS_TRY(check_ws(bwd_queries_ws_bytes(*dims, seq_len), ws, ws_bytes));
+  return launch_bwd_queries(*dims, Q, K, V, O, dO, lse, seq_len, idx, log_gate, scale, dQ, dK,
+                            dV, dlog_gate, ws, static_cast<hipStream_t>(stream));
+}
+
 sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, const void* K,
                             const float* Wq_sel, const float* summ, const int32_t* idx,
                             const float* score_lse, const float* dlog_gate, float* ds,
@@ -338,8 +364,8 @@ sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, 
 }
 
 size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
-  const bool bf16_only =
-      (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD || op == SAS_OP_PREFILL_FWD_QUERIES);
+  const bool bf16_only = (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD ||
+                          op == SAS_OP_PREFILL_FWD_QUERIES || op == SAS_OP_BWD_QUERIES);
   if (check_dims(dims, bf16_only) != SAS_OK) return SIZE_MAX;
   switch (op) {
     case SAS_OP_SELECT_DECODE: return select_decode_ws_bytes(*dims);
@@ -359,6 +385,9 @@ size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
     case SAS_OP_BWD:
       if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
       return bwd_ws_bytes(*dims, q_len);
+    case SAS_OP_BWD_QUERIES:
+      if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
+      return bwd_queries_ws_bytes(*dims, q_len);
     default:
       fail(SAS_ERR_INVALID_ARGUMENT, "op=%d is not a sas_op", op);
       return SIZE_MAX;

@@ -134,5 +134,11 @@ sas_status launch_bwd(const sas_dims& d, const void* Q, const void* K, const voi
                       const void* O, const void* dO, const float* lse, int seq_len,
                       const int32_t* idx, const float* log_gate, float scale, void* dQ,
                       void* dK, void* dV, float* dlog_gate, void* ws, hipStream_t st);
+// The same with one selection per query: idx/log_gate/dlog_gate [B,Hkv,seq_len,k].
+size_t bwd_queries_ws_bytes(const sas_dims& d, int seq_len);
+sas_status launch_bwd_queries(const sas_dims& d, const void* Q, const void* K, const void* V,
+                              const void* O, const void* dO, const float* lse, int seq_len,
+                              const int32_t* idx, const float* log_gate, float scale, void* dQ,
+                              void* dK, void* dV, float* dlog_gate, void* ws, hipStream_t st);
 
 }  // namespace sas

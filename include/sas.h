@@ -80,7 +80,8 @@ typedef enum {
   SAS_OP_DECODE_STEP = 5,
   SAS_OP_SELECTOR_BWD = 6,
   SAS_OP_SELECT_QUERIES = 7,
-  SAS_OP_PREFILL_FWD_QUERIES = 8
+  SAS_OP_PREFILL_FWD_QUERIES = 8,
+  SAS_OP_BWD_QUERIES = 9
 } sas_op;
 
 /* Problem sizes.  Supported: block_size 64; head_dim and sel_dim 64 or 128;
@@ -256,6 +257,25 @@ sas_status sas_bwd(const sas_dims* dims, const void* Q, const void* K, const voi
                    const void* O, const void* dO, const float* lse, int32_t seq_len,
                    const int32_t* idx, const float* log_gate, float scale, void* dQ, void* dK,
                    void* dV, float* dlog_gate, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of sas_prefill_fwd_queries (one selection per query; SAS close
+ * reading 2.4 and 2.2 eq. 5): as sas_bwd with each query's own token set,
+ * and one log-gate gradient per query and slot:
+ *     dlog_gate[b,r,i,slot] = sum over the heads of r and the tokens of block
+ *                             idx[b,r,i,slot] of dS of query i.
+ * Empty slots get 0.  Q, O, dO, dQ: bf16 [B,Hq,seq_len,d]; K, V, dK, dV: bf16
+ * [B,Hkv,t_max,d] (rows >= seq_len of dK/dV are not written); lse fp32
+ * [B,Hq,seq_len]; idx/log_gate/dlog_gate [B,Hkv,seq_len,k] (idx as for
+ * sas_prefill_fwd_queries); ceil(seq_len/64) <= 1024.
+ * ws: at least sas_workspace_bytes(SAS_OP_BWD_QUERIES, dims, seq_len): that of
+ * sas_bwd plus per-head log-gate partials (B*Hq*seq_len*k floats) and per-tile
+ * union bitmaps and gate rows (B*Hkv*(1 + n(n-1)/2)*64 floats, n the number
+ * of 64-query tiles).  Errors as sas_bwd. */
+sas_status sas_bwd_queries(const sas_dims* dims, const void* Q, const void* K, const void* V,
+                           const void* O, const void* dO, const float* lse, int32_t seq_len,
+                           const int32_t* idx, const float* log_gate, float scale, void* dQ,
+                           void* dK, void* dV, float* dlog_gate, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /* Backward of the selector into its weights, for the tile rows of a prefill
  * (SAS close reading 2.2, gate equation; 2.3, eq. 8, sparse scope; 2.4 and

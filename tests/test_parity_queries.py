@@ -21,8 +21,8 @@ import torch
 
 from gated_block_sparse_amd import synth
 from oracle import sas_oracle as O
-from tests.gpu_util import (TOL_F32_OUT, TOL_OUT, check_selection_row, dev, host, idx_dev,
-                            lg_dev, log, needs_gpu)
+from tests.gpu_util import (TOL_F32_OUT, TOL_GRAD_REL, TOL_OUT, check_selection_row, dev, host,
+                            idx_dev, lg_dev, log, needs_gpu)
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 TOL_LSE = 1e-3
@@ -178,3 +178,126 @@ def test_queries_full_workload():
     queries = [0, 1, 63, 64, 65, 1023, 1024, 1087, 4095, 8200, 12345, 16320, 16383]
     run_queries_case(p, queries=queries, selection="random", label="qwen3_4b_prefill_16k")
     _tile_vs_query_bitwise(p, "qwen3_4b_prefill_16k")
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def run_queries_bwd_case(p, queries=None, selection="oracle", label=""):
+    """sas_bwd_queries on the per-query forward's outputs vs the oracle's
+    query_backward.  With sampled queries, dQ and dlog_gate are compared on
+    those queries and dK/dV through identities that hold at any size."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hq, Hkv, d, k, G = int(p.seq_lens[0]), wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.top_k, wl.group
+    full = queries is None
+    queries = list(range(S)) if full else sorted(queries)
+    log(f"[queries bwd {label}] S={S} Hq={Hq} Hkv={Hkv} d={d} k={k} {len(queries)} queries checked")
+    Q, K, V, dO = dev(p.q), dev(p.K), dev(p.V), dev(p.dO)
+    Qf, Kf, Vf, dOf = (synth.to_f64(x[0], "bf16") for x in (p.q, p.K, p.V, p.dO))
+    if selection == "oracle":
+        sel = O.query_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        idx, lg = sel["idx"], sel["log_gate"]
+    else:
+        idx, lg = random_query_selection(np.random.default_rng(77), Hkv, S, k)
+    idx_d, lg_d = idx_dev(idx[None]), lg_dev(lg[None])
+    O_g, lse_g = S_.sas_prefill_fwd_queries(Q, K, V, idx_d, lg_d)
+    dQ, dK, dV, dlg = S_.sas_bwd_queries(Q, K, V, O_g, dO, lse_g, idx_d, lg_d)
+    scale = 1.0 / math.sqrt(d)
+    rQ, rK, rV, rlg = O.query_backward(Qf, Kf, Vf, dOf, S, idx, lg, scale, G,
+                                       queries=None if full else queries)
+    gQ, gK, gV, glg = host(dQ)[0], host(dK)[0][:, :S], host(dV)[0][:, :S], host(dlg)[0]
+    floor = 1e-2 * np.linalg.norm(dOf[:, queries])
+
+    def rel_l2(x, ref):
+        return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), floor))
+
+    e_q = rel_l2(gQ[:, queries], rQ[:, queries])
+    valid = np.zeros_like(idx, bool)
+    valid[:, queries] = idx[:, queries] >= 0
+    e_lg = 0.0
+    if valid.any():
+        e_lg = float(np.linalg.norm(glg[valid] - rlg[valid]) / max(np.linalg.norm(rlg[valid]), 1e-30))
+    assert (glg[idx < 0] == 0).all()
+    msg = f"[queries bwd {label}] rel dQ={e_q:.3g} dlog_gate={e_lg:.3g}"
+    if full:
+        e_k, e_v = rel_l2(gK, rK), rel_l2(gV, rV)
+        msg += f" dK={e_k:.3g} dV={e_v:.3g}"
+        assert max(e_k, e_v) <= TOL_GRAD_REL
+    # identities at any size: sum_j dV_j = sum over the group's rows of dO
+    # (softmax rows sum to 1), sum_j dK_j = 0 (shifting every key leaves each
+    # softmax row unchanged)
+    # (exactly 0: its GPU value is rounding residue, hence the absolute slack)
+    for r in range(Hkv):
+        so = dOf[r * G:(r + 1) * G, :S].sum(axis=(0, 1))
+        assert np.linalg.norm(gV[r].sum(axis=0) - so) <= TOL_GRAD_REL * max(np.linalg.norm(so), floor)
+        assert np.linalg.norm(gK[r].sum(axis=0)) <= TOL_GRAD_REL * np.linalg.norm(gK[r]) + 1e-3
+    log(msg)
+    assert max(e_q, e_lg) <= TOL_GRAD_REL
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,k", [
+    (64, 4, 1, 128, 4), (100, 4, 1, 128, 4), (1000, 8, 2, 128, 3), (777, 2, 2, 64, 5),
+    (700, 16, 2, 64, 6), (1, 4, 1, 128, 2), (900, 4, 4, 128, 64), (640, 8, 1, 128, 16),
+])
+def test_queries_bwd_small(S, Hq, Hkv, d, k):
+    run_queries_bwd_case(_problem(S, Hq, Hkv, d, 128, k, seed=S + 2 * Hq), label=f"S={S}")
+
+
+def test_queries_bwd_k0():
+    run_queries_bwd_case(_problem(333, 8, 2, 128, 128, 0, seed=8), label="k=0")
+
+
+def _tile_vs_query_bwd(p, label):
+    """Every query carries its tile's selection: dQ, dK and dV equal the tile
+    backward's bit for bit, and the per-query log-gate gradients sum over each
+    tile's queries to the tile's (fp32 sums in another order)."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hkv, k = int(p.seq_lens[0]), wl.n_kv_heads, wl.top_k
+    n_tiles = -(-S // 64)
+    rng = np.random.default_rng(98)
+    idx_t = np.full((Hkv, n_tiles, k), -1, np.int64)
+    lg_t = np.full((Hkv, n_tiles, k), -np.inf)
+    for r in range(Hkv):
+        for t in range(n_tiles):
+            n = min(k, t)
+            if n:
+                idx_t[r, t, :n] = np.sort(rng.choice(t, size=n, replace=False))
+                lg_t[r, t, :n] = -rng.uniform(0.5, 8.0, size=n)
+    tile_of = np.arange(S) // 64
+    Q, K, V, dO = dev(p.q), dev(p.K), dev(p.V), dev(p.dO)
+    it, lt = idx_dev(idx_t[None]), lg_dev(lg_t[None])
+    iq, lq = idx_dev(idx_t[:, tile_of][None]), lg_dev(lg_t[:, tile_of][None])
+    O_t, lse_t = S_.sas_prefill_fwd(Q, K, V, it, lt)
+    tQ, tK, tV, tlg = S_.sas_bwd(Q, K, V, O_t, dO, lse_t, it, lt)
+    qQ, qK, qV, qlg = S_.sas_bwd_queries(Q, K, V, O_t, dO, lse_t, iq, lq)
+    torch.cuda.synchronize()
+    same = [torch.equal(a, b) for a, b in ((tQ, qQ), (tK[:, :, :S], qK[:, :, :S]),
+                                           (tV[:, :, :S], qV[:, :, :S]))]
+    summed = np.zeros((Hkv, n_tiles, k))
+    ql = host(qlg)[0]
+    for i in range(S):
+        summed[:, i // 64] += ql[:, i]
+    tl = host(tlg)[0]
+    e = float(np.linalg.norm(summed - tl) / max(np.linalg.norm(tl), 1e-30))
+    log(f"[queries bwd {label}] tile selection broadcast: dQ/dK/dV equal={same} "
+        f"dlog_gate tile sums rel={e:.3g}")
+    assert all(same)
+    assert e <= 1e-4
+
+
+def test_queries_bwd_equal_tile_backward_small():
+    _tile_vs_query_bwd(_problem(1024, 8, 2, 128, 128, 5, seed=13), "S=1024")
+    _tile_vs_query_bwd(_problem(640, 4, 1, 64, 128, 3, seed=14), "S=640 d=64")
+
+
+@pytest.mark.timeout(900)
+def test_queries_bwd_full_workload():
+    """The training-style workload (S=16384, Qwen3-4B head shape, k=16) with a
+    random per-query selection: dQ and dlog_gate on sampled queries, the dK/dV
+    identities, and the bitwise equality with the tile backward."""
+    p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
+    queries = [0, 63, 64, 1000, 4095, 8200, 12345, 16383]
+    run_queries_bwd_case(p, queries=queries, selection="random", label="qwen3_4b_prefill_16k")
+    _tile_vs_query_bwd(p, "qwen3_4b_prefill_16k")
