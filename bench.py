@@ -530,20 +530,26 @@ def run_prefill(args, wl):
     # per-query selections with a per-query mask
     qidx, qlg, qlse, _ = Sb.sas_select(Sb.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S)
     Oq, lseq = Sb.sas_prefill_fwd_queries(Q, K, V, qidx, qlg)
-    t_qsel, t_qfwd = [], []
+    ws_qbwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_BWD_QUERIES, dims, S)), dtype=torch.uint8, device=dev)
+    qdlg = torch.empty(qidx.shape, dtype=torch.float32, device=dev)
+    t_qsel, t_qfwd, t_qbwd = [], [], []
     for i in range(n):
         if not args.no_flush:
             flush(i)
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
         e0.record(stream)
         Sb.sas_select(Sb.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S, idx=qidx,
                       log_gate=qlg, score_lse=qlse)
         e1.record(stream)
         Sb.sas_prefill_fwd_queries(Q, K, V, qidx, qlg, O=Oq, lse=lseq)
         e2.record(stream)
+        Sb.sas_bwd_queries(Q, K, V, Oq, dO, lseq, qidx, qlg, dQ=dQ, dK=dK, dV=dV, dlog_gate=qdlg,
+                           ws=ws_qbwd)
+        e3.record(stream)
         torch.cuda.synchronize()
         t_qsel.append(e0.elapsed_time(e1) * 1e3)
         t_qfwd.append(e1.elapsed_time(e2) * 1e3)
+        t_qbwd.append(e2.elapsed_time(e3) * 1e3)
     qsel_pairs, qvis_pairs = query_pairs(S, Hq // Hkv, qidx.cpu().numpy())
 
     med = statistics.median
@@ -571,11 +577,14 @@ def run_prefill(args, wl):
             "bwd_sink_heavy_selection": {"median": round(med(t_sink), 2), "p10": round(_pct(t_sink, .1), 2), "p90": round(_pct(t_sink, .9), 2)},
             "per_query_select": {"median": round(med(t_qsel), 2), "p10": round(_pct(t_qsel, .1), 2), "p90": round(_pct(t_qsel, .9), 2)},
             "per_query_fwd": {"median": round(us_qfwd, 2), "p10": round(_pct(t_qfwd, .1), 2), "p90": round(_pct(t_qfwd, .9), 2)},
+            "per_query_bwd": {"median": round(med(t_qbwd), 2), "p10": round(_pct(t_qbwd, .1), 2), "p90": round(_pct(t_qbwd, .9), 2)},
         },
         "per_query": {
             "selected_pairs": qsel_pairs, "visited_pairs": qvis_pairs,
             "fwd_TFLOPs_selected": round(4.0 * d * qsel_pairs / (us_qfwd * 1e-6) / 1e12, 1),
             "fwd_TFLOPs_visited": round(4.0 * d * qvis_pairs / (us_qfwd * 1e-6) / 1e12, 1),
+            "bwd_TFLOPs_selected": round(10.0 * d * qsel_pairs / (med(t_qbwd) * 1e-6) / 1e12, 1),
+            "bwd_TFLOPs_visited": round(10.0 * d * qvis_pairs / (med(t_qbwd) * 1e-6) / 1e12, 1),
             "note": "selected = the causally visible (query, key) pairs each query selected "
                     "(algorithmic); visited = the pairs the kernel multiplies: every query "
                     "of a tile against the union of the tile's selections",

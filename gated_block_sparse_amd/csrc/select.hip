@@ -406,7 +406,7 @@ constexpr int kQsRows = 32;   // queries per workgroup
 constexpr int kQsChunk = 64;  // blocks scored per pass
 
 template <typename T, int D, int DS, int G>
-__global__ void __launch_bounds__(kSelThreads)
+__global__ void __launch_bounds__(kSelThreads, 2)   // two workgroups per CU (LDS allows it)
 select_queries_kernel(const T* __restrict__ Q, int q_len, const float* __restrict__ Wq,
                       const float* __restrict__ summ, int Hkv, int c_max, int k,
                       int32_t* __restrict__ idx, float* __restrict__ log_gate,
@@ -419,7 +419,6 @@ select_queries_kernel(const T* __restrict__ Q, int q_len, const float* __restric
   __shared__ __attribute__((aligned(16))) float u[kQsRows * US];  // projected queries
   __shared__ float sc[kQsRows][kQsChunk + 1];
   __shared__ uint64_t top[kQsRows][kMaxTopK];
-  __shared__ uint64_t wk[NW][2][kQsChunk];
 
   const int t = blockIdx.x >> 1, r = blockIdx.y, b = blockIdx.z;
   const int i0 = t * kBlock + (blockIdx.x & 1) * kQsRows;
@@ -503,7 +502,7 @@ select_queries_kernel(const T* __restrict__ Q, int q_len, const float* __restric
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc[a][x] = 0.f;
-#pragma unroll 4
+#pragma unroll 2
       for (int j4 = 0; j4 < DS / 4; ++j4) {
         float4 uq[2], sv[4];
 #pragma unroll
@@ -527,41 +526,101 @@ select_queries_kernel(const T* __restrict__ Q, int q_len, const float* __restric
         }
     }
     __syncthreads();
-    // ---- per query: softmax state and Top-K list
-#pragma unroll
-    for (int e = 0; e < QPW; ++e) {
-      const int q = wave * QPW + e;
-      if (q >= nq) continue;   // wave-uniform
+    // ---- per query: softmax state and Top-K list.  A wave's QPW queries go
+    // through every step in lockstep (each cross-lane step is issued for all
+    // of them before the next), so the latencies of the lane shuffles and of
+    // the LDS reads of the searches overlap instead of adding up.  Rows of
+    // queries past nq are processed too (finite zeros) and never output.
+    {
       const bool ok = lane < nb;
-      const float s = sc[q][lane];
-      const float cm = wave_max_from(ok ? s : -INFINITY, 1);
-      const float m_new = fmaxf(run_m[e], cm);
-      const float cs = wave_sum_from(ok ? expf(s - m_new) : 0.f, 1);
-      run_s[e] = run_s[e] * expf(run_m[e] - m_new) + cs;
-      run_m[e] = m_new;
-      if (k == 0) continue;
-      const uint64_t key = wave_sort_desc(ok ? topk_key(s, c0 + lane) : 0ull);
-      const int n_old = min(k, c0);            // kept so far (every earlier block is a candidate)
-      const int n_new = min(k, c0 + nb);
-      if (c0 == 0) {
-        if (lane < n_new) top[q][lane] = key;
-      } else {
-        uint64_t* chunk = wk[wave][0];
-        uint64_t* merged = wk[wave][1];
-        chunk[lane] = key;
+      float sv[QPW], cm[QPW], ex[QPW];
+#pragma unroll
+      for (int e = 0; e < QPW; ++e) {
+        sv[e] = sc[wave * QPW + e][lane];
+        cm[e] = ok ? sv[e] : -INFINITY;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) cm[e] = fmaxf(cm[e], __shfl_xor(cm[e], o, 64));
+#pragma unroll
+      for (int e = 0; e < QPW; ++e) {
+        cm[e] = fmaxf(run_m[e], cm[e]);   // the new running max
+        ex[e] = ok ? expf(sv[e] - cm[e]) : 0.f;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) ex[e] += __shfl_xor(ex[e], o, 64);
+#pragma unroll
+      for (int e = 0; e < QPW; ++e) {
+        run_s[e] = run_s[e] * expf(run_m[e] - cm[e]) + ex[e];
+        run_m[e] = cm[e];
+      }
+      if (k > 0) {
+        // bitonic sort of each query's 64 chunk keys across the lanes
+        // (descending: lane 0 holds the largest)
+        uint64_t key[QPW];
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) key[e] = ok ? topk_key(sv[e], c0 + lane) : 0ull;
+#pragma unroll
+        for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+#pragma unroll
+            for (int e = 0; e < QPW; ++e) {
+              const uint64_t other = shfl_xor_u64(key[e], stride);
+              key[e] = keep_max ? (key[e] > other ? key[e] : other)
+                                : (key[e] < other ? key[e] : other);
+            }
+          }
+        // merge with the running list by rank: a key's place is its own
+        // position plus the number of larger keys in the other list (a
+        // binary search of at most 7 steps, n <= 64)
+        const int n_old = min(k, c0);   // kept so far (every earlier block is a candidate)
+        const int n_new = min(k, c0 + nb);
+        uint64_t lk[QPW];
+        int lo[QPW], hi[QPW], lo2[QPW], hi2[QPW];
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) {
+          lk[e] = lane < n_old ? top[wave * QPW + e][lane] : 0ull;
+          lo[e] = 0;
+          hi[e] = n_old;
+          lo2[e] = 0;
+          hi2[e] = nb;
+        }
+#pragma unroll
+        for (int step = 0; step < 7; ++step)
+#pragma unroll
+          for (int e = 0; e < QPW; ++e) {
+            // place of this lane's chunk key in the list (LDS)
+            const int mid = (lo[e] + hi[e]) >> 1;
+            if (lo[e] < hi[e]) {
+              if (top[wave * QPW + e][mid] > key[e]) lo[e] = mid + 1;
+              else hi[e] = mid;
+            }
+            // place of this lane's list key among the chunk keys (lanes)
+            const int mid2 = (lo2[e] + hi2[e]) >> 1;
+            const uint32_t src = static_cast<uint32_t>(min(mid2, 63));
+            const uint64_t v = (static_cast<uint64_t>(__shfl(static_cast<uint32_t>(key[e] >> 32), src, 64)) << 32) |
+                               __shfl(static_cast<uint32_t>(key[e]), src, 64);
+            if (lo2[e] < hi2[e]) {
+              if (v > lk[e]) lo2[e] = mid2 + 1;
+              else hi2[e] = mid2;
+            }
+          }
+        // every read of the lists is done before any lane writes them
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // place of the chunk key and of the list key held by this lane
-        const int pc = ok ? lane + count_greater_desc(top[q], n_old, key) : kMaxTopK;
-        const uint64_t lk = lane < n_old ? top[q][lane] : 0ull;
-        const int pl = lane < n_old ? lane + count_greater_desc(chunk, nb, lk) : kMaxTopK;
-        if (pc < n_new) merged[pc] = key;
-        if (pl < n_new) merged[pl] = lk;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < n_new) top[q][lane] = merged[lane];
+#pragma unroll
+        for (int e = 0; e < QPW; ++e) {
+          const int pc = ok ? lane + lo[e] : kMaxTopK;
+          const int pl = lane < n_old ? lane + lo2[e] : kMaxTopK;
+          if (pc < n_new) top[wave * QPW + e][pc] = key[e];
+          if (pl < n_new) top[wave * QPW + e][pl] = lk[e];
+        }
       }
     }
   }
