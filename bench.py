@@ -68,7 +68,7 @@ def _args():
 
 
 DECODE_KERNELS = ("sas::decode_split_kernel", "sas::decode_merge_kernel")
-PREFILL_KERNELS = ("sas::prefill_fwd_kernel",)
+PREFILL_KERNELS = ("sas::prefill_fwd_kernel<128, 4, false>",)   # the tile forward
 # the sources those kernels are built from
 DECODE_SOURCES = ("decode.hip", "sas_device.h", "sas_internal.h", "sas_select_dev.h")
 PREFILL_SOURCES = ("prefill.hip", "sas_device.h", "sas_internal.h", "sas_mfma.h")
