@@ -301,3 +301,51 @@ def test_queries_bwd_full_workload():
     queries = [0, 63, 64, 1000, 4095, 8200, 12345, 16383]
     run_queries_bwd_case(p, queries=queries, selection="random", label="qwen3_4b_prefill_16k")
     _tile_vs_query_bwd(p, "qwen3_4b_prefill_16k")
+
+
+def test_queries_batch2_select_fwd_bwd():
+    """Two sequences in one call (grid z) with a t_max above S: the per-query
+    selection, forward and backward of each sequence against the oracle run on
+    that sequence alone."""
+    S_ = _sas()
+    S, Hq, Hkv, d, k = 650, 8, 2, 128, 5
+    wl = synth.custom_workload("prefill", batch=2, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                               sel_dim=128, top_k=k, dtype="bf16", seq_len=S)
+    p = synth.make_problem(wl, 41)
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    t_max = S + 100     # K/V rows past S are never read
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:2] + (t_max - S, d), x.dtype)], axis=2)
+    Qd, dOd = dev(p.q), dev(p.dO)
+    Kd, Vd = dev(pad(p.K)), dev(pad(p.V))
+    lens = torch.tensor([S, S], dtype=torch.int32).cuda()
+    summ = S_.sas_block_summaries(Kd, lens, dev(p.Wk_sel))
+    gidx, glg, _, _ = S_.sas_select(S_.SAS_SELECT_QUERIES, Qd, None, dev(p.Wq_sel), summ, k,
+                                    t_max=t_max)
+    sels, refs = [], []
+    for b in range(2):
+        Qf, Kf, Vf, dOf = (synth.to_f64(x[b], "bf16") for x in (p.q, p.K, p.V, p.dO))
+        sel = O.query_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        gi = gidx.cpu().numpy()[b]
+        exact = (gi == sel["idx"]).all(axis=-1) | (sel["gap"] <= 1e-4)
+        assert exact.all(), b
+        sels.append(sel)
+        Or, lser = O.query_attend(Qf, Kf, Vf, S, sel["idx"], sel["log_gate"], scale, G)
+        gr = O.query_backward(Qf, Kf, Vf, dOf, S, sel["idx"], sel["log_gate"], scale, G)
+        refs.append((Or, lser, gr))
+    idx = idx_dev(np.stack([s["idx"] for s in sels]))
+    lg = lg_dev(np.stack([s["log_gate"] for s in sels]))
+    O_g, lse_g = S_.sas_prefill_fwd_queries(Qd, Kd, Vd, idx, lg)
+    dQ, dK, dV, dlg = S_.sas_bwd_queries(Qd, Kd, Vd, O_g, dOd, lse_g, idx, lg)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Or, lser, (rQ, rK, rV, rlg) = refs[b]
+        err = np.abs(host(O_g)[b] - Or).max()
+        assert err <= TOL_OUT["bf16"], (b, err)
+        for g, r in ((dQ, rQ), (dK, rK), (dV, rV)):
+            x = host(g)[b][:, :S]
+            assert np.linalg.norm(x - r) <= TOL_GRAD_REL * np.linalg.norm(r), b
+        valid = sels[b]["idx"] >= 0
+        e = np.linalg.norm(host(dlg)[b][valid] - rlg[valid]) / np.linalg.norm(rlg[valid])
+        assert e <= TOL_GRAD_REL, (b, e)
+        log(f"[queries batch2] sequence {b}: max|O-O_ref|={err:.3g} rel dlog_gate={e:.3g}")
