@@ -584,10 +584,11 @@ def run_prefill(args, wl):
             "fwd_TFLOPs_selected": round(4.0 * d * qsel_pairs / (us_qfwd * 1e-6) / 1e12, 1),
             "fwd_TFLOPs_visited": round(4.0 * d * qvis_pairs / (us_qfwd * 1e-6) / 1e12, 1),
             "bwd_TFLOPs_selected": round(10.0 * d * qsel_pairs / (med(t_qbwd) * 1e-6) / 1e12, 1),
-            "bwd_TFLOPs_visited": round(10.0 * d * qvis_pairs / (med(t_qbwd) * 1e-6) / 1e12, 1),
             "note": "selected = the causally visible (query, key) pairs each query selected "
-                    "(algorithmic); visited = the pairs the kernel multiplies: every query "
-                    "of a tile against the union of the tile's selections",
+                    "(algorithmic); visited = the pairs the forward and the backward's dQ pass "
+                    "multiply: every query of a tile against the union of the tile's "
+                    "selections (the backward's dK/dV pass multiplies selected pairs only, "
+                    "from per-block query lists)",
         },
         "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
         "bwd_TFLOPs": round(bwd_tf, 1),

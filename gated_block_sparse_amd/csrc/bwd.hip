@@ -333,7 +333,7 @@ __device__ int reading_tiles(int m, int n_tiles, int k, const int32_t* __restric
 __global__ void __launch_bounds__(256)
 bwd_qsel_prep_kernel(int S, int Hkv, int n_tiles, int k, const int32_t* __restrict__ idx,
                      const float* __restrict__ log_gate, uint32_t* __restrict__ ubits,
-                     int* __restrict__ ucnt, float* __restrict__ table) {
+                     int* __restrict__ ucnt, float* __restrict__ table, int* __restrict__ qcnt) {
   __shared__ uint32_t bits[kUnionWords];
   __shared__ int cnt[kUnionWords];
   const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -346,7 +346,10 @@ bwd_qsel_prep_kernel(int S, int Hkv, int n_tiles, int k, const int32_t* __restri
   __syncthreads();
   for (int e = tid; e < n_ent; e += 256) {
     const int m = idx[qrow0 * k + e];
-    if (m >= 0) atomicOr(&bits[m >> 5], 1u << (m & 31));
+    if (m >= 0) {
+      atomicOr(&bits[m >> 5], 1u << (m & 31));
+      if (qcnt) atomicAdd(&qcnt[grow * n_tiles + m], 1);   // selecting queries of block m
+    }
   }
   __syncthreads();
   if (tid < 64) {
@@ -392,6 +395,100 @@ bwd_qsel_dlg_kernel(int S, int Hkv, int G, int k, const int32_t* __restrict__ id
     for (int g = 0; g < G; ++g)
       tot += part[(((b * Hkv + r) * G + g) * S + qi) * k + slot];
   dlg[x] = tot;
+}
+
+// Per-block lists of the queries that selected each key block (d = 128
+// dK/dV pass under per-query selection): block m's list holds, in ascending
+// query order, every query i >= 64(m+1) whose selection contains m, with its
+// base-2 gate, padded with masked entries (gate -inf, a valid query index) to
+// a multiple of 64; qoff[m] is where it starts.  Built in a fixed order (the
+// counts by integer atomics, the lists by one workgroup per block walking
+// the readers in tile order), so the dK/dV sums stay bitwise reproducible.
+constexpr int kQlistScanThreads = 1024;
+
+__global__ void __launch_bounds__(kQlistScanThreads)
+bwd_qlist_scan_kernel(int n_tiles, const int* __restrict__ qcnt, int* __restrict__ qoff) {
+  __shared__ int part[kQlistScanThreads / 64];
+  const size_t grow = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = tid < n_tiles ? (qcnt[grow * n_tiles + tid] + 63) & ~63 : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += part[w];
+  if (tid < n_tiles) qoff[grow * (n_tiles + 1) + tid] = base + incl - c;
+  if (tid == kQlistScanThreads - 1) qoff[grow * (n_tiles + 1) + n_tiles] = base + incl;
+}
+
+template <int NWV>
+__device__ int reading_tiles_pq(int m, int n_tiles, const uint32_t* __restrict__ ubits,
+                                const int* __restrict__ ucnt, int* list_t, int* list_row,
+                                int* s_count, int* s_wcount);
+
+__global__ void __launch_bounds__(256)
+bwd_qlist_fill_kernel(int S, int Hkv, int n_tiles, size_t cap,
+                      const uint32_t* __restrict__ ubits, const int* __restrict__ ucnt,
+                      const float* __restrict__ gtab, const int* __restrict__ qoff,
+                      int* __restrict__ qlist, float* __restrict__ qbeta) {
+  constexpr int NWV = 4;
+  __shared__ int list_t[kMaxTileRows];
+  __shared__ int list_row[kMaxTileRows];
+  __shared__ int cnt_e[kMaxTileRows];
+  __shared__ int s_count;
+  __shared__ int s_wcount[NWV];
+  const int m = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t grow = static_cast<size_t>(b) * Hkv + r;
+  const int n_list = reading_tiles_pq<NWV>(m, n_tiles, ubits + grow * n_tiles * kUnionWords,
+                                           ucnt + grow * n_tiles * kUnionWords, list_t, list_row,
+                                           &s_count, s_wcount);
+  const float* gt = gtab + grow * qsel_rows(n_tiles) * 64;
+  // pass 1: how many queries of each reading tile selected m (entry 0 is the
+  // diagonal tile, not part of the list)
+  for (int e = 1 + wave; e < n_list; e += NWV) {
+    const bool sel = gt[static_cast<size_t>(list_row[e]) * 64 + lane] > -INFINITY;
+    const int c = __popcll(__ballot(sel));
+    if (lane == 0) cnt_e[e] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {   // exclusive prefix in entry (= tile) order
+    int acc = 0;
+    for (int e = 1; e < n_list; ++e) {
+      const int c = cnt_e[e];
+      cnt_e[e] = acc;
+      acc += c;
+    }
+    cnt_e[0] = acc;   // the list length
+  }
+  __syncthreads();
+  const int o0 = qoff[grow * (n_tiles + 1) + m], o1 = qoff[grow * (n_tiles + 1) + m + 1];
+  // the lists of one (sequence, group) are contiguous in its slice of cap entries
+  int* ql = qlist + grow * cap + o0;
+  float* qb = qbeta + grow * cap + o0;
+  // pass 2: the queries of each reading tile, in ascending order
+  for (int e = 1 + wave; e < n_list; e += NWV) {
+    const float g = gt[static_cast<size_t>(list_row[e]) * 64 + lane];
+    const bool sel = g > -INFINITY;
+    const unsigned long long mask = __ballot(sel);
+    if (sel) {
+      const int at = cnt_e[e] + __popcll(mask & ((1ull << lane) - 1ull));
+      ql[at] = 64 * list_t[e] + lane;
+      qb[at] = g;
+    }
+  }
+  // padding: masked entries that repeat a valid query index
+  const int len = cnt_e[0];
+  const int pad_q = min(64 * (m + 1), S - 1);
+  for (int at = len + tid; at < o1 - o0; at += 256) {
+    ql[at] = pad_q;
+    qb[at] = -INFINITY;
+  }
 }
 
 // The readers of key block m under per-query selection: the diagonal tile
@@ -729,10 +826,14 @@ constexpr int kTsSlot = 2 * kTsTensor + 64 * 4;      // Q, dO, lse[32], D[32]
 __device__ __forceinline__ int ts_swz(int q) { return 2 * (q & 7) + ((q >> 2) & 1); }
 
 
-// PQ (one selection per query): the readers come from the prep bitmaps, the
-// gates are per query: wave 1 also copies the step's 32 base-2 gates from the
-// prep's gate row of (tile, block) into the slot (row 0, zeros, for the
-// diagonal tile), and no dlog_gate is formed here (the dQ pass does it).
+// PQ (one selection per query): after the diagonal tile, the entries are
+// groups of 64 from the block's list of selecting queries (bwd_qlist_*), so
+// only (query, block) pairs that were selected are multiplied.  Each wave
+// gathers its Q/dO rows by the list's query indices (scalar loads of the
+// indices), wave 0 the lse and D of the 32 listed queries, and wave 1 copies
+// their 32 base-2 gates into the slot (padding entries carry -inf; the
+// diagonal tile takes the zero gate row 0 of the prep table).  No dlog_gate
+// is formed here (the dQ pass does it).
 template <int G, bool PQ>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -741,9 +842,10 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
                    const float* __restrict__ log_gate, float scale2, float scale, int n_hot,
                    int max_chunks, float* __restrict__ hot_part, int* __restrict__ hot_cnt,
-                   const uint32_t* __restrict__ ubits, const int* __restrict__ ucnt,
-                   const float* __restrict__ gtab, uint16_t* __restrict__ dK,
-                   uint16_t* __restrict__ dV, float* __restrict__ dlg) {
+                   const float* __restrict__ gtab, const int* __restrict__ qoff,
+                   const int* __restrict__ qlist, const float* __restrict__ qbeta, size_t qcap,
+                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                   float* __restrict__ dlg) {
   constexpr int D = 128, NWV = 4, KS = D / 32, CT = D / 16;
   constexpr int SLOT = kTsSlot + (PQ ? 64 * 4 : 0);   // + the step's gates (PQ)
   __shared__ __attribute__((aligned(16))) unsigned char ring[kTsSlots * SLOT];
@@ -776,15 +878,20 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const size_t grow = static_cast<size_t>(b) * Hkv + r;
 
   int n_list;
-  if constexpr (PQ)
-    n_list = reading_tiles_pq<NWV>(m, n_tiles, ubits + grow * n_tiles * kUnionWords,
-                                   ucnt + grow * n_tiles * kUnionWords, list_t, list_slot,
-                                   &s_count, s_wcount);
-  else
+  int q_o0 = 0;   // PQ: start of the block's query list
+  if constexpr (PQ) {
+    q_o0 = qoff[grow * (n_tiles + 1) + m];
+    n_list = 1 + (qoff[grow * (n_tiles + 1) + m + 1] - q_o0) / 64;
+    if (tid == 0) list_t[0] = m;
+    __syncthreads();
+  } else {
     n_list = reading_tiles<NWV>(m, n_tiles, k, idx + grow * n_tiles * k,
                                 log_gate ? log_gate + grow * n_tiles * k : nullptr, list_t,
                                 list_slot, list_beta, &s_count, s_wcount);
+  }
   const float* gt = PQ ? gtab + grow * qsel_rows(n_tiles) * 64 : nullptr;
+  const int* qlg = PQ ? qlist + grow * qcap : nullptr;
+  const float* qbg = PQ ? qbeta + grow * qcap : nullptr;
   // Hot-block chunking: a hot block read by more than kHotCap tiles is split
   // over ceil(n_list / kHotCap) workgroups, chunk c taking entries c, c + nc,
   // c + 2nc, ... (interleaved, so the chunks sweep the tiles together and
@@ -807,26 +914,55 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // (into a slot nobody reads), so every step issues the same number of
   // copies per wave and the wait counts below stay exact.  Query rows past
   // the sequence end repeat its last row (finite values; masked below).
+  const int wv_s = __builtin_amdgcn_readfirstlane(wave);
   auto issue = [&](int s2) {
     const int sc = min(s2, n_steps - 1);
     const int qt2 = sc & 1, g2 = (sc >> 1) % G, e2 = chunk + ((sc >> 1) / G) * n_chunks;
     const int qbase = 64 * list_t[e2] + 32 * qt2;
     const size_t hrow = (static_cast<size_t>(b) * Hq + r * G + g2) * S;
     const uint32_t slot = ring_lds + (s2 % kTsSlots) * SLOT;
+    // the query of each copied row: contiguous in the diagonal tile, else from
+    // the block's list (wave-uniform position: scalar loads)
+    const bool listed = PQ && e2 > 0;
+    const int p0 = __builtin_amdgcn_readfirstlane(q_o0 + 64 * (e2 - 1) + 32 * qt2);
+    int rq[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int ql = 8 * wave + 4 * n + i4;
+      rq[n] = min(qbase + ql, S - 1);
+    }
+    if (listed) {
+      const int* wl = qlg + p0 + 8 * wv_s;
+      int r8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r8[j] = __builtin_amdgcn_readfirstlane(wl[j]);   // scalar loads
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        rq[n] = i4 == 0 ? r8[4 * n] : i4 == 1 ? r8[4 * n + 1] : i4 == 2 ? r8[4 * n + 2] : r8[4 * n + 3];
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int row0 = 8 * wave + 4 * n;
       const int ql = row0 + i4;
-      const size_t src = (hrow + min(qbase + ql, S - 1)) * D + 8 * (l16 ^ ts_swz(ql));
+      const size_t src = (hrow + rq[n]) * D + 8 * (l16 ^ ts_swz(ql));
       lds_dma<16>(Q + src, slot + row0 * kTsRow);
       lds_dma<16>(dO + src, slot + kTsTensor + row0 * kTsRow);
     }
     if (wave == 0) {
-      const float* src = (lane < 32 ? lse : Dq) + hrow + min(qbase + (lane & 31), S - 1);
+      int rl = min(qbase + (lane & 31), S - 1);
+      if (listed) {
+        const int* wl = qlg + p0;
+        int r32[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) r32[j] = __builtin_amdgcn_readfirstlane(wl[j]);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) rl = (lane & 31) == j ? r32[j] : rl;
+      }
+      const float* src = (lane < 32 ? lse : Dq) + hrow + rl;
       lds_dma<4>(src, slot + 2 * kTsTensor);
     }
     if (PQ && wave == 1)   // gates of the 32 queries (lanes 32..63 repeat them)
-      lds_dma<4>(gt + static_cast<size_t>(list_slot[e2]) * 64 + 32 * qt2 + (lane & 31),
+      lds_dma<4>(listed ? qbg + p0 + (lane & 31) : gt + 32 * qt2 + (lane & 31),
                  slot + 2 * kTsTensor + 256);
   };
   // ---- K and V rows of the wave's tokens: B operands, k-step ks holds
@@ -890,7 +1026,7 @@ bwd_dkdv_ts_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int qt = s & 1, g = (s >> 1) % G, e = chunk + jl * n_chunks;
     const bool diag = e == 0;
     const float beta2 = PQ ? 0.f : list_beta[e];
-    const int nq = min(64, S - 64 * list_t[e]);
+    const int nq = (PQ && e > 0) ? 64 : min(64, S - 64 * list_t[e]);
     const unsigned char* slot = ring + (s % kTsSlots) * SLOT;
     const float* bq = reinterpret_cast<const float*>(slot + 2 * kTsTensor + 256);   // PQ gates
     const unsigned char* Qs = slot;
@@ -1037,7 +1173,7 @@ static size_t align_up256(size_t x) { return (x + 255) & ~size_t(255); }
 // [B,Hkv,n_tiles,32] | their word prefix counts | gate rows
 // [B,Hkv,1 + n_tiles(n_tiles-1)/2,64] fp32.
 struct BwdWs {
-  size_t dq, hot_part, hot_cnt, part, ubits, ucnt, gtab, total;
+  size_t dq, hot_part, hot_cnt, part, ubits, ucnt, gtab, qcnt, qoff, qlist, qbeta, qcap, total;
 };
 static BwdWs bwd_ws_layout(const sas_dims& d, int seq_len, bool pq) {
   BwdWs w{};
@@ -1068,6 +1204,20 @@ static BwdWs bwd_ws_layout(const sas_dims& d, int seq_len, bool pq) {
     off = align_up256(off);
     w.gtab = off;
     off += groups * qsel_rows(n_tiles) * 64 * sizeof(float);
+    // per-block lists of selecting queries (d = 128 dK/dV pass), each padded to 64
+    w.qcap = static_cast<size_t>(seq_len) * d.top_k + 64 * static_cast<size_t>(n_tiles);
+    off = align_up256(off);
+    w.qcnt = off;
+    off += groups * n_tiles * sizeof(int);
+    off = align_up256(off);
+    w.qoff = off;
+    off += groups * (n_tiles + 1) * sizeof(int);
+    off = align_up256(off);
+    w.qlist = off;
+    off += groups * w.qcap * sizeof(int);
+    off = align_up256(off);
+    w.qbeta = off;
+    off += groups * w.qcap * sizeof(float);
   }
   w.total = off;
   return w;
@@ -1092,23 +1242,43 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   uint32_t* ubits = PQ ? reinterpret_cast<uint32_t*>(wsb + lay.ubits) : nullptr;
   int* ucnt = PQ ? reinterpret_cast<int*>(wsb + lay.ucnt) : nullptr;
   float* gtab = PQ ? reinterpret_cast<float*>(wsb + lay.gtab) : nullptr;
+  const bool qlists = PQ && D == 128;   // the d = 128 dK/dV pass walks per-block query lists
+  int* qcnt = qlists ? reinterpret_cast<int*>(wsb + lay.qcnt) : nullptr;
+  int* qoff = qlists ? reinterpret_cast<int*>(wsb + lay.qoff) : nullptr;
+  int* qlist = qlists ? reinterpret_cast<int*>(wsb + lay.qlist) : nullptr;
+  float* qbeta = qlists ? reinterpret_cast<float*>(wsb + lay.qbeta) : nullptr;
+  const size_t groups = static_cast<size_t>(d.batch) * d.n_kv_heads;
   const size_t n_rows = static_cast<size_t>(d.batch) * d.n_q_heads * S;
-  // the tile backward's dlog_gate entries are zeroed here and written by the
-  // dK/dV pass; the per-query one is written whole by its reduction kernel
-  const size_t n_dlg = (!PQ && d.top_k > 0 && dlg)
-                           ? static_cast<size_t>(d.batch) * d.n_kv_heads * n_tiles * d.top_k : 0;
+  // The pre-pass zeroes a buffer besides forming D: the tile backward's
+  // dlog_gate (written by its dK/dV pass), or the per-query block counts
+  // (the per-query dlog_gate is written whole by its reduction kernel).
+  float* zero = PQ ? reinterpret_cast<float*>(qcnt) : dlg;
+  const size_t n_zero = PQ ? (qlists ? groups * n_tiles : 0)
+                           : ((d.top_k > 0 && dlg) ? groups * n_tiles * d.top_k : 0);
   const size_t thr = n_rows * (D / 8);
   const int pre_blocks = static_cast<int>((thr + 255) / 256);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_blocks), dim3(256), 0, st,
                      static_cast<const uint16_t*>(O), static_cast<const uint16_t*>(dO), n_rows,
-                     Dq, dlg, n_dlg);
+                     Dq, zero, n_zero);
   sas_status s = check_launch("bwd_pre");
   if (s != SAS_OK) return s;
   if constexpr (PQ) {
     hipLaunchKernelGGL(bwd_qsel_prep_kernel, dim3(n_tiles, d.n_kv_heads, d.batch), dim3(256), 0,
-                       st, S, d.n_kv_heads, n_tiles, d.top_k, idx, log_gate, ubits, ucnt, gtab);
+                       st, S, d.n_kv_heads, n_tiles, d.top_k, idx, log_gate, ubits, ucnt, gtab,
+                       qcnt);
     s = check_launch("bwd_qsel_prep");
     if (s != SAS_OK) return s;
+    if (qlists) {
+      hipLaunchKernelGGL(bwd_qlist_scan_kernel, dim3(static_cast<unsigned>(groups)),
+                         dim3(kQlistScanThreads), 0, st, n_tiles, qcnt, qoff);
+      s = check_launch("bwd_qlist_scan");
+      if (s != SAS_OK) return s;
+      hipLaunchKernelGGL(bwd_qlist_fill_kernel, dim3(n_tiles, d.n_kv_heads, d.batch), dim3(256),
+                         0, st, S, d.n_kv_heads, n_tiles, lay.qcap, ubits, ucnt, gtab, qoff,
+                         qlist, qbeta);
+      s = check_launch("bwd_qlist_fill");
+      if (s != SAS_OK) return s;
+    }
   }
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* kk = static_cast<const uint16_t*>(K);
@@ -1142,8 +1312,9 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
 #define SAS_DKDV_TS(GG)                                                                          \
   hipLaunchKernelGGL((bwd_dkdv_ts_kernel<GG, PQ>), dim3(grid_x, 1, d.batch), dim3(256), 0, st, q, \
                      kk, v, dop, lse, Dq, S, d.n_kv_heads, d.t_max, n_tiles, d.top_k, idx,        \
-                     log_gate, scale2, scale, n_hot, max_chunks, hot_part, hot_cnt, ubits, ucnt,  \
-                     gtab, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV), dlg)
+                     log_gate, scale2, scale, n_hot, max_chunks, hot_part, hot_cnt, gtab, qoff,   \
+                     qlist, qbeta, lay.qcap, static_cast<uint16_t*>(dK),                           \
+                     static_cast<uint16_t*>(dV), dlg)
     switch (G) {
       case 1: SAS_DKDV_TS(1); break;
       case 2: SAS_DKDV_TS(2); break;
