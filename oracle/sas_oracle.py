@@ -580,6 +580,40 @@ def query_backward(Q, K, V, dO, S, idx, log_gate, scale, G, b=BLOCK, queries=Non
     return dQ, dK, dV, dlg
 
 
+def query_selector_backward(Q, K, S, Wq_sel, Wk_sel, idx, dlog_gate, G, b=BLOCK):
+    """Step 8 for per-query rows: the selector weights' gradients from the
+    per-query log-gate gradients (the selection held fixed).  Row (i, r) has
+    the C_i = i // b blocks before query i's block, the score
+    s_m = (Wq_sel qbar) . summ_m / sqrt(d_sel) with qbar the mean of query i
+    over the group's heads, and ds = score_grad(s, idx, dlog_gate) over all
+    C_i blocks; then, as for the tile rows,
+      dWq_sel += ds_m summ_m qbar^T / sqrt(d_sel),
+      dWk_sel += ds_m (Wq_sel qbar / sqrt(d_sel)) kbar_m^T.
+    Q: [Hq,>=S,d], K: [Hkv,>=S,d]; idx/dlog_gate [Hkv, S, k].  Returns
+    (ds rows: dict i -> [Hkv, C_i], dWq_sel [d_sel,d], dWk_sel [d_sel,d])."""
+    d_sel, d = Wq_sel.shape
+    Hkv = K.shape[0]
+    summ = block_summaries(K, S, Wk_sel, b)
+    rows = query_scores(Q, S, Wq_sel, summ, G, b)
+    dWq = np.zeros((d_sel, d))
+    dWk = np.zeros((d_sel, d))
+    ds_rows = {}
+    for i in range(S):
+        C = i // b
+        ds_i = np.zeros((Hkv, C))
+        for r in range(Hkv):
+            ds = score_grad(rows[i][r], idx[r, i], dlog_gate[r, i])
+            ds_i[r] = ds
+            qbar = Q[r * G:(r + 1) * G, i].mean(axis=0)
+            u = Wq_sel @ qbar / math.sqrt(d_sel)
+            for m in range(C):
+                kbar = K[r, b * m:b * m + b].mean(axis=0)
+                dWq += ds[m] * np.outer(summ[r, m], qbar) / math.sqrt(d_sel)
+                dWk += ds[m] * np.outer(u, kbar)
+        ds_rows[i] = ds_i
+    return ds_rows, dWq, dWk
+
+
 # --------------------------------------------------------------------------
 # Second formulation for tiny inputs: dense logits with a block mask
 # --------------------------------------------------------------------------

@@ -693,6 +693,92 @@ def check_query_backward_vs_tiles(seed=35):
     assert np.abs(summed - tlg).max() < 1e-12
 
 
+def _query_lg_from_scores(rows, idx):
+    """Per-query log g of the selected slots from explicit score rows."""
+    Hkv, S, k = idx.shape
+    lg = np.full(idx.shape, -np.inf)
+    for i in range(S):
+        for r in range(Hkv):
+            s = rows[i][r]
+            if s.size:
+                ls = s - (s.max() + np.log(np.exp(s - s.max()).sum()))
+                for slot in range(k):
+                    if idx[r, i, slot] >= 0:
+                        lg[r, i, slot] = ls[idx[r, i, slot]]
+    return lg
+
+
+def _query_loss_of_weights(Q, K, V, dO, S, b, G, idx, Wq, Wk, scale):
+    summ = O.block_summaries(K, S, Wk, b)
+    rows = O.query_scores(Q, S, Wq, summ, G, b)
+    return _query_loss(Q, K, V, dO, S, idx, _query_lg_from_scores(rows, idx), scale, G, b)
+
+
+def check_query_selector_weights_fd(seed=36):
+    """Per-query rows: dWq_sel / dWk_sel of the attention loss through the
+    per-query gates, scores and summaries, by central differences on every
+    weight (the selection held fixed)."""
+    S, b, Hq, Hkv, d, d_sel, k, scale = 22, 4, 4, 2, 5, 3, 2, 0.41
+    G = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal(sh) for sh in ((Hq, S, d), (Hkv, S, d), (Hkv, S, d)))
+    dO = rng.standard_normal((Hq, S, d))
+    Wq = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    Wk = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    idx, _ = _random_query_selection(rng, Hkv, S, b, k)
+    summ = O.block_summaries(K, S, Wk, b)
+    lg = _query_lg_from_scores(O.query_scores(Q, S, Wq, summ, G, b), idx)
+    _, _, _, dlg = O.query_backward(Q, K, V, dO, S, idx, lg, scale, G, b)
+    _, dWq, dWk = O.query_selector_backward(Q, K, S, Wq, Wk, idx, dlg, G, b)
+    h = 1e-6
+    for W, dW, which in ((Wq, dWq, "q"), (Wk, dWk, "k")):
+        fd = np.zeros_like(W)
+        for j, c in itertools.product(range(W.shape[0]), range(W.shape[1])):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[j, c] += h
+            Wm[j, c] -= h
+            args = (Wp, Wk) if which == "q" else (Wq, Wp)
+            lp = _query_loss_of_weights(Q, K, V, dO, S, b, G, idx, *args, scale)
+            args = (Wm, Wk) if which == "q" else (Wq, Wm)
+            lm = _query_loss_of_weights(Q, K, V, dO, S, b, G, idx, *args, scale)
+            fd[j, c] = (lp - lm) / (2 * h)
+        assert np.abs(fd).max() > 1e-4
+        np.testing.assert_allclose(dW, fd, atol=1e-6 * np.abs(fd).max(), rtol=1e-5)
+
+
+def check_query_selector_vs_tiles(seed=37):
+    """Queries equal within each tile and carrying their tile's selection: the
+    per-query selector gradients equal the tile rows' gradients taken with
+    each tile's log-gate gradients summed over its queries."""
+    S, b, Hq, Hkv, d, d_sel, k = 40, 8, 4, 2, 5, 3, 2
+    G = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((Hq, S, d))
+    for t in range(S // b):
+        Q[:, b * t:b * t + b] = Q[:, b * t:b * t + 1]
+    K = rng.standard_normal((Hkv, S, d))
+    Wq = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    Wk = rng.standard_normal((d_sel, d)) / math.sqrt(d)
+    n_tiles = S // b
+    idx_t, _ = _random_selection(rng, Hkv, n_tiles, k)
+    tile_of = np.arange(S) // b
+    dlg_q = rng.standard_normal((Hkv, S, k)) * (idx_t[:, tile_of] >= 0)
+    _, qWq, qWk = O.query_selector_backward(Q, K, S, Wq, Wk, idx_t[:, tile_of], dlg_q, G, b)
+    dlg_t = np.zeros((Hkv, n_tiles, k))
+    for i in range(S):
+        dlg_t[:, i // b] += dlg_q[:, i]
+    _, tWq, tWk = O.selector_backward(Q, K, S, Wq, Wk, idx_t, dlg_t, G, b)
+    assert np.abs(qWq - tWq).max() < 1e-12 and np.abs(qWk - tWk).max() < 1e-12
+
+
+def test_query_selector_weight_gradients_match_finite_differences():
+    check_query_selector_weights_fd()
+
+
+def test_query_selector_gradients_reduce_to_tile_rows():
+    check_query_selector_vs_tiles()
+
+
 def test_query_backward_matches_finite_differences():
     check_query_backward_fd()
 
@@ -718,7 +804,8 @@ PINS = [check_hand_worked, check_topk_lexsort, check_topk_exhaustive, check_gath
         check_uniform_gate_is_dense_with_bias, check_k0_is_local_causal, check_dlog_gate_fd,
         check_qkv_grads_fd, check_summaries, check_selector_score_grad_fd,
         check_selector_weights_fd, check_query_selection_dense, check_query_k0_local,
-        check_query_scores_vs_tiles, check_query_backward_fd, check_query_backward_vs_tiles]
+        check_query_scores_vs_tiles, check_query_backward_fd, check_query_backward_vs_tiles,
+        check_query_selector_weights_fd, check_query_selector_vs_tiles]
 
 
 def _some_pin_fails():
