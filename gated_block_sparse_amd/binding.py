@@ -22,7 +22,7 @@ SAS_F32, SAS_BF16 = 0, 1
 SAS_SELECT_DECODE, SAS_SELECT_TILES, SAS_SELECT_QUERIES = 0, 1, 2
 (SAS_OP_SELECT_DECODE, SAS_OP_SELECT_TILES, SAS_OP_DECODE_FWD, SAS_OP_PREFILL_FWD, SAS_OP_BWD,
  SAS_OP_DECODE_STEP, SAS_OP_SELECTOR_BWD, SAS_OP_SELECT_QUERIES, SAS_OP_PREFILL_FWD_QUERIES,
- SAS_OP_BWD_QUERIES) = range(10)
+ SAS_OP_BWD_QUERIES, SAS_OP_SELECTOR_BWD_QUERIES) = range(11)
 BLOCK = 64
 SIZE_MAX = 2 ** 64 - 1
 
@@ -59,6 +59,8 @@ _SIGNATURES = {
                                _vp, _vp, _vp, _sz, _vp]),
     "sas_selector_bwd": (_i32, [_PD, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 _sz, _vp]),
+    "sas_selector_bwd_queries": (_i32, [_PD, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _sz, _vp]),
     "sas_workspace_bytes": (_sz, [_i32, _PD, _i32]),
     "sas_status_str": (ctypes.c_char_p, [_i32]),
     "sas_last_error": (ctypes.c_char_p, []),
@@ -415,4 +417,32 @@ def sas_selector_bwd(Q, K, Wq_sel, summ, idx, score_lse, dlog_gate, q_len=None, 
                                            _ptr(Wq_sel), _ptr(summ), _ptr(idx), _ptr(score_lse),
                                            _ptr(dlog_gate), _ptr(ds), _ptr(dWq), _ptr(dWk),
                                            _ptr(ws), ws_bytes, _stream()))
+    return dWq, dWk, ds
+
+
+def sas_selector_bwd_queries(Q, K, Wq_sel, Wk_sel, summ, idx, score_lse, dlog_gate, q_len=None,
+                             t_max=None, ds=None, want_ds=False, dWq=None, dWk=None, ws=None):
+    """Selector weight gradients for per-query rows.  Q [B,Hq,S,d]; K
+    [B,Hkv,t_max,d]; summ [B,Hkv,t_max//64,d_sel]; idx/dlog_gate [B,Hkv,S,k];
+    score_lse [B,Hkv,S].  Returns (dWq_sel, dWk_sel, ds | None)."""
+    B, Hq, S, d = Q.shape
+    _, Hkv, tm, _ = K.shape
+    t_max = tm if t_max is None else t_max
+    q_len = S if q_len is None else q_len
+    ds_dim = Wq_sel.shape[0]
+    k = idx.shape[-1]
+    dims = make_dims(B, Hq, Hkv, d, ds_dim, k, t_max, _dtype_code(Q))
+    dev = Q.device
+    if want_ds and ds is None:
+        ds = torch.full((B, Hkv, q_len, t_max // BLOCK), float("nan"), dtype=torch.float32,
+                        device=dev)
+    if dWq is None:
+        dWq = torch.empty_like(Wq_sel)
+    if dWk is None:
+        dWk = torch.empty_like(Wq_sel)
+    ws, ws_bytes = _workspace(SAS_OP_SELECTOR_BWD_QUERIES, dims, q_len, ws, dev)
+    _check(load_library().sas_selector_bwd_queries(
+        ctypes.byref(dims), _ptr(Q), q_len, _ptr(K), _ptr(Wq_sel), _ptr(Wk_sel), _ptr(summ),
+        _ptr(idx), _ptr(score_lse), _ptr(dlog_gate), _ptr(ds), _ptr(dWq), _ptr(dWk), _ptr(ws),
+        ws_bytes, _stream()))
     return dWq, dWk, ds

@@ -363,6 +363,34 @@ sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, 
                              dWq_sel, dWk_sel, ws, static_cast<hipStream_t>(stream));
 }
 
+sas_status sas_selector_bwd_queries(const sas_dims* dims, const void* Q, int32_t q_len,
+                                    const void* K, const float* Wq_sel, const float* Wk_sel,
+                                    const float* summ, const int32_t* idx,
+                                    const float* score_lse, const float* dlog_gate, float* ds,
+                                    float* dWq_sel, float* dWk_sel, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  SAS_TRY(check_dims(dims, false));
+  SAS_TRY(check_len(dims, q_len, "q_len"));
+  if (cdiv(q_len, kBlock) > kMaxTileRows)
+    return fail(SAS_ERR_UNSUPPORTED, "q_len=%d gives more than %d tiles", q_len, kMaxTileRows);
+  SAS_NONNULL(Q);
+  SAS_NONNULL(K);
+  SAS_NONNULL(Wq_sel);
+  SAS_NONNULL(Wk_sel);
+  SAS_NONNULL(score_lse);
+  SAS_NONNULL(dWq_sel);
+  SAS_NONNULL(dWk_sel);
+  if (dims->t_max >= kBlock) SAS_NONNULL(summ);
+  if (dims->top_k > 0) {
+    SAS_NONNULL(idx);
+    SAS_NONNULL(dlog_gate);
+  }
+  SAS_TRY(check_ws(selector_bwd_queries_ws_bytes(*dims, q_len), ws, ws_bytes));
+  return launch_selector_bwd_queries(*dims, Q, q_len, K, Wq_sel, Wk_sel, summ, idx, score_lse,
+                                     dlog_gate, ds, dWq_sel, dWk_sel, ws,
+                                     static_cast<hipStream_t>(stream));
+}
+
 size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
   const bool bf16_only = (op == SAS_OP_PREFILL_FWD || op == SAS_OP_BWD ||
                           op == SAS_OP_PREFILL_FWD_QUERIES || op == SAS_OP_BWD_QUERIES);
@@ -388,6 +416,9 @@ size_t sas_workspace_bytes(int32_t op, const sas_dims* dims, int32_t q_len) {
     case SAS_OP_BWD_QUERIES:
       if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
       return bwd_queries_ws_bytes(*dims, q_len);
+    case SAS_OP_SELECTOR_BWD_QUERIES:
+      if (check_len(dims, q_len, "q_len") != SAS_OK) return SIZE_MAX;
+      return selector_bwd_queries_ws_bytes(*dims, q_len);
     default:
       fail(SAS_ERR_INVALID_ARGUMENT, "op=%d is not a sas_op", op);
       return SIZE_MAX;

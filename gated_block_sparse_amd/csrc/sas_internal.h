@@ -118,6 +118,13 @@ sas_status launch_selector_bwd(const sas_dims& d, const void* Q, int q_len, cons
                                const float* Wq, const float* summ, const int32_t* idx,
                                const float* score_lse, const float* dlg, float* ds, float* dWq,
                                float* dWk, void* ws, hipStream_t st);
+// The same for per-query rows (idx/score_lse/dlog_gate [B,Hkv,q_len,...]).
+size_t selector_bwd_queries_ws_bytes(const sas_dims& d, int q_len);
+sas_status launch_selector_bwd_queries(const sas_dims& d, const void* Q, int q_len,
+                                       const void* K, const float* Wq, const float* Wk,
+                                       const float* summ, const int32_t* idx,
+                                       const float* score_lse, const float* dlg, float* ds,
+                                       float* dWq, float* dWk, void* ws, hipStream_t st);
 
 size_t prefill_ws_bytes(const sas_dims& d, int seq_len);
 sas_status launch_prefill_fwd(const sas_dims& d, const void* Q, const void* K, const void* V,

@@ -273,6 +273,368 @@ static sas_status sbwd_by_dims(const sas_dims& d, const void* Q, int q_len, cons
   return sbwd_by_group<T, 64, 64>(d, Q, q_len, K, Wq, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
 }
 
+// ---------------------------------------------------------- query rows ---
+// Per-query rows (one selection per query): row (i, r) has C = i / 64 blocks
+// and the pooled query qbar_i (mean of query i over the group's heads).  A
+// block is seen by up to S rows, so instead of forming e_m = sum_rows ds u
+// per block the gradients go through one D x D matrix:
+//   h_i = sum_m ds_(i,m) kbar_m,   H = sum_rows h_i qbar_i^T,
+//   dWq_sel = Wk_sel H / sqrt(d_sel)      (= sum_rows a_i qbar_i^T / sqrt(d_sel),
+//                                          a_i = sum_m ds_(i,m) Wk_sel kbar_m),
+//   dWk_sel = Wq_sel H^T / sqrt(d_sel)    (= sum_m e_m kbar_m^T,
+//                                          e_m = sum_rows ds_(i,m) Wq_sel qbar_i / sqrt(d_sel)).
+// Four kernels, fixed summation orders (bitwise reproducible): mean keys;
+// one workgroup per 32 rows (scores, ds, h); chunked outer-product partials
+// of H; H and the two small products.
+constexpr int kQsbRows = 32;      // rows per workgroup of the row kernel
+constexpr int kQsbChunk = 64;     // blocks per scoring pass
+constexpr int kQsbPartRows = 1024;  // rows per H partial
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kSelThreads)
+qsb_kbar_kernel(const T* __restrict__ K, int Hkv, int t_max, int c_max, int n_blk,
+                float* __restrict__ kbar) {
+  __shared__ float part[kSelThreads / D][D];
+  const int m = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const size_t grp = static_cast<size_t>(b) * Hkv + r;
+  constexpr int NQ = kSelThreads / D;
+  const int c = tid % D, q = tid / D;
+  const T* kb = K + (grp * t_max + static_cast<size_t>(m) * kBlock) * D + c;
+  float a = 0.f;
+  for (int j = q; j < kBlock; j += NQ) a += load_scalar<T>(kb + static_cast<size_t>(j) * D);
+  part[q][c] = a;
+  __syncthreads();
+  if (tid < D) {
+    float x = 0.f;
+    for (int qq = 0; qq < NQ; ++qq) x += part[qq][tid];
+    kbar[(grp * c_max + m) * D + tid] = x * (1.0f / kBlock);
+  }
+  (void)n_blk;
+}
+
+template <typename T, int D, int DS, int G>
+__global__ void __launch_bounds__(kSelThreads)
+qsb_rows_kernel(const T* __restrict__ Q, int q_len, const float* __restrict__ Wq,
+                const float* __restrict__ summ, const float* __restrict__ kbar,
+                const int32_t* __restrict__ idx, const float* __restrict__ score_lse,
+                const float* __restrict__ dlg, int Hkv, int c_max, int k,
+                float* __restrict__ ds_out, float* __restrict__ rowdat) {
+  constexpr int QS = D + 4, US = DS + 4;
+  constexpr int MS = (D > DS ? D : DS) + 4;   // staging row stride (summaries, then mean keys)
+  __shared__ __attribute__((aligned(16))) float qb[kQsbRows * QS];    // pooled queries
+  __shared__ __attribute__((aligned(16))) float u[kQsbRows * US];     // their projections
+  __shared__ __attribute__((aligned(16))) float stg[kQsbChunk * MS];
+  __shared__ float sc[kQsbRows][kQsbChunk + 1];                        // ds of the chunk
+  __shared__ float s_lse[kQsbRows], s_tot[kQsbRows];
+
+  const int t = blockIdx.x >> 1, r = blockIdx.y, b = blockIdx.z;
+  const int i0 = t * kBlock + (blockIdx.x & 1) * kQsbRows;
+  const int nq = min(kQsbRows, q_len - i0);
+  if (nq <= 0) return;   // second half of a short last tile (workgroup-uniform)
+  const int C = t;
+  const int tid = threadIdx.x;
+  const size_t grp = static_cast<size_t>(b) * Hkv + r;
+  const size_t row0 = grp * q_len + i0;
+
+  // pooled queries (G heads summed in head order, times 1/G)
+  {
+    constexpr int EPL = Vec16<T>::N, LPR = D / EPL;
+    for (int x = tid; x < kQsbRows * LPR; x += kSelThreads) {
+      const int q = x / LPR, col = x % LPR;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+      if (q < nq) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const T* src = Q + ((grp * G + h) * q_len + i0 + q) * D + col * EPL;
+          float f[EPL];
+          Vec16<T>::unpack(*reinterpret_cast<const uint4*>(src), f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += f[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qb[q * QS + col * EPL + e] = acc[e] * (1.0f / G);
+    }
+  }
+  if (tid < kQsbRows) {
+    float tot = 0.f;
+    if (tid < nq)
+      for (int slot = 0; slot < k; ++slot)
+        if (idx[(row0 + tid) * k + slot] >= 0) tot += dlg[(row0 + tid) * k + slot];
+    s_tot[tid] = tot;
+    s_lse[tid] = tid < nq ? score_lse[row0 + tid] : 0.f;
+  }
+  __syncthreads();
+  // u = Wq qbar / sqrt(DS)
+  {
+    constexpr int NQG = kSelThreads / DS, NE = kQsbRows / NQG;
+    const int c = tid % DS, qg = tid / DS;
+    float acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.f;
+    const float4* w = reinterpret_cast<const float4*>(Wq + static_cast<size_t>(c) * D);
+#pragma unroll 4
+    for (int j4 = 0; j4 < D / 4; ++j4) {
+      const float4 x = w[j4];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const float4 a = *reinterpret_cast<const float4*>(&qb[(qg + NQG * e) * QS + 4 * j4]);
+        acc[e] += x.x * a.x + x.y * a.y + x.z * a.z + x.w * a.w;
+      }
+    }
+    const float inv = 1.0f / sqrtf(static_cast<float>(DS));
+#pragma unroll
+    for (int e = 0; e < NE; ++e) u[(qg + NQG * e) * US + c] = acc[e] * inv;
+  }
+  // h: thread (hq, hc) keeps row hq's channels 16 hc .. 16 hc + 15 (D = 128)
+  // or 8 hc .. 8 hc + 7 (D = 64)
+  constexpr int HC = D / 8;   // channels per thread
+  const int hq = tid >> 3, hc = tid & 7;
+  float h[HC];
+#pragma unroll
+  for (int e = 0; e < HC; ++e) h[e] = 0.f;
+
+  const float* srow = summ + grp * static_cast<size_t>(c_max) * DS;
+  const float* krow = kbar + grp * static_cast<size_t>(c_max) * D;
+  for (int c0 = 0; c0 < C; c0 += kQsbChunk) {
+    const int nb = min(kQsbChunk, C - c0);
+    __syncthreads();   // u written / the previous chunk's readers of stg and sc are done
+    for (int x = tid; x < kQsbChunk * (DS / 4); x += kSelThreads) {
+      const int m = x / (DS / 4), c4 = x % (DS / 4);
+      const float4 v = m < nb ? *reinterpret_cast<const float4*>(srow + static_cast<size_t>(c0 + m) * DS + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&stg[m * MS + 4 * c4]) = v;
+    }
+    __syncthreads();
+    // ds = -g * (sum of the row's log-gate gradients) over the chunk's blocks
+    {
+      const int tq = tid >> 4, tm = tid & 15;
+      float acc[2][4];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[a][x] = 0.f;
+#pragma unroll 2
+      for (int j4 = 0; j4 < DS / 4; ++j4) {
+        float4 uq[2], sv[4];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) uq[a] = *reinterpret_cast<const float4*>(&u[(2 * tq + a) * US + 4 * j4]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sv[x] = *reinterpret_cast<const float4*>(&stg[(tm + 16 * x) * MS + 4 * j4]);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            acc[a][x] += uq[a].x * sv[x].x + uq[a].y * sv[x].y + uq[a].z * sv[x].z + uq[a].w * sv[x].w;
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int q = 2 * tq + a, m = tm + 16 * x;
+          sc[q][m] = (q < nq && m < nb) ? -expf(acc[a][x] - s_lse[q]) * s_tot[q] : 0.f;
+        }
+    }
+    __syncthreads();
+    // the selected blocks' own terms (block indices are distinct within a row)
+    for (int x = tid; x < nq * k; x += kSelThreads) {
+      const int q = x / k;
+      const int m = idx[row0 * k + x];
+      if (m >= c0 && m < c0 + nb) sc[q][m - c0] += dlg[row0 * k + x];
+    }
+    __syncthreads();
+    if (ds_out)
+      for (int x = tid; x < nq * nb; x += kSelThreads) {
+        const int q = x / nb, m = x % nb;
+        ds_out[(row0 + q) * c_max + c0 + m] = sc[q][m];
+      }
+    // stage the chunk's mean keys (the scores are done with the summaries)
+    for (int x = tid; x < kQsbChunk * (D / 4); x += kSelThreads) {
+      const int m = x / (D / 4), c4 = x % (D / 4);
+      const float4 v = m < nb ? *reinterpret_cast<const float4*>(krow + static_cast<size_t>(c0 + m) * D + 4 * c4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&stg[m * MS + 4 * c4]) = v;
+    }
+    __syncthreads();
+    // h += ds kbar, blocks in order
+#pragma unroll 2
+    for (int m = 0; m < nb; ++m) {
+      const float w = sc[hq][m];
+#pragma unroll
+      for (int e4 = 0; e4 < HC / 4; ++e4) {
+        const float4 kv = *reinterpret_cast<const float4*>(&stg[m * MS + HC * hc + 4 * e4]);
+        h[4 * e4 + 0] = fmaf(w, kv.x, h[4 * e4 + 0]);
+        h[4 * e4 + 1] = fmaf(w, kv.y, h[4 * e4 + 1]);
+        h[4 * e4 + 2] = fmaf(w, kv.z, h[4 * e4 + 2]);
+        h[4 * e4 + 3] = fmaf(w, kv.w, h[4 * e4 + 3]);
+      }
+    }
+  }
+  // rowdat: h [D], qbar [D] per row (rows past q_len are not stored)
+  if (hq < nq) {
+    float* rd = rowdat + (row0 + hq) * (2 * D);
+#pragma unroll
+    for (int e = 0; e < HC; ++e) rd[HC * hc + e] = h[e];
+    for (int e = 0; e < HC; ++e) rd[D + HC * hc + e] = qb[hq * QS + HC * hc + e];
+  }
+}
+
+// Partial of H = sum_rows h qbar^T over kQsbPartRows rows, staged 64 at a
+// time; thread (c, half) keeps H[half * D/2 + j][c], j < D/2.
+template <int D>
+__global__ void __launch_bounds__(2 * D)
+qsb_partial_kernel(size_t n_rows, const float* __restrict__ rowdat, float* __restrict__ partial) {
+  constexpr int JH = D / 2;
+  __shared__ float left[64][D];
+  __shared__ float right[64][D];
+  const int c = threadIdx.x % D, half = threadIdx.x / D;
+  const size_t e_begin = static_cast<size_t>(blockIdx.x) * kQsbPartRows;
+  const size_t e_end = e_begin + kQsbPartRows < n_rows ? e_begin + kQsbPartRows : n_rows;
+  float acc[JH];
+#pragma unroll
+  for (int j = 0; j < JH; ++j) acc[j] = 0.f;
+  for (size_t e0 = e_begin; e0 < e_end; e0 += 64) {
+    const int ne = static_cast<int>(e_end - e0 < 64 ? e_end - e0 : 64);
+    __syncthreads();
+    for (int x = threadIdx.x; x < ne * D; x += 2 * D) {
+      const float* rd = rowdat + (e0 + x / D) * (2 * D);
+      left[x / D][x % D] = rd[x % D];
+      right[x / D][x % D] = rd[D + x % D];
+    }
+    __syncthreads();
+    for (int e = 0; e < ne; ++e) {
+      const float rv = right[e][c];
+#pragma unroll
+      for (int j = 0; j < JH; ++j) acc[j] = fmaf(left[e][half * JH + j], rv, acc[j]);
+    }
+  }
+  float* out = partial + (static_cast<size_t>(blockIdx.x) * D + half * JH) * D + c;
+#pragma unroll
+  for (int j = 0; j < JH; ++j) out[static_cast<size_t>(j) * D] = acc[j];
+}
+
+// H = sum of the partials in chunk order.
+template <int D>
+__global__ void __launch_bounds__(D)
+qsb_sum_kernel(int n_chunks, const float* __restrict__ partial, float* __restrict__ H) {
+  const int x = blockIdx.x, c = threadIdx.x;
+  float a = 0.f;
+  for (int ch = 0; ch < n_chunks; ++ch) a += partial[(static_cast<size_t>(ch) * D + x) * D + c];
+  H[x * D + c] = a;
+}
+
+// dWq[j][c] = sum_x Wk[j][x] H[x][c] / sqrt(DS); dWk[j][c] = sum_x Wq[j][x] H[c][x] / sqrt(DS).
+template <int D, int DS>
+__global__ void __launch_bounds__(D)
+qsb_weights_kernel(const float* __restrict__ Wq, const float* __restrict__ Wk,
+                   const float* __restrict__ H, float* __restrict__ dWq, float* __restrict__ dWk) {
+  const int which = blockIdx.y, j = blockIdx.x, c = threadIdx.x;
+  const float inv = 1.0f / sqrtf(static_cast<float>(DS));
+  float a = 0.f;
+  if (which == 0) {
+    for (int x = 0; x < D; ++x) a = fmaf(Wk[j * D + x], H[x * D + c], a);
+    dWq[j * D + c] = a * inv;
+  } else {
+    for (int x = 0; x < D; ++x) a = fmaf(Wq[j * D + x], H[c * D + x], a);
+    dWk[j * D + c] = a * inv;
+  }
+}
+
+// workspace: kbar [grp * c_max * D] | rowdat [grp * q_len * 2D] |
+//            partial [chunks * D * D] | H [D * D]
+static size_t qsb_chunks(const sas_dims& d, int q_len) {
+  const size_t rows = static_cast<size_t>(d.batch) * d.n_kv_heads * q_len;
+  return (rows + kQsbPartRows - 1) / kQsbPartRows;
+}
+size_t selector_bwd_queries_ws_bytes(const sas_dims& d, int q_len) {
+  const size_t grp = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  const size_t c_max = d.t_max / kBlock, D = d.head_dim;
+  return align256(grp * c_max * D * sizeof(float)) +
+         align256(grp * q_len * 2 * D * sizeof(float)) +
+         align256(qsb_chunks(d, q_len) * D * D * sizeof(float)) + D * D * sizeof(float);
+}
+
+template <typename T, int D, int DS, int G>
+static sas_status launch_qsb(const sas_dims& d, const void* Q, int q_len, const void* K,
+                             const float* Wq, const float* Wk, const float* summ,
+                             const int32_t* idx, const float* score_lse, const float* dlg,
+                             float* ds, float* dWq, float* dWk, void* ws, hipStream_t st) {
+  const size_t grp = static_cast<size_t>(d.batch) * d.n_kv_heads;
+  const int c_max = d.t_max / kBlock;
+  const int n_tiles = cdiv(q_len, kBlock);
+  char* w = static_cast<char*>(ws);
+  float* kbar = reinterpret_cast<float*>(w);
+  w += align256(grp * c_max * D * sizeof(float));
+  float* rowdat = reinterpret_cast<float*>(w);
+  w += align256(grp * q_len * 2 * D * sizeof(float));
+  float* partial = reinterpret_cast<float*>(w);
+  const int n_chunks = static_cast<int>(qsb_chunks(d, q_len));
+  w += align256(static_cast<size_t>(n_chunks) * D * D * sizeof(float));
+  float* H = reinterpret_cast<float*>(w);
+  if (n_tiles > 1) {   // history blocks 0 .. n_tiles - 2
+    hipLaunchKernelGGL((qsb_kbar_kernel<T, D>), dim3(n_tiles - 1, d.n_kv_heads, d.batch),
+                       dim3(kSelThreads), 0, st, static_cast<const T*>(K), d.n_kv_heads, d.t_max,
+                       c_max, n_tiles - 1, kbar);
+    sas_status s = check_launch("selector_bwd_queries_kbar");
+    if (s != SAS_OK) return s;
+  }
+  hipLaunchKernelGGL((qsb_rows_kernel<T, D, DS, G>), dim3(2 * n_tiles, d.n_kv_heads, d.batch),
+                     dim3(kSelThreads), 0, st, static_cast<const T*>(Q), q_len, Wq, summ, kbar,
+                     idx, score_lse, dlg, d.n_kv_heads, c_max, d.top_k, ds, rowdat);
+  sas_status s = check_launch("selector_bwd_queries_rows");
+  if (s != SAS_OK) return s;
+  hipLaunchKernelGGL((qsb_partial_kernel<D>), dim3(n_chunks), dim3(2 * D), 0, st,
+                     grp * static_cast<size_t>(q_len), rowdat, partial);
+  s = check_launch("selector_bwd_queries_partial");
+  if (s != SAS_OK) return s;
+  hipLaunchKernelGGL((qsb_sum_kernel<D>), dim3(D), dim3(D), 0, st, n_chunks, partial, H);
+  s = check_launch("selector_bwd_queries_sum");
+  if (s != SAS_OK) return s;
+  hipLaunchKernelGGL((qsb_weights_kernel<D, DS>), dim3(DS, 2), dim3(D), 0, st, Wq, Wk, H, dWq,
+                     dWk);
+  return check_launch("selector_bwd_queries_weights");
+}
+
+template <typename T, int D, int DS>
+static sas_status qsb_by_group(const sas_dims& d, const void* Q, int q_len, const void* K,
+                               const float* Wq, const float* Wk, const float* summ,
+                               const int32_t* idx, const float* score_lse, const float* dlg,
+                               float* ds, float* dWq, float* dWk, void* ws, hipStream_t st) {
+  switch (d.n_q_heads / d.n_kv_heads) {
+    case 1: return launch_qsb<T, D, DS, 1>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+    case 2: return launch_qsb<T, D, DS, 2>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+    case 4: return launch_qsb<T, D, DS, 4>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+    case 8: return launch_qsb<T, D, DS, 8>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+  }
+  return fail(SAS_ERR_UNSUPPORTED, "selector backward: group size");
+}
+
+template <typename T>
+static sas_status qsb_by_dims(const sas_dims& d, const void* Q, int q_len, const void* K,
+                              const float* Wq, const float* Wk, const float* summ,
+                              const int32_t* idx, const float* score_lse, const float* dlg,
+                              float* ds, float* dWq, float* dWk, void* ws, hipStream_t st) {
+  if (d.head_dim == 128 && d.sel_dim == 128)
+    return qsb_by_group<T, 128, 128>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+  if (d.head_dim == 128)
+    return qsb_by_group<T, 128, 64>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+  if (d.sel_dim == 128)
+    return qsb_by_group<T, 64, 128>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+  return qsb_by_group<T, 64, 64>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+}
+
+sas_status launch_selector_bwd_queries(const sas_dims& d, const void* Q, int q_len,
+                                       const void* K, const float* Wq, const float* Wk,
+                                       const float* summ, const int32_t* idx,
+                                       const float* score_lse, const float* dlg, float* ds,
+                                       float* dWq, float* dWk, void* ws, hipStream_t st) {
+  if (d.dtype == SAS_BF16)
+    return qsb_by_dims<uint16_t>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+  return qsb_by_dims<float>(d, Q, q_len, K, Wq, Wk, summ, idx, score_lse, dlg, ds, dWq, dWk, ws, st);
+}
+
 sas_status launch_selector_bwd(const sas_dims& d, const void* Q, int q_len, const void* K,
                                const float* Wq, const float* summ, const int32_t* idx,
                                const float* score_lse, const float* dlg, float* ds, float* dWq,

@@ -81,7 +81,8 @@ typedef enum {
   SAS_OP_SELECTOR_BWD = 6,
   SAS_OP_SELECT_QUERIES = 7,
   SAS_OP_PREFILL_FWD_QUERIES = 8,
-  SAS_OP_BWD_QUERIES = 9
+  SAS_OP_BWD_QUERIES = 9,
+  SAS_OP_SELECTOR_BWD_QUERIES = 10
 } sas_op;
 
 /* Problem sizes.  Supported: block_size 64; head_dim and sel_dim 64 or 128;
@@ -304,6 +305,28 @@ sas_status sas_selector_bwd(const sas_dims* dims, const void* Q, int32_t q_len, 
                             const float* score_lse, const float* dlog_gate, float* ds,
                             float* dWq_sel, float* dWk_sel, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* The selector backward for per-query rows (one selection per query, as
+ * written by sas_select(SAS_SELECT_QUERIES) and differentiated by
+ * sas_bwd_queries; SAS close reading 2.2-2.4): row (b, r, i) has the C = i/64
+ * blocks before query i's block and the pooled query qbar_i (mean of query i
+ * over the group's heads); ds over those blocks as for sas_selector_bwd, and
+ *     dWq_sel = sum_rows sum_m ds_m summ_m qbar_i^T / sqrt(d_sel),
+ *     dWk_sel = sum_rows sum_m ds_m (Wq_sel qbar_i / sqrt(d_sel)) kbar_m^T,
+ * computed through H = sum_rows (sum_m ds_m kbar_m) qbar_i^T as
+ * Wk_sel H / sqrt(d_sel) and Wq_sel H^T / sqrt(d_sel) (hence Wk_sel).
+ * Q: [B,Hq,q_len,d]; K: [B,Hkv,t_max,d]; Wq_sel, Wk_sel: fp32 [d_sel,d];
+ * summ as read by the selection; idx/dlog_gate [B,Hkv,q_len,k]; score_lse
+ * [B,Hkv,q_len]; ds (nullable) fp32 [B,Hkv,q_len,t_max/64] (entry m < C of a
+ * row); dWq_sel, dWk_sel fp32 [d_sel,d], overwritten.  q_len <= t_max and
+ * ceil(q_len/64) <= 1024.  Bitwise reproducible (no atomics).
+ * ws: at least sas_workspace_bytes(SAS_OP_SELECTOR_BWD_QUERIES, dims, q_len). */
+sas_status sas_selector_bwd_queries(const sas_dims* dims, const void* Q, int32_t q_len,
+                                    const void* K, const float* Wq_sel, const float* Wk_sel,
+                                    const float* summ, const int32_t* idx,
+                                    const float* score_lse, const float* dlog_gate, float* ds,
+                                    float* dWq_sel, float* dWk_sel, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /* Workspace bytes an op needs for these sizes (q_len: prefill/tiles length,
  * ignored otherwise).  Returns SIZE_MAX if the sizes are invalid or

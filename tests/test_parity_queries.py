@@ -349,3 +349,118 @@ def test_queries_batch2_select_fwd_bwd():
         e = np.linalg.norm(host(dlg)[b][valid] - rlg[valid]) / np.linalg.norm(rlg[valid])
         assert e <= TOL_GRAD_REL, (b, e)
         log(f"[queries batch2] sequence {b}: max|O-O_ref|={err:.3g} rel dlog_gate={e:.3g}")
+
+
+# --------------------------------------------------------------------------
+# selector backward for per-query rows
+# --------------------------------------------------------------------------
+def run_selector_queries_case(p, dlg_from="random", label=""):
+    """sas_selector_bwd_queries against the oracle's query_selector_backward;
+    both sides get the oracle's per-query selection, score LSE and log-gate
+    gradients (seeded random ones, or the oracle's query_backward of the
+    attention loss)."""
+    S_ = _sas()
+    wl = p.wl
+    S, Hkv, G, k, dt, d = int(p.seq_lens[0]), wl.n_kv_heads, wl.group, wl.top_k, wl.dtype, wl.head_dim
+    t_max = p.K.shape[2]
+    log(f"[selector bwd queries {label}] S={S} Hq={wl.n_q_heads} Hkv={Hkv} d={d} "
+        f"d_sel={wl.sel_dim} k={k} {dt}")
+    Qf, Kf = synth.to_f64(p.q[0], dt), synth.to_f64(p.K[0], dt)
+    sel = O.query_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+    idx, lse = sel["idx"], sel["score_lse"]
+    if dlg_from == "random":
+        rng = np.random.default_rng(S + k)
+        dlg = rng.standard_normal(idx.shape) * 0.1 * (idx >= 0)
+    else:
+        Vf, dOf = synth.to_f64(p.V[0], dt), synth.to_f64(p.dO[0], dt)
+        dlg = O.query_backward(Qf, Kf, Vf, dOf, S, idx, sel["log_gate"], 1.0 / math.sqrt(d), G)[3]
+    Q, K = dev(p.q), dev(p.K)
+    Wq, Wk = dev(p.Wq_sel), dev(p.Wk_sel)
+    summ = S_.sas_block_summaries(K, torch.tensor([S], dtype=torch.int32).cuda(), Wk)
+    dWq_g, dWk_g, ds_g = S_.sas_selector_bwd_queries(
+        Q, K, Wq, Wk, summ, idx_dev(idx[None]), lg_dev(lse[None]), lg_dev(dlg[None]),
+        t_max=t_max, want_ds=True)
+    torch.cuda.synchronize()
+    ds_rows, dWq_r, dWk_r = O.query_selector_backward(Qf, Kf, S, p.f64("Wq_sel"),
+                                                      p.f64("Wk_sel"), idx, dlg, G)
+    ds_h = host(ds_g)[0]
+    got = np.concatenate([ds_h[:, i, :i // 64].ravel() for i in range(S)])
+    ref = np.concatenate([ds_rows[i].ravel() for i in range(S)])
+    e_ds = rel_l2(got, ref) if ref.size else 0.0
+    e_q, e_k = rel_l2(host(dWq_g), dWq_r), rel_l2(host(dWk_g), dWk_r)
+    log(f"[selector bwd queries {label}] rel ds={e_ds:.3g} dWq={e_q:.3g} dWk={e_k:.3g}")
+    assert max(e_ds, e_q, e_k) <= TOL_GRAD_REL
+    return dWq_g, dWk_g
+
+
+def rel_l2(x, ref):
+    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,ds,k,dtype", [
+    (64, 4, 1, 128, 128, 4, "bf16"), (100, 4, 1, 128, 128, 4, "bf16"),
+    (1000, 8, 2, 128, 128, 3, "bf16"), (700, 16, 2, 64, 64, 6, "bf16"),
+    (777, 2, 2, 64, 128, 5, "f32"), (640, 8, 1, 128, 64, 16, "bf16"), (1, 4, 1, 128, 128, 2, "bf16"),
+    (333, 8, 2, 128, 128, 0, "bf16"), (900, 4, 4, 128, 128, 64, "bf16"),
+])
+def test_selector_bwd_queries_small(S, Hq, Hkv, d, ds, k, dtype):
+    run_selector_queries_case(_problem(S, Hq, Hkv, d, ds, k, dtype=dtype, seed=S + 3 * Hq),
+                              label=f"S={S}")
+
+
+def test_selector_bwd_queries_from_attention_backward():
+    run_selector_queries_case(_problem(640, 4, 1, 128, 128, 4, seed=17), dlg_from="attention",
+                              label="end to end")
+
+
+@pytest.mark.timeout(900)
+def test_selector_bwd_queries_full_workload():
+    """S = 16384 (Qwen3-4B head shape, k = 16): (1) with queries equal within
+    each tile and every query carrying its tile's selection, the per-query
+    selector gradients equal the tile rows' (sas_selector_bwd) with each
+    tile's log-gate gradients summed over its queries; (2) ds of sampled rows
+    against the oracle; (3) two runs give the same bits."""
+    S_ = _sas()
+    p = synth.make_problem(synth.WORKLOADS["qwen3_4b_prefill_16k"], seed=0)
+    wl = p.wl
+    S, Hkv, G, k = int(p.seq_lens[0]), wl.n_kv_heads, wl.group, wl.top_k
+    n_tiles = S // 64
+    q_tile = p.q.copy()
+    for t in range(n_tiles):
+        q_tile[:, :, 64 * t:64 * t + 64] = q_tile[:, :, 64 * t:64 * t + 1]
+    Q, K = dev(q_tile), dev(p.K)
+    Wq, Wk = dev(p.Wq_sel), dev(p.Wk_sel)
+    summ = S_.sas_block_summaries(K, torch.tensor([S], dtype=torch.int32).cuda(), Wk)
+    idx_t, _, lse_t, _ = S_.sas_select(S_.SAS_SELECT_TILES, Q, None, Wq, summ, k, t_max=S)
+    _, _, lse_q, _ = S_.sas_select(S_.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S)
+    rng = np.random.default_rng(5)
+    it = idx_t.cpu().numpy()
+    tile_of = np.arange(S) // 64
+    dlg_q = (rng.standard_normal((1, Hkv, S, k)) * 0.1 * (it[:, :, tile_of] >= 0)).astype(np.float32)
+    dlg_t = dlg_q.reshape(1, Hkv, n_tiles, 64, k).sum(axis=3, dtype=np.float64).astype(np.float32)
+    iq = idx_t[:, :, tile_of].contiguous()
+    qWq, qWk, qds = S_.sas_selector_bwd_queries(Q, K, Wq, Wk, summ, iq, lse_q,
+                                                torch.from_numpy(dlg_q).cuda(), want_ds=True)
+    tWq, tWk, _ = S_.sas_selector_bwd(Q, K, Wq, summ, idx_t, lse_t, torch.from_numpy(dlg_t).cuda())
+    torch.cuda.synchronize()
+    e_q, e_k = rel_l2(host(qWq), host(tWq)), rel_l2(host(qWk), host(tWk))
+    log(f"[selector bwd queries S=16384] per-query vs tile rows: rel dWq={e_q:.3g} dWk={e_k:.3g}")
+    assert max(e_q, e_k) <= 1e-4
+    # ds of sampled rows against the oracle's score gradient of those rows
+    Qf, Kf = synth.to_f64(q_tile[0], "bf16"), synth.to_f64(p.K[0], "bf16")
+    summ_f = O.block_summaries(Kf, S, p.f64("Wk_sel"))
+    rows = [0, 64, 65, 1000, 4097, 9999, 16383]
+    sc = O.query_scores(Qf, S, p.f64("Wq_sel"), summ_f, G, queries=rows)
+    ds_h = host(qds)[0]
+    iq_h = iq.cpu().numpy()[0]
+    for i in rows:
+        for r in range(Hkv):
+            ref = O.score_grad(sc[i][r], iq_h[r, i], dlg_q[0, r, i].astype(np.float64))
+            got = ds_h[r, i, :i // 64]
+            if ref.size:
+                assert rel_l2(got, ref) <= TOL_GRAD_REL, (i, r)
+    # determinism
+    qWq2, qWk2, _ = S_.sas_selector_bwd_queries(Q, K, Wq, Wk, summ, iq, lse_q,
+                                                torch.from_numpy(dlg_q).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(qWq, qWq2) and torch.equal(qWk, qWk2)
