@@ -532,11 +532,12 @@ def run_prefill(args, wl):
     Oq, lseq = Sb.sas_prefill_fwd_queries(Q, K, V, qidx, qlg)
     ws_qbwd = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_BWD_QUERIES, dims, S)), dtype=torch.uint8, device=dev)
     qdlg = torch.empty(qidx.shape, dtype=torch.float32, device=dev)
-    t_qsel, t_qfwd, t_qbwd = [], [], []
+    ws_qsb = torch.zeros(max(1, Sb.sas_workspace_bytes(Sb.SAS_OP_SELECTOR_BWD_QUERIES, dims, S)), dtype=torch.uint8, device=dev)
+    t_qsel, t_qfwd, t_qbwd, t_qsb = [], [], [], []
     for i in range(n):
         if not args.no_flush:
             flush(i)
-        e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+        e0, e1, e2, e3, e4 = (torch.cuda.Event(enable_timing=True) for _ in range(5))
         e0.record(stream)
         Sb.sas_select(Sb.SAS_SELECT_QUERIES, Q, None, Wq, summ, k, t_max=S, idx=qidx,
                       log_gate=qlg, score_lse=qlse)
@@ -546,10 +547,14 @@ def run_prefill(args, wl):
         Sb.sas_bwd_queries(Q, K, V, Oq, dO, lseq, qidx, qlg, dQ=dQ, dK=dK, dV=dV, dlog_gate=qdlg,
                            ws=ws_qbwd)
         e3.record(stream)
+        Sb.sas_selector_bwd_queries(Q, K, Wq, Wk, summ, qidx, qlse, qdlg, dWq=dWq, dWk=dWk,
+                                    ws=ws_qsb)
+        e4.record(stream)
         torch.cuda.synchronize()
         t_qsel.append(e0.elapsed_time(e1) * 1e3)
         t_qfwd.append(e1.elapsed_time(e2) * 1e3)
         t_qbwd.append(e2.elapsed_time(e3) * 1e3)
+        t_qsb.append(e3.elapsed_time(e4) * 1e3)
     qsel_pairs, qvis_pairs = query_pairs(S, Hq // Hkv, qidx.cpu().numpy())
 
     med = statistics.median
@@ -578,6 +583,7 @@ def run_prefill(args, wl):
             "per_query_select": {"median": round(med(t_qsel), 2), "p10": round(_pct(t_qsel, .1), 2), "p90": round(_pct(t_qsel, .9), 2)},
             "per_query_fwd": {"median": round(us_qfwd, 2), "p10": round(_pct(t_qfwd, .1), 2), "p90": round(_pct(t_qfwd, .9), 2)},
             "per_query_bwd": {"median": round(med(t_qbwd), 2), "p10": round(_pct(t_qbwd, .1), 2), "p90": round(_pct(t_qbwd, .9), 2)},
+            "per_query_selector_bwd": {"median": round(med(t_qsb), 2), "p10": round(_pct(t_qsb, .1), 2), "p90": round(_pct(t_qsb, .9), 2)},
         },
         "per_query": {
             "selected_pairs": qsel_pairs, "visited_pairs": qvis_pairs,
