@@ -336,22 +336,29 @@ bwd_qsel_prep_kernel(int S, int Hkv, int n_tiles, int k, const int32_t* __restri
                      int* __restrict__ ucnt, float* __restrict__ table, int* __restrict__ qcnt) {
   __shared__ uint32_t bits[kUnionWords];
   __shared__ int cnt[kUnionWords];
+  __shared__ int bcnt[kMaxTileRows];   // queries of this tile selecting each block
   const int t = blockIdx.x, r = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const size_t grow = static_cast<size_t>(b) * Hkv + r;
   const size_t qrow0 = grow * S + static_cast<size_t>(t) * 64;
   const int n_ent = min(64, S - 64 * t) * k;
   float* tab = table + grow * qsel_rows(n_tiles) * 64;
   if (tid < kUnionWords) bits[tid] = 0u;
+  for (int m = tid; m < t; m += 256) bcnt[m] = 0;
   if (t == 0 && tid < 64) tab[tid] = 0.f;   // row 0: the diagonal block's zero gates
   __syncthreads();
   for (int e = tid; e < n_ent; e += 256) {
     const int m = idx[qrow0 * k + e];
     if (m >= 0) {
       atomicOr(&bits[m >> 5], 1u << (m & 31));
-      if (qcnt) atomicAdd(&qcnt[grow * n_tiles + m], 1);   // selecting queries of block m
+      atomicAdd(&bcnt[m], 1);
     }
   }
   __syncthreads();
+  // selecting queries of block m over all tiles: one integer add per (tile,
+  // selected block) (order-free, so the totals are exact and reproducible)
+  if (qcnt)
+    for (int m = tid; m < t; m += 256)
+      if (bcnt[m]) atomicAdd(&qcnt[grow * n_tiles + m], bcnt[m]);
   if (tid < 64) {
     const uint32_t w = tid < kUnionWords ? bits[tid] : 0u;
     int incl = __popc(w);

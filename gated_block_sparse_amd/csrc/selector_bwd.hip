@@ -288,7 +288,7 @@ static sas_status sbwd_by_dims(const sas_dims& d, const void* Q, int q_len, cons
 // of H; H and the two small products.
 constexpr int kQsbRows = 32;      // rows per workgroup of the row kernel
 constexpr int kQsbChunk = 64;     // blocks per scoring pass
-constexpr int kQsbPartRows = 1024;  // rows per H partial
+constexpr int kQsbPartRows = 512;   // rows per H partial
 
 template <typename T, int D>
 __global__ void __launch_bounds__(kSelThreads)
@@ -482,37 +482,53 @@ qsb_rows_kernel(const T* __restrict__ Q, int q_len, const float* __restrict__ Wq
 }
 
 // Partial of H = sum_rows h qbar^T over kQsbPartRows rows, staged 64 at a
-// time; thread (c, half) keeps H[half * D/2 + j][c], j < D/2.
+// time; thread (ti, tj) of a 16 x 16 grid keeps the TR x TR block of H at
+// rows TR ti.., columns TR tj.. in registers, so each staged value feeds TR
+// multiply-adds.
 template <int D>
-__global__ void __launch_bounds__(2 * D)
+__global__ void __launch_bounds__(256)
 qsb_partial_kernel(size_t n_rows, const float* __restrict__ rowdat, float* __restrict__ partial) {
-  constexpr int JH = D / 2;
-  __shared__ float left[64][D];
-  __shared__ float right[64][D];
-  const int c = threadIdx.x % D, half = threadIdx.x / D;
+  constexpr int TR = D / 16;
+  __shared__ __attribute__((aligned(16))) float left[64][D];
+  __shared__ __attribute__((aligned(16))) float right[64][D];
+  const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
   const size_t e_begin = static_cast<size_t>(blockIdx.x) * kQsbPartRows;
   const size_t e_end = e_begin + kQsbPartRows < n_rows ? e_begin + kQsbPartRows : n_rows;
-  float acc[JH];
+  float acc[TR][TR];
 #pragma unroll
-  for (int j = 0; j < JH; ++j) acc[j] = 0.f;
+  for (int a = 0; a < TR; ++a)
+#pragma unroll
+    for (int c = 0; c < TR; ++c) acc[a][c] = 0.f;
   for (size_t e0 = e_begin; e0 < e_end; e0 += 64) {
     const int ne = static_cast<int>(e_end - e0 < 64 ? e_end - e0 : 64);
     __syncthreads();
-    for (int x = threadIdx.x; x < ne * D; x += 2 * D) {
-      const float* rd = rowdat + (e0 + x / D) * (2 * D);
-      left[x / D][x % D] = rd[x % D];
-      right[x / D][x % D] = rd[D + x % D];
+    for (int x = tid; x < ne * (D / 4); x += 256) {
+      const int e = x / (D / 4), c4 = x % (D / 4);
+      const float* rd = rowdat + (e0 + e) * (2 * D);
+      *reinterpret_cast<float4*>(&left[e][4 * c4]) = *reinterpret_cast<const float4*>(rd + 4 * c4);
+      *reinterpret_cast<float4*>(&right[e][4 * c4]) = *reinterpret_cast<const float4*>(rd + D + 4 * c4);
     }
     __syncthreads();
     for (int e = 0; e < ne; ++e) {
-      const float rv = right[e][c];
+      float l[TR], rr[TR];
 #pragma unroll
-      for (int j = 0; j < JH; ++j) acc[j] = fmaf(left[e][half * JH + j], rv, acc[j]);
+      for (int a4 = 0; a4 < TR / 4; ++a4) {
+        const float4 x = *reinterpret_cast<const float4*>(&left[e][TR * ti + 4 * a4]);
+        const float4 y = *reinterpret_cast<const float4*>(&right[e][TR * tj + 4 * a4]);
+        l[4 * a4] = x.x; l[4 * a4 + 1] = x.y; l[4 * a4 + 2] = x.z; l[4 * a4 + 3] = x.w;
+        rr[4 * a4] = y.x; rr[4 * a4 + 1] = y.y; rr[4 * a4 + 2] = y.z; rr[4 * a4 + 3] = y.w;
+      }
+#pragma unroll
+      for (int a = 0; a < TR; ++a)
+#pragma unroll
+        for (int c = 0; c < TR; ++c) acc[a][c] = fmaf(l[a], rr[c], acc[a][c]);
     }
   }
-  float* out = partial + (static_cast<size_t>(blockIdx.x) * D + half * JH) * D + c;
+  float* out = partial + static_cast<size_t>(blockIdx.x) * D * D;
 #pragma unroll
-  for (int j = 0; j < JH; ++j) out[static_cast<size_t>(j) * D] = acc[j];
+  for (int a = 0; a < TR; ++a)
+#pragma unroll
+    for (int c = 0; c < TR; ++c) out[(TR * ti + a) * D + TR * tj + c] = acc[a][c];
 }
 
 // H = sum of the partials in chunk order.
@@ -585,7 +601,7 @@ static sas_status launch_qsb(const sas_dims& d, const void* Q, int q_len, const 
                      idx, score_lse, dlg, d.n_kv_heads, c_max, d.top_k, ds, rowdat);
   sas_status s = check_launch("selector_bwd_queries_rows");
   if (s != SAS_OK) return s;
-  hipLaunchKernelGGL((qsb_partial_kernel<D>), dim3(n_chunks), dim3(2 * D), 0, st,
+  hipLaunchKernelGGL((qsb_partial_kernel<D>), dim3(n_chunks), dim3(256), 0, st,
                      grp * static_cast<size_t>(q_len), rowdat, partial);
   s = check_launch("selector_bwd_queries_partial");
   if (s != SAS_OK) return s;
