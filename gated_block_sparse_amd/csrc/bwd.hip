@@ -23,6 +23,7 @@
 //     the only writer of dK/dV for its block and of the dlog_gate entries
 //     that point at it, which it sums in a fixed order.
 #include <climits>
+#include <type_traits>
 
 #include "sas_device.h"
 #include "sas_internal.h"
@@ -170,9 +171,44 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
   __syncthreads();
   const int nblk = s_nblk;
-  // per-thread share of one block's K and V rows (16-byte chunks), loaded into
-  // registers one block ahead of its LDS store
-  constexpr int TOT = 64 * (D / 8), CH = (TOT + NT - 1) / NT;
+  // Per-query mode: K (twice: row-read and transpose-read strides) and V of a
+  // block are staged by LDS DMA (global_load_lds_dwordx4), which keeps the
+  // kernel's registers (the gate cursor takes a few more) clear of staging
+  // values: 238 VGPRs and no spill, 4150 -> 3680 us at S = 16384.  (With
+  // one selection per tile the register staging below measured faster:
+  // 509 against 536 us.)  One copy instruction fills
+  // 64 consecutive 16-byte positions of a padded tile, so a row of RS
+  // elements takes RS / 8 positions and a tile RS / 8 instructions; a lane
+  // whose position is row padding fetches the row's first chunk again.  Rows
+  // past the sequence end repeat its last row (finite; their probabilities
+  // are masked to zero).  Block i + 1 is copied into the other buffer while
+  // block i computes.
+  constexpr int NW = NT / 64;
+  auto copy_tile = [&](const uint16_t* src, int valid, uint32_t dst, auto rs_tag) {
+    constexpr int RS = decltype(rs_tag)::value, POS = RS / 8;
+#pragma unroll
+    for (int n = 0; n < (POS + NW - 1) / NW; ++n) {
+      const int ins = min(wave + NW * n, POS - 1);
+      const int pos = 64 * ins + lane, row = pos / POS, c = pos % POS;
+      lds_dma<16>(src + static_cast<size_t>(min(row, valid - 1)) * D + 8 * (c < D / 8 ? c : 0),
+                  dst + 1024 * ins);
+    }
+  };
+  using RowTag = std::integral_constant<int, kRowStride<D>>;
+  using TrTag = std::integral_constant<int, kTrStride<D>>;
+  const uint32_t ks_lds = lds_addr_of(&Ks[0][0]), kt_lds = lds_addr_of(&Kt[0][0]),
+                 vs_lds = lds_addr_of(&Vs[0][0]);
+  auto copy_block = [&](int i, int buf) {
+    const int tok = s_blk[i] * 64;
+    const uint16_t* kb = Kg + static_cast<size_t>(tok) * D;
+    const uint16_t* vb = Vg + static_cast<size_t>(tok) * D;
+    copy_tile(kb, S - tok, ks_lds + buf * (64 * kRowStride<D> * 2), RowTag{});
+    copy_tile(kb, S - tok, kt_lds + buf * (64 * kTrStride<D> * 2), TrTag{});
+    copy_tile(vb, S - tok, vs_lds + buf * (64 * kRowStride<D> * 2), RowTag{});
+  };
+  // Tile mode: each thread's share of the block's K and V rows (16-byte
+  // chunks) is loaded into registers one block ahead of its LDS store.
+  constexpr int TOT = 64 * (D / 8), CH = PQ ? 1 : (TOT + NT - 1) / NT;
   uint4 kreg[CH], vreg[CH];
   auto load_block = [&](int i) {
     const int tok = s_blk[i] * 64;
@@ -197,9 +233,14 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
     }
   };
-  load_block(0);
-  store_block(0);
-  __syncthreads();
+  if constexpr (PQ) {
+    copy_block(0, 0);
+    dma_sync<0>();
+  } else {
+    load_block(0);
+    store_block(0);
+    __syncthreads();
+  }
 
   for (int it = 0; it < nblk; ++it) {
     const bool diag = it == nblk - 1;
@@ -217,7 +258,10 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
     float dsq = 0.f;   // PQ: sum of dS over the block's tokens (this lane's rows)
     const int buf = it & 1;
-    if (it + 1 < nblk) load_block(it + 1);   // in flight while this block computes
+    if (it + 1 < nblk) {   // lands (PQ) or is in flight (tile) while this block computes
+      if constexpr (PQ) copy_block(it + 1, buf ^ 1);
+      else load_block(it + 1);
+    }
     const float off = beta2 - lse2;
     // one 32-token half at a time, so only one S^T / dP^T pair is live
 #pragma unroll
@@ -262,8 +306,12 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (hit_slot >= 0 && hi == 0)
         part[((static_cast<size_t>(b) * Hq + h) * S + qi) * k + hit_slot] = dsq;
     }
-    if (it + 1 < nblk) store_block(buf ^ 1);
-    __syncthreads();
+    if constexpr (PQ) {
+      dma_sync<0>();   // the next block has landed; every wave is done with this one
+    } else {
+      if (it + 1 < nblk) store_block(buf ^ 1);
+      __syncthreads();
+    }
   }
   if (qvalid) store_acc_col<CT>(dq, scale, dQ + qrow_i * D, hi);
 }
