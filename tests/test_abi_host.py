@@ -194,3 +194,61 @@ def test_workspace_sizes(lib):
         B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, _dims(head_dim=96))
     with pytest.raises(B.SasError):
         B.sas_workspace_bytes(B.SAS_OP_PREFILL_FWD, d, 0)
+
+
+def test_per_query_calls_validation(lib):
+    """The per-query selection path: the QUERIES select mode, the forward,
+    the backward and the selector backward reject what they do not support
+    before enqueueing anything, and size their workspaces."""
+    d = _dims()
+    sel = lambda dims, q_len: lib.sas_select(
+        ctypes.byref(dims), B.SAS_SELECT_QUERIES, FAKE, q_len, None, FAKE, FAKE, FAKE, FAKE,
+        FAKE, None, None, 0, None)
+    assert sel(d, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sel(d, 65537) == B.SAS_ERR_INVALID_ARGUMENT               # q_len > t_max
+    big = _dims(t_max=64 * 1025 * 64)
+    assert sel(big, 64 * 1025) == B.SAS_ERR_UNSUPPORTED               # more than 1024 tiles
+    assert B.sas_workspace_bytes(B.SAS_OP_SELECT_QUERIES, d, 16384) == 0
+
+    pf = lambda dims, seq_len, idx=FAKE: lib.sas_prefill_fwd_queries(
+        ctypes.byref(dims), FAKE, FAKE, FAKE, seq_len, idx, FAKE, 0.1, FAKE, FAKE, None, 0, None)
+    assert pf(d, 0) == B.SAS_ERR_INVALID_ARGUMENT
+    assert pf(d, 128, idx=None) == B.SAS_ERR_INVALID_ARGUMENT          # idx NULL with k > 0
+    assert pf(_dims(dtype=B.SAS_F32), 128) == B.SAS_ERR_UNSUPPORTED
+    assert pf(big, 64 * 1025) == B.SAS_ERR_UNSUPPORTED
+    assert B.sas_workspace_bytes(B.SAS_OP_PREFILL_FWD_QUERIES, d, 16384) == 0
+
+    # backward workspace: that of sas_bwd plus the per-head log-gate partials,
+    # the union bitmaps and their prefix counts, the gate rows and the
+    # per-block query lists (each region 256-byte aligned)
+    S, k, grp, n_tiles = 16384, 16, 8, 256
+    al = lambda x: (x + 255) // 256 * 256
+    need_tile = B.sas_workspace_bytes(B.SAS_OP_BWD, d, S)
+    qcap = S * k + 64 * n_tiles
+    extra = (al(32 * S * k * 4) + al(grp * n_tiles * 32 * 4) + al(grp * n_tiles * 32 * 4)
+             + al(grp * (1 + n_tiles * (n_tiles - 1) // 2) * 64 * 4) + al(grp * n_tiles * 4)
+             + al(grp * (n_tiles + 1) * 4) + al(grp * qcap * 4) + grp * qcap * 4)
+    need = B.sas_workspace_bytes(B.SAS_OP_BWD_QUERIES, d, S)
+    assert need == al(need_tile) + extra
+    bw = lambda dims, seq_len, ws_bytes, dlg=FAKE: lib.sas_bwd_queries(
+        ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, seq_len, FAKE, FAKE, 0.1, FAKE,
+        FAKE, FAKE, dlg, FAKE, ws_bytes, None)
+    assert bw(d, S, need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+    assert bw(d, 0, need) == B.SAS_ERR_INVALID_ARGUMENT
+    assert bw(d, S, need, dlg=None) == B.SAS_ERR_INVALID_ARGUMENT
+    assert bw(_dims(dtype=B.SAS_F32), 128, 1 << 40) == B.SAS_ERR_UNSUPPORTED
+
+    # selector backward of per-query rows: mean keys, per-row (h, qbar), the
+    # H partials of 512-row chunks and H
+    need = B.sas_workspace_bytes(B.SAS_OP_SELECTOR_BWD_QUERIES, d, S)
+    c_max = 65536 // 64
+    chunks = (grp * S + 511) // 512
+    assert need == (al(grp * c_max * 128 * 4) + al(grp * S * 2 * 128 * 4)
+                    + al(chunks * 128 * 128 * 4) + 128 * 128 * 4)
+    sb = lambda dims, q_len, ws_bytes, wk=FAKE: lib.sas_selector_bwd_queries(
+        ctypes.byref(dims), FAKE, q_len, FAKE, FAKE, wk, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+        FAKE, FAKE, ws_bytes, None)
+    assert sb(d, S, need - 1) == B.SAS_ERR_WORKSPACE_TOO_SMALL
+    assert sb(d, S, need, wk=None) == B.SAS_ERR_INVALID_ARGUMENT       # Wk_sel is required
+    assert sb(d, 65537, 1 << 40) == B.SAS_ERR_INVALID_ARGUMENT
+    assert sb(big, 64 * 1025, 1 << 40) == B.SAS_ERR_UNSUPPORTED
