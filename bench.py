@@ -68,7 +68,7 @@ def _args():
 
 
 DECODE_KERNELS = ("sas::decode_split_kernel", "sas::decode_merge_kernel")
-PREFILL_KERNELS = ("sas::prefill_fwd_kernel<128, 4, false>",)   # the tile forward
+PREFILL_KERNELS = ("sas::prefill_fwd_persistent_kernel<128, 4>",)   # the tile forward
 # the sources those kernels are built from
 DECODE_SOURCES = ("decode.hip", "sas_device.h", "sas_internal.h", "sas_select_dev.h")
 PREFILL_SOURCES = ("prefill.hip", "sas_device.h", "sas_internal.h", "sas_mfma.h")
@@ -598,7 +598,7 @@ def run_prefill(args, wl):
         },
         "flops": {"visible_selected_pairs": pairs, "fwd": fwd_flop, "bwd": bwd_flop},
         "bwd_TFLOPs": round(bwd_tf, 1),
-        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_kernel (sas_prefill_fwd)",
+        "roofline": {"bound": "mfma", "kernel": "prefill_fwd_persistent_kernel (sas_prefill_fwd)",
                      "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name, PREFILL_KERNELS, PREFILL_SOURCES)},

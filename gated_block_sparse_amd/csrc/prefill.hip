@@ -20,6 +20,7 @@
 //  * the log-gate is added per block; the diagonal block is masked j > i;
 //  * the block loop is software-pipelined (see the kernel) so each wave always
 //    has matrix and vector work that do not depend on each other.
+#include <algorithm>
 #include <climits>
 
 #include "sas_device.h"
@@ -361,6 +362,238 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 }
 
+// Tile selection, persistent form: one workgroup per CU walks the work items
+// w = blockIdx.x, blockIdx.x + gridDim.x, ... (item = tile, group, head chunk,
+// sequence; heaviest tiles first), with the per-item arithmetic of
+// prefill_fwd_kernel, so that kernel's per-query form fed one selection per
+// tile gives the same bits.  The staged blocks
+// of consecutive items continue one ring sequence (block i of an item sits in
+// buffer (base + i) % 4), so while an item finishes its diagonal block the
+// next item's block list is in LDS (its idx row loaded early into wave 0's
+// registers), its Q rows are on their way into registers (no longer needed
+// by the item finishing) and its first K/V copies are in flight into buffers
+// the finishing item no longer reads.  The first P V of an item runs on the
+// previous item's diagonal V tile with P = 0 (finite data), so only the very
+// first item needs a zeroed buffer.  4% faster than one workgroup per item at
+// S = 16384 (335 against 350 us).
+template <int D, int HPW>
+__global__ void __launch_bounds__(128 * HPW)
+prefill_fwd_persistent_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                              const uint16_t* __restrict__ V, int S, int Hkv, int G, int t_max,
+                              int n_tiles, int k, int batch, const int32_t* __restrict__ idx,
+                              const float* __restrict__ log_gate, float scale2,
+                              uint16_t* __restrict__ O, float* __restrict__ lse) {
+  constexpr int NT = 128 * HPW;
+  constexpr int KS = D / 16;
+  constexpr int CT = D / 32;
+  constexpr int NBUF = 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][64 * kRowStride<D>];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][64 * kTrStride<D>];
+  __shared__ int s_blk[kMaxTopK + 1];
+  __shared__ float s_beta[kMaxTopK + 1];
+  __shared__ int s_nblk;
+
+  const int nhc = G / HPW;
+  const int per_t = Hkv * batch * nhc;   // items per tile
+  const int n_items = n_tiles * per_t;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int Hq = Hkv * G;
+  int w = blockIdx.x;
+  if (w >= n_items) return;   // workgroup-uniform
+  auto coords = [&](int ww, int& t, int& r, int& b, int& hc) {
+    t = n_tiles - 1 - ww / per_t;
+    int rem = ww % per_t;
+    hc = rem % nhc;
+    rem /= nhc;
+    r = rem % Hkv;
+    b = rem / Hkv;
+  };
+  // wave 0: an item's idx / log_gate row, loaded ahead into registers, then
+  // written to the LDS block list (valid slots in order, then the diagonal)
+  int pf_idx = -1;
+  float pf_lg = 0.f;
+  auto prefetch_list = [&](int ww) {
+    int t, r, b, hc;
+    coords(ww, t, r, b, hc);
+    const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
+    pf_idx = lane < k ? idx[srow * k + lane] : -1;
+    pf_lg = (lane < k && log_gate) ? log_gate[srow * k + lane] : 0.f;
+  };
+  auto commit_list = [&](int t) {
+    const bool ok = lane < k && pf_idx >= 0;
+    const unsigned long long mask = __ballot(ok);
+    if (ok) {
+      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+      s_blk[pos] = pf_idx;
+      s_beta[pos] = log_gate ? pf_lg * kLog2eF : 0.f;
+    }
+    if (lane == 0) {
+      const int nv = __popcll(mask);
+      s_blk[nv] = t;
+      s_beta[nv] = 0.f;
+      s_nblk = nv + 1;
+    }
+  };
+  auto kv_rows = [&](const uint16_t* X, int b, int r) {
+    return X + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
+  };
+  bf16x8_t qb[KS];  // B operand of S^T = K Q^T: Q[qi][16ks + 8hi .. +8]
+  auto load_q = [&](int t, int r, int b, int hc) {
+    const int h = r * G + hc * HPW + (wave >> 1);
+    const int qi = t * 64 + (wave & 1) * 32 + l32;
+    const bool qvalid = qi < S;
+    const uint16_t* qrow =
+        Q + ((static_cast<size_t>(b) * Hq + h) * S + (qvalid ? qi : 0)) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks)
+                                : make_uint4(0, 0, 0, 0));
+  };
+  using Stage = DmaStage<D, NT / 64>;
+  Stage stg;
+  stg.init(wave, lane);
+  const uint32_t ks_lds = lds_addr_of(&Ks[0][0]), vs_lds = lds_addr_of(&Vs[0][0]);
+  // block i of the current list (clamped to the diagonal nh) into ring slot `slot`
+  auto copy_k = [&](const uint16_t* Kg, int nh, int i, int slot) {
+    const int tok = s_blk[min(i, nh)] * 64;
+    stg.k(Kg + static_cast<size_t>(tok) * D, S - tok, ks_lds + (slot & 3) * Stage::KTILE, wave);
+  };
+  auto copy_v = [&](const uint16_t* Vg, int nh, int i, int slot) {
+    const int tok = s_blk[min(i, nh)] * 64;
+    stg.v(Vg + static_cast<size_t>(tok) * D, S - tok, vs_lds + (slot & 3) * Stage::VTILE, wave);
+  };
+  // the first copies of an item (ring slots base ..): in this order the wait
+  // that starts the item leaves at most K of block 2 and V of block 1 in flight
+  auto first_copies = [&](const uint16_t* Kg, const uint16_t* Vg, int nh, int base) {
+    copy_k(Kg, nh, 0, base);
+    copy_v(Vg, nh, 0, base);
+    copy_k(Kg, nh, 1, base + 1);
+    copy_k(Kg, nh, 2, base + 2);
+    copy_v(Vg, nh, 1, base + 1);
+  };
+
+  int t, r, b, hc;
+  coords(w, t, r, b, hc);
+  if (wave == 0) {
+    prefetch_list(w);
+    commit_list(t);
+  }
+  for (int c = tid; c < 64 * kTrStride<D> / 8; c += NT)
+    *reinterpret_cast<uint4*>(&Vs[3][8 * c]) = make_uint4(0, 0, 0, 0);
+  __syncthreads();
+  load_q(t, r, b, hc);
+  int base = 0;
+  first_copies(kv_rows(K, b, r), kv_rows(V, b, r), s_nblk - 1, base);
+  dma_sync<Stage::KPW + Stage::VPW>();
+
+  for (;;) {
+    const int h = r * G + hc * HPW + (wave >> 1);
+    const int qloc = (wave & 1) * 32 + l32;
+    const int qi = t * 64 + qloc;
+    const bool qvalid = qi < S;
+    const uint16_t* Kg = kv_rows(K, b, r);
+    const uint16_t* Vg = kv_rows(V, b, r);
+    const int nh = s_nblk - 1;
+    const int wn = w + static_cast<int>(gridDim.x);
+    const bool has_next = wn < n_items;
+
+    f32x16_t acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) zero16(acc[ct]);
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16_t s_cur[2];
+    block_scores<D>(Ks[base & 3], qb, s_cur, l32, hi);
+    bf16x8_t p_prev[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p_prev[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    if (wave == 0 && has_next) prefetch_list(wn);
+
+    // the online softmax, as in prefill_fwd_kernel
+    auto update_max = [&](float beta2) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[tt][v]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_cand = fmaxf(m_run, mx * scale2 + beta2);
+      if (__any(!(m_cand - m_run <= 8.f))) {
+        const float alpha = exp2f(m_run - m_cand);
+        l_run *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
+        m_run = m_cand;
+      }
+    };
+    auto probabilities = [&](float beta2) {
+      const float off = beta2 - m_run;
+      float ls = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(fmaf(s_cur[tt][v], scale2, off));
+          s_cur[tt][v] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 32, 64);
+      l_run += ls;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p_prev[j] = acc_to_bop(s_cur, j);
+    };
+
+    for (int it = 0; it < nh; ++it) {
+      const float beta2 = s_beta[it];
+      copy_k(Kg, nh, it + 3, base + it + 3);
+      copy_v(Vg, nh, it + 2, base + it + 2);
+      block_pv<D>(Vs[(base + it + 3) & 3], p_prev, acc, hi);
+      update_max(beta2);
+      f32x16_t s_next[2];
+      block_scores<D>(Ks[(base + it + 1) & 3], qb, s_next, l32, hi);
+      probabilities(beta2);
+      dma_sync<2 * Stage::VPW + Stage::KPW>();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) s_cur[tt] = s_next[tt];
+    }
+    dma_sync<0>();   // the copies past the list have landed; nobody reads the list again
+    // the next item: its list, Q rows and first copies, while this one finishes
+    int tn = 0, rn = 0, bn = 0, hcn = 0;
+    const int nbase = base + nh + 1;
+    if (has_next) {   // workgroup-uniform
+      coords(wn, tn, rn, bn, hcn);
+      if (wave == 0) commit_list(tn);
+      __syncthreads();
+      first_copies(kv_rows(K, bn, rn), kv_rows(V, bn, rn), s_nblk - 1, nbase);
+      load_q(tn, rn, bn, hcn);
+    }
+    // the diagonal block: causal mask j > i
+    block_pv<D>(Vs[(base + nh + 3) & 3], p_prev, acc, hi);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (32 * tt + acc_row(v, hi) > qloc) s_cur[tt][v] = -INFINITY;
+    update_max(0.f);
+    probabilities(0.f);
+    block_pv<D>(Vs[(base + nh) & 3], p_prev, acc, hi);
+    if (qvalid) {
+      store_acc_col<CT>(acc, 1.f / l_run, O + ((static_cast<size_t>(b) * Hq + h) * S + qi) * D, hi);
+      if (hi == 0) lse[(static_cast<size_t>(b) * Hq + h) * S + qi] = (m_run + log2f(l_run)) * kLn2F;
+    }
+    if (!has_next) break;
+    w = wn;
+    t = tn;
+    r = rn;
+    b = bn;
+    hc = hcn;
+    base = nbase;
+    dma_sync<Stage::KPW + Stage::VPW>();   // the item's K0, V0, K1 have landed
+  }
+}
+
 size_t prefill_ws_bytes(const sas_dims&, int) { return 0; }
 
 template <int D, bool PQ>
@@ -370,12 +603,30 @@ static sas_status launch_pf(const sas_dims& d, const void* Q, const void* K, con
   const int G = d.n_q_heads / d.n_kv_heads;
   const int n_tiles = cdiv(S, kBlock);
   const float scale2 = scale * kLog2eF;
+  // tile selection: persistent, one workgroup per CU (LDS holds one)
+  int n_cu = 0;
+  if (!PQ) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu < 1)
+      return fail(SAS_ERR_HIP, "prefill_fwd: cannot read the device's CU count");
+  }
 #define SAS_PF_CASE(HPW)                                                                   \
-  hipLaunchKernelGGL((prefill_fwd_kernel<D, HPW, PQ>), dim3(n_tiles * (G / HPW),           \
-                     d.n_kv_heads, d.batch), dim3(128 * HPW), 0, st,                        \
-                     static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),      \
-                     static_cast<const uint16_t*>(V), S, d.n_kv_heads, G, d.t_max, n_tiles, \
-                     d.top_k, idx, log_gate, scale2, static_cast<uint16_t*>(O), lse)
+  if (PQ)                                                                                  \
+    hipLaunchKernelGGL((prefill_fwd_kernel<D, HPW, true>), dim3(n_tiles * (G / HPW),       \
+                       d.n_kv_heads, d.batch), dim3(128 * HPW), 0, st,                      \
+                       static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),    \
+                       static_cast<const uint16_t*>(V), S, d.n_kv_heads, G, d.t_max,        \
+                       n_tiles, d.top_k, idx, log_gate, scale2, static_cast<uint16_t*>(O),  \
+                       lse);                                                                \
+  else                                                                                     \
+    hipLaunchKernelGGL((prefill_fwd_persistent_kernel<D, HPW>),                            \
+                       dim3(std::min(n_cu, n_tiles * (G / HPW) * d.n_kv_heads * d.batch)), \
+                       dim3(128 * HPW), 0, st, static_cast<const uint16_t*>(Q),            \
+                       static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V), S, \
+                       d.n_kv_heads, G, d.t_max, n_tiles, d.top_k, d.batch, idx, log_gate,  \
+                       scale2, static_cast<uint16_t*>(O), lse)
   switch (G) {
     case 1: SAS_PF_CASE(1); break;
     case 2: SAS_PF_CASE(2); break;
