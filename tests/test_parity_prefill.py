@@ -281,6 +281,42 @@ def test_prefill_batch2_fwd_bwd():
         assert e <= TOL_GRAD_REL, (b, e)
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,d,k,B", [
+    (1000, 32, 4, 64, 5, 3), (1000, 16, 4, 128, 6, 5), (1000, 8, 4, 128, 4, 5),
+    (1000, 4, 4, 64, 3, 5),
+])
+def test_prefill_fwd_more_items_than_cus(S, Hq, Hkv, d, k, B):
+    """More (tile, group, head chunk, sequence) items than the GPU has CUs, so
+    the tile forward's workgroups each take several items in turn, ragged last
+    tile and tile 0 (diagonal only) among them; every tile of every sequence
+    against the oracle with the oracle's own selection."""
+    S_ = _sas()
+    G = Hq // Hkv
+    n_items = -(-S // 64) * Hkv * B * max(1, G // 4)
+    assert n_items > torch.cuda.get_device_properties(0).multi_processor_count
+    wl = synth.custom_workload("prefill", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                               sel_dim=128, top_k=k, dtype="bf16", seq_len=S)
+    p = synth.make_problem(wl, 17 + B)
+    scale = 1.0 / math.sqrt(d)
+    log(f"[prefill items] S={S} Hq={Hq} Hkv={Hkv} d={d} k={k} B={B} items={n_items}")
+    sels, refs = [], []
+    for b in range(B):
+        Qf, Kf, Vf = (synth.to_f64(x[b], "bf16") for x in (p.q, p.K, p.V))
+        sel = O.prefill_select(Qf, Kf, S, p.f64("Wq_sel"), p.f64("Wk_sel"), k, G)
+        sels.append(sel)
+        refs.append(O.prefill_attend(Qf, Kf, Vf, S, sel["idx"], sel["log_gate"], scale, G))
+    idx = idx_dev(np.stack([s["idx"] for s in sels]))
+    lg = lg_dev(np.stack([s["log_gate"] for s in sels]))
+    O_g, lse_g = S_.sas_prefill_fwd(dev(p.q), dev(p.K), dev(p.V), idx, lg)
+    O_h, lse_h = host(O_g), host(lse_g)
+    for b in range(B):
+        Or, lser = refs[b]
+        err_o = np.abs(O_h[b] - Or).max()
+        err_l = np.abs(lse_h[b] - lser).max()
+        assert err_o <= TOL_OUT["bf16"], (b, err_o)
+        assert err_l <= TOL_LSE, (b, err_l)
+
+
 def test_prefill_k64_fwd_bwd():
     """The largest k built (64): tiles past the 64th select 64 history blocks."""
     p = _problem(64 * 70 + 17, 4, 1, 128, 128, 64, seed=64)
