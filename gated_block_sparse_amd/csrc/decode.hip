@@ -12,11 +12,16 @@
 // query heads of the group (each K/V byte serves G heads), and leaves an
 // unnormalised partial softmax state (max, sum, acc) in the workspace.  Two
 // blocks per unit are used once the grid has enough units to fill the chip:
-// twice the bytes in flight per thread and half the partials to merge.  A second, small kernel merges the k+1 partials of each head
-// in slot order:  o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u,  issuing
-// all of its loads at once; the kernel boundary orders the two, so no
-// device-wide fences or atomics are needed and results are bitwise
-// reproducible.
+// twice the bytes in flight per thread and half the partials to merge.  The
+// k+1 partials of each head are merged in slot order:
+//   o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u.
+// sas_decode_fwd does it in a second, small kernel that issues all of its
+// loads at once (the kernel boundary orders the two).  The fused decode step
+// does it in the split kernel: each unit publishes its partial (stores at
+// device scope, then one atomic count per row) and the unit that arrives
+// last merges the row, which saves the merge launch.  Both merges run the same
+// arithmetic in slot order, so every path gives the same bits, whichever
+// unit arrives last.
 #include "sas_device.h"
 #include "sas_internal.h"
 #include "sas_select_dev.h"
@@ -39,6 +44,24 @@ template <int G, int D> struct SplitLds {
   float acc[4][G][D];
 };
 
+// Partial states are stored and, by the fused merge, loaded at device scope
+// (relaxed atomics: written through to, and read from, the level where all
+// XCDs see the same data), so publishing a partial needs only the wait for
+// its stores, no write-back or invalidation of a whole L2.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent2(const float* p) {   // 8-byte aligned
+  const unsigned long long v = __hip_atomic_load(
+      reinterpret_cast<unsigned long long*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)),
+                     __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+
 // Attention over the (up to NB) blocks of one unit, all G heads of group
 // `row`: writes the unit's partial state to `out`.  Every thread of the
 // workgroup calls it.
@@ -58,7 +81,8 @@ __device__ __forceinline__ void split_unit(const T* __restrict__ q, const T* __r
 #pragma unroll
   for (int bb = 0; bb < NB; ++bb) tot += ntok[bb];
   if (tot == 0) {  // only empty slots: a neutral partial
-    for (int x = tid; x < PF; x += kDecThreads) out[x] = (x >= G * D && x < G * D + G) ? -INFINITY : 0.f;
+    for (int x = tid; x < PF; x += kDecThreads)
+      store_coherent(out + x, (x >= G * D && x < G * D + G) ? -INFINITY : 0.f);
     return;
   }
   const int col = lane % LPR, rsub = lane / LPR;
@@ -193,12 +217,99 @@ __device__ __forceinline__ void split_unit(const T* __restrict__ q, const T* __r
   __syncthreads();
   for (int x = tid; x < G * D; x += kDecThreads) {
     const int h = x / D, c = x % D;
-    out[x] = sh.acc[0][h][c] + sh.acc[1][h][c] + sh.acc[2][h][c] + sh.acc[3][h][c];
+    store_coherent(out + x, sh.acc[0][h][c] + sh.acc[1][h][c] + sh.acc[2][h][c] + sh.acc[3][h][c]);
   }
   if (tid < G) {
-    out[G * D + tid] = mh[tid];
-    out[G * D + G + tid] = sh.l[0][tid] + sh.l[1][tid] + sh.l[2][tid] + sh.l[3][tid];
+    store_coherent(out + G * D + tid, mh[tid]);
+    store_coherent(out + G * D + G + tid, sh.l[0][tid] + sh.l[1][tid] + sh.l[2][tid] + sh.l[3][tid]);
   }
+}
+
+// The merge's arithmetic for one output pair (x, x+1) of head g, in slot
+// order, shared by the merge kernel and the fused merge:
+//   M = max_u m_u,  w_u = 2^(m_u - M),  o = sum_u w_u acc_u / sum_u w_u l_u,
+// with w_u = 0 for an empty slot (m_u = -inf).
+__device__ __forceinline__ void merge_fold(float mu, float lu, float2 a, float M, float& L,
+                                           float& A0, float& A1) {
+  const float w = fast_exp2(mu - M);
+  L = fmaf(w, lu, L);
+  A0 = fmaf(w, a.x, A0);
+  A1 = fmaf(w, a.y, A1);
+}
+template <typename T>
+__device__ __forceinline__ void merge_store(float M, float L, float A0, float A1, T* op,
+                                            float* lse_g) {
+  const float inv = 1.f / L;
+  store_scalar<T>(op, A0 * inv);
+  store_scalar<T>(op + 1, A1 * inv);
+  if (lse_g) *lse_g = fmaf(M, kLn2, logf(L));
+}
+
+constexpr int kMergeMaxSlots = kMaxTopK + 1;
+constexpr int kFusedMergeSlots = 17;  // accumulator slots per round trip in the fused merge
+
+// Fused merge: called by every thread of the unit that arrived last, once
+// the other units' partials are visible.  The (max, sum) pairs of all slots
+// go to LDS (ml), the accumulators come kFusedMergeSlots slots per round trip
+// (the first batch together with the pairs), which bounds the registers the
+// split kernel needs for it.
+template <typename T, int D, int G>
+__device__ __forceinline__ void fused_merge(int ns, const float* __restrict__ base,
+                                            T* __restrict__ o_row, float* __restrict__ lse_row,
+                                            float (*ml)[2 * G]) {
+  constexpr int PF = DecPartial<G, D>::kFloats;
+  constexpr int SB = kFusedMergeSlots;
+  const int tid = threadIdx.x;
+  float2 av[SB];
+  auto load_batch = [&](int x, int u0) {
+#pragma unroll
+    for (int j = 0; j < SB; ++j)
+      if (u0 + j < ns) av[j] = load_coherent2(base + static_cast<size_t>(u0 + j) * PF + x);
+  };
+  if (2 * tid < G * D) load_batch(2 * tid, 0);
+  for (int i = tid; i < ns * 2 * G; i += kDecThreads) {
+    const int u = i / (2 * G), j = i % (2 * G);
+    ml[u][j] = load_coherent(base + static_cast<size_t>(u) * PF + G * D + j);
+  }
+  __syncthreads();
+  for (int x = 2 * tid; x < G * D; x += 2 * kDecThreads) {
+    if (x != 2 * tid) load_batch(x, 0);
+    const int g = x / D;
+    float M = -INFINITY;
+    for (int u = 0; u < ns; ++u) M = fmaxf(M, ml[u][g]);
+    float L = 0.f, A0 = 0.f, A1 = 0.f;
+    for (int u0 = 0; u0 < ns; u0 += SB) {
+      if (u0 > 0) load_batch(x, u0);
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (u0 + j < ns) merge_fold(ml[u0 + j][g], ml[u0 + j][G + g], av[j], M, L, A0, A1);
+    }
+    merge_store<T>(M, L, A0, A1, o_row + x, (lse_row && (x % D) == 0) ? lse_row + g : nullptr);
+  }
+}
+
+// The end of a split unit with a fused merge (cnt non-null; the row's count
+// starts at zero): publish this unit's partial (its device-scope stores have
+// completed once every wave has waited for them), count it with one atomic
+// add, and merge the row in the unit that arrives last, reading the
+// partials at device scope.  No unit waits for another.
+template <typename T, int D, int G>
+__device__ __forceinline__ void publish_and_merge(int* __restrict__ cnt, size_t row, int n_units,
+                                                  const float* __restrict__ part,
+                                                  T* __restrict__ o, float* __restrict__ lse,
+                                                  SplitLds<G, D>& sh, int& s_last) {
+  constexpr int PF = DecPartial<G, D>::kFloats;
+  static_assert(sizeof(sh.acc) >= sizeof(float) * kMergeMaxSlots * 2 * G, "merge pairs fit");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial stores are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(cnt + row, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             n_units - 1;
+  __syncthreads();
+  if (!s_last) return;   // workgroup-uniform
+  fused_merge<T, D, G>(n_units, part + row * n_units * static_cast<size_t>(PF),
+                       o + (row * G) * static_cast<size_t>(D), lse ? lse + row * G : nullptr,
+                       reinterpret_cast<float (*)[2 * G]>(&sh.acc[0][0][0]));
 }
 
 // Split kernel of sas_decode_fwd: the unit's blocks come from idx/log_gate.
@@ -207,9 +318,11 @@ __global__ void __launch_bounds__(kDecThreads)
 decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ V,
                     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ idx,
                     const float* __restrict__ log_gate, int gated, float scale2, int Hkv,
-                    int t_max, int k, KvPages pg, float* __restrict__ part) {
+                    int t_max, int k, KvPages pg, float* __restrict__ part,
+                    int* __restrict__ cnt, T* __restrict__ o, float* __restrict__ lse) {
   constexpr int PF = DecPartial<G, D>::kFloats;
   __shared__ SplitLds<G, D> sh;
+  __shared__ int s_last;
   const int unit = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const int n_units = (k + NB) / NB;   // ceil((k + 1) / NB)
@@ -241,6 +354,7 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ K, const T* _
   }
   split_unit<T, D, G, NB>(q, K, V, row, brow, ntok, beta2, scale2,
                           part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
+  if (cnt) publish_and_merge<T, D, G>(cnt, row, n_units, part, o, lse, sh, s_last);
 }
 
 // Split kernel of sas_decode_step: the selection of the row is finished here
@@ -256,10 +370,12 @@ decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
                            int nchunk, int nlist, int kc, int gated, float scale2, int Hkv,
                            int t_max, int k, KvPages pg, int32_t* __restrict__ idx,
                            float* __restrict__ log_gate, float* __restrict__ score_lse,
-                           float* __restrict__ part) {
+                           float* __restrict__ part, int* __restrict__ cnt, T* __restrict__ o,
+                           float* __restrict__ lse) {
   constexpr int PF = DecPartial<G, D>::kFloats;
   extern __shared__ uint64_t keys[];   // two buffers of nlist * kc keys
   __shared__ SplitLds<G, D> sh;
+  __shared__ int s_last;
   __shared__ float red[kDecThreads / 64];
   __shared__ int32_t sel_blk[kMaxTopK];
   __shared__ float sel_lg[kMaxTopK];
@@ -305,6 +421,7 @@ decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
   }
   split_unit<T, D, G, NB>(q, K, V, row, brow, ntok, beta2, scale2,
                           part + (row * n_units + unit) * static_cast<size_t>(PF), sh);
+  publish_and_merge<T, D, G>(cnt, row, n_units, part, o, lse, sh, s_last);
 }
 
 // One workgroup per (sequence, group), one thread per pair of outputs (a
@@ -313,8 +430,6 @@ decode_select_split_kernel(const T* __restrict__ q, const T* __restrict__ K,
 // accumulator pairs of all slots to registers, so the merge costs a single
 // round trip to memory.  Then, in slot order,
 //   M = max_u m_u,  w_u = 2^(m_u - M),  o = sum_u w_u acc_u / sum_u w_u l_u.
-constexpr int kMergeMaxSlots = kMaxTopK + 1;
-
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(G * D / 2 < 64 ? 64 : G * D / 2)
 decode_merge_kernel(int Hkv, int ns, const float* __restrict__ part, T* __restrict__ o,
@@ -343,19 +458,10 @@ decode_merge_kernel(int Hkv, int ns, const float* __restrict__ part, T* __restri
   for (int u = 0; u < ns; ++u) M = fmaxf(M, ml[u][g]);
   float L = 0.f, A0 = 0.f, A1 = 0.f;
 #pragma unroll
-  for (int u = 0; u < kMergeMaxSlots; ++u) {
-    if (u < ns) {
-      const float w = fast_exp2(ml[u][g] - M);  // 0 for an empty slot (m = -inf)
-      L = fmaf(w, ml[u][G + g], L);
-      A0 = fmaf(w, av[u].x, A0);
-      A1 = fmaf(w, av[u].y, A1);
-    }
-  }
-  const float inv = 1.f / L;
-  T* op = o + (row * G) * static_cast<size_t>(D) + x;
-  store_scalar<T>(op, A0 * inv);
-  store_scalar<T>(op + 1, A1 * inv);
-  if (lse && (x % D) == 0) lse[row * G + g] = M * kLn2 + logf(L);
+  for (int u = 0; u < kMergeMaxSlots; ++u)
+    if (u < ns) merge_fold(ml[u][g], ml[u][G + g], av[u], M, L, A0, A1);
+  merge_store<T>(M, L, A0, A1, o + (row * G) * static_cast<size_t>(D) + x,
+                 (lse && (x % D) == 0) ? lse + row * G + g : nullptr);
 }
 
 // workspace: partials[B*Hkv*(k+1)*G*(d+2)] fp32
@@ -376,7 +482,8 @@ template <typename T, int D, int G, int NB>
 static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K, const void* V,
                                 const int32_t* seq_lens, const int32_t* idx,
                                 const float* log_gate, float scale, void* o, float* lse,
-                                void* ws, hipStream_t st, KvPages pg = KvPages{nullptr, 0}) {
+                                void* ws, hipStream_t st, KvPages pg = KvPages{nullptr, 0},
+                                int* cnt = nullptr) {
   float* part = static_cast<float*>(ws);
   const int n_units = (d.top_k + NB) / NB;
   // k = 0 or the ungated rule may pass NULL idx / log_gate: the kernel then
@@ -387,9 +494,9 @@ static sas_status launch_dec_nb(const sas_dims& d, const void* q, const void* K,
                      dim3(kDecThreads), 0, st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, idx_r, lg_r,
                      log_gate != nullptr ? 1 : 0, scale * kLog2e, d.n_kv_heads, d.t_max,
-                     d.top_k, pg, part);
+                     d.top_k, pg, part, cnt, static_cast<T*>(o), lse);
   sas_status s = check_launch("decode_split");
-  if (s != SAS_OK) return s;
+  if (s != SAS_OK || cnt) return s;   // with counts, the last unit of each row merged it
   constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
   hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(d.n_kv_heads, d.batch),
                      dim3(kMergeThreads), 0, st, d.n_kv_heads, n_units, part, static_cast<T*>(o),
@@ -407,24 +514,26 @@ static sas_status launch_dec(const sas_dims& d, const void* q, const void* K, co
 }
 
 // Fused decode step: the selection's chunk stage, then (rows of more than
-// one chunk) the select-merge + split kernel, then the merge.  Workspace:
-// the selection's, then the partials.  Large grids (two blocks per unit)
-// take the unfused sequence instead.
+// one chunk) the select-merge + split kernel, whose last unit per row merges
+// the row.  Large grids (two blocks per unit) run the selection's own merge
+// kernel and then the plain split kernel (also merging in its last unit).
 template <typename T, int D, int G, int NB>
 static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K, const void* V,
                                  const int32_t* seq_lens, const float* Wq, const float* summ,
                                  const float* Wk, KvPages pg, int gated, float scale,
                                  int32_t* idx, float* log_gate, float* score_lse, void* o,
                                  float* lse, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws) + ((select_decode_ws_bytes(d) + 255) & ~size_t(255));
+  float* part = reinterpret_cast<float*>(w);
+  int* cnt = reinterpret_cast<int*>(w + ((decode_ws_bytes(d) + 255) & ~size_t(255)));
+  // the chunk stage also zeroes the arrival counts of the split kernel's merge
   sas_status s = launch_select_decode_chunks(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate,
-                                             score_lse, ws, st);
+                                             score_lse, ws, st, cnt);
   if (s != SAS_OK) return s;
   const SelectDecodeLayout L = select_decode_layout(d, ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                         ((select_decode_ws_bytes(d) + 255) & ~size_t(255)));
   if (L.nchunk == 1)  // the chunk stage already wrote the selection
     return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
-                                      scale, o, lse, part, st, pg);
+                                      scale, o, lse, part, st, pg, cnt);
   if constexpr (NB > 1) {
     // Grids this large keep the chip busy on their own; there the redundant
     // per-workgroup merge costs more than the launch it saves, so the
@@ -432,7 +541,7 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
     s = launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
     if (s != SAS_OK) return s;
     return launch_dec_nb<T, D, G, NB>(d, q, K, V, seq_lens, idx, gated ? log_gate : nullptr,
-                                      scale, o, lse, part, st, pg);
+                                      scale, o, lse, part, st, pg, cnt);
   } else {
   const int n_units = (d.top_k + NB) / NB;
   hipLaunchKernelGGL((decode_select_split_kernel<T, D, G, NB>),
@@ -440,14 +549,8 @@ static sas_status launch_step_nb(const sas_dims& d, const void* q, const void* K
                      2 * L.nlist * L.kc * sizeof(uint64_t), st, static_cast<const T*>(q),
                      static_cast<const T*>(K), static_cast<const T*>(V), seq_lens, L.part, L.cand,
                      L.nchunk, L.nlist, L.kc, gated, scale * kLog2e, d.n_kv_heads, d.t_max,
-                     d.top_k, pg, idx, log_gate, score_lse, part);
-  s = check_launch("decode_select_split");
-  if (s != SAS_OK) return s;
-  constexpr int kMergeThreads = G * D / 2 < 64 ? 64 : G * D / 2;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(d.n_kv_heads, d.batch),
-                     dim3(kMergeThreads), 0, st, d.n_kv_heads, n_units, part, static_cast<T*>(o),
-                     lse);
-  return check_launch("decode_merge");
+                     d.top_k, pg, idx, log_gate, score_lse, part, cnt, static_cast<T*>(o), lse);
+  return check_launch("decode_select_split");
   }
 }
 
@@ -478,8 +581,11 @@ static sas_status step_by_group(const sas_dims& d, const void* q, const void* K,
   return fail(SAS_ERR_UNSUPPORTED, "decode step: group size");
 }
 
+// workspace: the selection's | partials | one arrival count per row (int)
 size_t decode_step_ws_bytes(const sas_dims& d) {
-  return ((select_decode_ws_bytes(d) + 255) & ~size_t(255)) + decode_ws_bytes(d);
+  return ((select_decode_ws_bytes(d) + 255) & ~size_t(255)) +
+         ((decode_ws_bytes(d) + 255) & ~size_t(255)) +
+         static_cast<size_t>(d.batch) * d.n_kv_heads * sizeof(int);
 }
 
 sas_status launch_decode_step(const sas_dims& d, const void* q, const void* K, const void* V,

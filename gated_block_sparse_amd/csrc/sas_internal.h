@@ -90,12 +90,14 @@ SelectDecodeLayout select_decode_layout(const sas_dims& d, void* ws);
 // when a row fits one chunk it also writes the final idx/log_gate/score_lse.
 // With Wk non-null, the workgroup holding each row's newest complete block
 // C-1 first recomputes that block's summary from K (the summaries kernel's
-// arithmetic, same bits), stores it into summ and scores with it.
+// arithmetic, same bits), stores it into summ and scores with it.  With
+// dec_cnt non-null it also zeroes dec_cnt[row] for every (sequence, group)
+// row (the arrival counts of the fused decode step's merge).
 sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                        const float* Wq, const float* summ, const void* K,
                                        const float* Wk, KvPages pg, int32_t* idx,
                                        float* log_gate, float* score_lse, void* ws,
-                                       hipStream_t st);
+                                       hipStream_t st, int* dec_cnt = nullptr);
 // Its second stage: merges the per-chunk state into idx/log_gate/score_lse
 // (nothing to do when a row fits one chunk).
 sas_status launch_select_decode_merge(const sas_dims& d, const int32_t* seq_lens, int32_t* idx,

@@ -45,7 +45,8 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
                            int kc, int nchunk,
                            float* __restrict__ scores, float2* __restrict__ part,
                            uint64_t* __restrict__ cand, int32_t* __restrict__ idx,
-                           float* __restrict__ log_gate, float* __restrict__ score_lse) {
+                           float* __restrict__ log_gate, float* __restrict__ score_lse,
+                           int* __restrict__ dec_cnt) {
   constexpr int PL = DS / 32;                 // summary floats per lane
   constexpr int PD = D / 32;                  // query channels per lane
   constexpr int RW = DS / 8;                  // Wq_sel rows per half wave
@@ -69,6 +70,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   const size_t row = static_cast<size_t>(b) * Hkv + r;
   const size_t p = row * nchunk + chunk;
   const int n = max(0, min(kChunk, C - m0));
+  if (dec_cnt && chunk == 0 && tid == 0) dec_cnt[row] = 0;
   // fused refresh (Wk given): this workgroup holds the newest complete block
   const int mnew = C - 1;
   const bool refresh = Wk != nullptr && n > 0 && mnew >= m0 && mnew < m0 + n;
@@ -296,7 +298,8 @@ template <typename T, int D, int DS, int G>
 static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32_t* seq_lens,
                                    const float* Wq, const float* summ, const void* K,
                                    const float* Wk, KvPages pg, int32_t* idx, float* log_gate,
-                                   float* score_lse, float* scores, void* ws, hipStream_t st) {
+                                   float* score_lse, float* scores, void* ws, hipStream_t st,
+                                   int* dec_cnt) {
   const SelectDecodeLayout L = select_decode_layout(d, ws);
   if (L.nlist * L.kc > kMaxMergeKeys)
     return fail(SAS_ERR_UNSUPPORTED, "select: %d chunk candidates exceed the merge buffer",
@@ -306,7 +309,8 @@ static sas_status launch_sd_chunks(const sas_dims& d, const void* q, const int32
                      dim3(L.nchunk, d.n_kv_heads, d.batch), dim3(kSelThreads), 0, st,           \
                      static_cast<const T*>(q), seq_lens, Wq, summ, static_cast<const T*>(K),    \
                      Wk, const_cast<float*>(summ), pg, d.n_kv_heads, d.t_max, d.t_max / kBlock, \
-                     d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx, log_gate, score_lse)
+                     d.top_k, L.kc, L.nchunk, scores, L.part, L.cand, idx, log_gate, score_lse, \
+                     dec_cnt)
   switch (decode_chunk_rows(d)) {
     case 8: SAS_SD_CHUNK(8); break;
     case 16: SAS_SD_CHUNK(16); break;
@@ -333,7 +337,7 @@ static sas_status launch_sd(const sas_dims& d, const void* q, const int32_t* seq
                             float* score_lse, float* scores, void* ws, hipStream_t st) {
   sas_status s = launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, nullptr, nullptr,
                                                KvPages{nullptr, 0}, idx, log_gate, score_lse,
-                                               scores, ws, st);
+                                               scores, ws, st, nullptr);
   if (s != SAS_OK) return s;
   return launch_select_decode_merge(d, seq_lens, idx, log_gate, score_lse, ws, st);
 }
@@ -664,9 +668,9 @@ struct SelDecodeChunks {
   static sas_status run(const sas_dims& d, const void* q, const int32_t* seq_lens, const float* Wq,
                         const float* summ, const void* K, const float* Wk, KvPages pg,
                         int32_t* idx, float* log_gate, float* score_lse, float* scores, void* ws,
-                        hipStream_t st) {
+                        hipStream_t st, int* dec_cnt) {
     return launch_sd_chunks<T, D, DS, G>(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate,
-                                         score_lse, scores, ws, st);
+                                         score_lse, scores, ws, st, dec_cnt);
   }
 };
 
@@ -734,9 +738,9 @@ sas_status launch_select_decode_chunks(const sas_dims& d, const void* q, const i
                                        const float* Wq, const float* summ, const void* K,
                                        const float* Wk, KvPages pg, int32_t* idx,
                                        float* log_gate, float* score_lse, void* ws,
-                                       hipStream_t st) {
+                                       hipStream_t st, int* dec_cnt) {
   return by_type<SelDecodeChunks>(d, q, seq_lens, Wq, summ, K, Wk, pg, idx, log_gate, score_lse,
-                                  static_cast<float*>(nullptr), ws, st);
+                                  static_cast<float*>(nullptr), ws, st, dec_cnt);
 }
 
 sas_status launch_select_tiles(const sas_dims& d, const void* Q, int q_len, const float* Wq,

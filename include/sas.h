@@ -160,7 +160,11 @@ sas_status sas_decode_fwd(const sas_dims* dims, const void* q, const void* K, co
  * bit for bit, as sas_select(SAS_SELECT_DECODE, ...) followed by
  * sas_decode_fwd(..., gated ? log_gate : NULL, ...) on its selection, in
  * fewer launches: the merge of the selection's per-chunk candidates runs
- * inside the attention's split kernel instead of a kernel of its own.
+ * inside the attention's split kernel instead of a kernel of its own, and
+ * the split workgroup of each (sequence, group) that finishes last merges
+ * the attention partials (counted with one integer atomic per row in ws,
+ * which the step zeroes itself: ws needs no initial content, but two calls
+ * in flight on one ws race).
  * Wk_sel (nullable) fp32 [d_sel,d]: when given, the step first refreshes the
  * summary of each sequence's newest complete history block m = C-1 (C =
  * (seq_lens[b]-1)/64 >= 1), exactly as sas_block_summaries(..., C-1, C, ...)

@@ -91,9 +91,11 @@ def test_decode_rejects_nulls_scale_and_small_workspace(lib):
 def test_decode_step_validation(lib):
     d = _dims()
     need = B.sas_workspace_bytes(B.SAS_OP_DECODE_STEP, d)
-    # the selection's chunk state, 256-byte aligned, then the attention partials
+    # the selection's chunk state and the attention partials, each 256-byte
+    # aligned, then one int arrival count per (sequence, group) row
     sel = B.sas_workspace_bytes(B.SAS_OP_SELECT_DECODE, d)
-    assert need == (sel + 255) // 256 * 256 + B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d)
+    part = B.sas_workspace_bytes(B.SAS_OP_DECODE_FWD, d)
+    assert need == (sel + 255) // 256 * 256 + (part + 255) // 256 * 256 + 4 * d.batch * d.n_kv_heads
     step = lambda dims, ws_bytes, scale=0.1, q=FAKE, lg=FAKE, wk=None: lib.sas_decode_step(
         ctypes.byref(dims), q, FAKE, FAKE, FAKE, FAKE, wk, FAKE, 1, scale, FAKE, lg, FAKE, FAKE,
         FAKE, FAKE, ws_bytes, None)

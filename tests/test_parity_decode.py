@@ -250,6 +250,34 @@ def test_decode_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("B,T,k", [(1, 20000, 16), (8, 40000, 32)])
+def test_decode_step_reused_workspace(B, T, k):
+    """The fused step's merge counts arrivals per row in its workspace: one
+    workspace filled with junk bytes, then reused by several steps in a row
+    (the last one on a shorter batch), gives select + decode_fwd's bits each
+    time.  Covers the one-block and two-block split units."""
+    S = _sas()
+    wl = synth.custom_workload("decode", batch=B, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                               sel_dim=128, top_k=k, dtype="bf16", seq_len=T,
+                               seq_len_range=(T // 2, T) if B > 1 else None)
+    p = synth.make_problem(wl, 5 + B)
+    q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    lens = torch.from_numpy(p.seq_lens).cuda()
+    Wq, Wk = dev(p.Wq_sel), dev(p.Wk_sel)
+    summ = S.sas_block_summaries(K, lens, Wk)
+    dims = S.make_dims(B, 32, 8, 128, 128, k, K.shape[2], S.SAS_BF16)
+    ws = torch.randint(0, 256, (S.sas_workspace_bytes(S.SAS_OP_DECODE_STEP, dims),),
+                       dtype=torch.uint8, device="cuda")
+    for rep, nb in enumerate((B, B, max(1, B // 2))):
+        qq, KK, VV, ll, ss = q[:nb], K[:nb], V[:nb], lens[:nb], summ[:nb]
+        idx_g, lg_g, slse_g, _ = S.sas_select(S.SAS_SELECT_DECODE, qq, ll, Wq, ss, k)
+        o_r, lse_r = S.sas_decode_fwd(qq, KK, VV, ll, idx_g, lg_g)
+        idx_f, lg_f, slse_f, o_f, lse_f = S.sas_decode_step(qq, KK, VV, ll, Wq, ss, k, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_f, idx_g) and torch.equal(lg_f, lg_g), rep
+        assert torch.equal(o_f, o_r) and torch.equal(lse_f, lse_r), rep
+
+
 def test_block_summaries_range_leaves_other_rows():
     """Refreshing one block range writes exactly those rows."""
     S = _sas()
