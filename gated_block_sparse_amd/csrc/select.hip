@@ -75,7 +75,14 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   const int mnew = C - 1;
   const bool refresh = Wk != nullptr && n > 0 && mnew >= m0 && mnew < m0 + n;
 
-  // ---- all loads up front
+  // ---- all loads up front (the refresh's K block and Wk_sel slice first:
+  // they start the longest chain of this workgroup)
+  WkSlice<D, DS> wsl;
+  BlockMean<T, D> bm;
+  if (refresh) {
+    wsl.load(Wk, tid);
+    if (wave == 0) bm.load(K + kv_block_row(pg, b, r, mnew, Hkv, t_max) * D, lane);
+  }
   float qraw[G][PD];
   {
     const T* qb = q + (row * G) * static_cast<size_t>(D) + PD * l32;
@@ -120,13 +127,7 @@ select_decode_chunk_kernel(const T* __restrict__ q, const int32_t* __restrict__ 
   // the summaries kernel's own arithmetic, stored, and replaces the (stale)
   // slice of row mnew loaded above
   if (refresh) {
-    WkSlice<D, DS> wsl;
-    wsl.load(Wk, tid);
-    if (wave == 0) {
-      BlockMean<T, D> bm;
-      bm.load(K + kv_block_row(pg, b, r, mnew, Hkv, t_max) * D, lane);
-      bm.reduce(lane, rmean);
-    }
+    if (wave == 0) bm.reduce(lane, rmean);
     __syncthreads();
     const float a = wsl.project(rmean, tid);
     if (tid % WkSlice<D, DS>::SPLIT == 0) {
