@@ -117,18 +117,19 @@ __device__ __forceinline__ void block_pv(const uint16_t* Vc, const bf16x8_t* pb,
 // that ends iteration i-1, and has two iterations to land.  One wait + barrier
 // per iteration suffices.
 //
-// PQ (one selection per query, idx/log_gate [B,Hkv,S,k]): the workgroup walks
-// the union of its queries' selected blocks in ascending order (built from a
-// bitmap in LDS), and each lane, which owns one query column, takes the bias
+// One selection per query (idx/log_gate [B,Hkv,S,k]), one workgroup per
+// (tile, group, head chunk, sequence): the workgroup walks the union of its
+// queries' selected blocks in ascending order (built from a bitmap in LDS),
+// and each lane, which owns one query column, takes the bias
 // of its own query for the block: log g if its query selected the block, -inf
 // otherwise (the per-query mask of the pages' training kernel), found by a
 // cursor into its query's ascending idx row.  Blocks no query of the tile
 // selected are never visited.  The running max starts at a finite floor so
 // that a query whose first visited blocks are all masked keeps l = 0 and
 // O = 0 until its first selected block.
-template <int D, int HPW, bool PQ>
+template <int D, int HPW>
 __global__ void __launch_bounds__(128 * HPW)
-prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+prefill_fwd_queries_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, int S, int Hkv, int G, int t_max,
                    int n_tiles, int k, const int32_t* __restrict__ idx,
                    const float* __restrict__ log_gate, float scale2, uint16_t* __restrict__ O,
@@ -139,9 +140,8 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int NBUF = 4;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][64 * kRowStride<D>];  // row reads
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][64 * kTrStride<D>];   // transpose reads
-  __shared__ int s_blk[PQ ? kMaxTileRows + 1 : kMaxTopK + 1];
-  __shared__ float s_beta[PQ ? 1 : kMaxTopK + 1];
-  __shared__ uint32_t s_bits[PQ ? kMaxTileRows / 32 : 1];
+  __shared__ int s_blk[kMaxTileRows + 1];
+  __shared__ uint32_t s_bits[kMaxTileRows / 32];
   __shared__ int s_nblk;
 
   const int nhc = G / HPW;                       // head chunks per group
@@ -155,53 +155,36 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int qi = t * 64 + qloc;
   const bool qvalid = qi < S;
 
-  // block list: the valid selected blocks (in slot order), then the diagonal
-  const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
-  if constexpr (PQ) {
-    // union of the tile's per-query selections: bitmap, then a compaction by
-    // wave 0 (lane w owns blocks 32w .. 32w+31) into ascending order
-    for (int w = tid; w < kMaxTileRows / 32; w += NT) s_bits[w] = 0u;
-    __syncthreads();
-    const size_t qrow0 = (static_cast<size_t>(b) * Hkv + r) * S + static_cast<size_t>(t) * 64;
-    const int n_ent = min(64, S - t * 64) * k;
-    for (int e = tid; e < n_ent; e += NT) {
-      const int m = idx[qrow0 * k + e];
-      if (m >= 0) atomicOr(&s_bits[m >> 5], 1u << (m & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t w = lane < kMaxTileRows / 32 ? s_bits[lane] : 0u;
-      const int cnt = __popc(w);
-      int incl = cnt;
+  // block list: the union of the tile's per-query selections, ascending (a
+  // bitmap, then a compaction by wave 0, lane w owning blocks 32w .. 32w+31),
+  // then the diagonal
+  for (int w = tid; w < kMaxTileRows / 32; w += NT) s_bits[w] = 0u;
+  __syncthreads();
+  const size_t qrow0 = (static_cast<size_t>(b) * Hkv + r) * S + static_cast<size_t>(t) * 64;
+  const int n_ent = min(64, S - t * 64) * k;
+  for (int e = tid; e < n_ent; e += NT) {
+    const int m = idx[qrow0 * k + e];
+    if (m >= 0) atomicOr(&s_bits[m >> 5], 1u << (m & 31));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < kMaxTileRows / 32 ? s_bits[lane] : 0u;
+    const int cnt = __popc(w);
+    int incl = cnt;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      int pos = incl - cnt;
-      while (w) {
-        s_blk[pos++] = 32 * lane + (__ffs(w) - 1);
-        w &= w - 1u;
-      }
-      const int total = __shfl(incl, 63, 64);
-      if (lane == 0) {
-        s_blk[total] = t;
-        s_nblk = total + 1;
-      }
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
     }
-  } else if (wave == 0) {
-    const bool ok = lane < k && idx[srow * k + lane] >= 0;
-    const unsigned long long mask = __ballot(ok);
-    if (ok) {
-      const int pos = __popcll(mask & ((1ull << lane) - 1ull));
-      s_blk[pos] = idx[srow * k + lane];
-      s_beta[pos] = log_gate ? log_gate[srow * k + lane] * kLog2eF : 0.f;
+    int pos = incl - cnt;
+    while (w) {
+      s_blk[pos++] = 32 * lane + (__ffs(w) - 1);
+      w &= w - 1u;
     }
+    const int total = __shfl(incl, 63, 64);
     if (lane == 0) {
-      const int nv = __popcll(mask);
-      s_blk[nv] = t;
-      s_beta[nv] = 0.f;
-      s_nblk = nv + 1;
+      s_blk[total] = t;
+      s_nblk = total + 1;
     }
   }
 
@@ -216,11 +199,11 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   f32x16_t acc[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) zero16(acc[ct]);
-  float m_run = PQ ? -1e30f : -INFINITY, l_run = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
 
-  // PQ: cursor into the lane's query's ascending selection (next selected
-  // block and its log2-scaled gate; INT_MAX once the row is exhausted)
-  const size_t qsel = PQ ? ((static_cast<size_t>(b) * Hkv + r) * S + (qvalid ? qi : 0)) * k : 0;
+  // cursor into the lane's query's ascending selection (next selected block
+  // and its log2-scaled gate; INT_MAX once the row is exhausted)
+  const size_t qsel = ((static_cast<size_t>(b) * Hkv + r) * S + (qvalid ? qi : 0)) * k;
   int cur = 0, nxt = INT_MAX;
   float nxt_beta = 0.f;
   auto fetch = [&]() {
@@ -233,7 +216,7 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       }
     }
   };
-  if constexpr (PQ) fetch();
+  fetch();
 
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
@@ -316,16 +299,11 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   };
 
   for (int it = 0; it < nh; ++it) {
-    float beta2;
-    if constexpr (PQ) {
-      const bool hit = nxt == s_blk[it];
-      beta2 = hit ? nxt_beta : -INFINITY;
-      if (hit) {
-        ++cur;
-        fetch();
-      }
-    } else {
-      beta2 = s_beta[it];
+    const bool hit = nxt == s_blk[it];
+    const float beta2 = hit ? nxt_beta : -INFINITY;
+    if (hit) {
+      ++cur;
+      fetch();
     }
     copy_k(it + 3);
     copy_v(it + 2);
@@ -365,8 +343,8 @@ prefill_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // Tile selection, persistent form: one workgroup per CU walks the work items
 // w = blockIdx.x, blockIdx.x + gridDim.x, ... (item = tile, group, head chunk,
 // sequence; heaviest tiles first), with the per-item arithmetic of
-// prefill_fwd_kernel, so that kernel's per-query form fed one selection per
-// tile gives the same bits.  The staged blocks
+// prefill_fwd_queries_kernel, which therefore gives the same bits when every
+// query of a tile carries the tile's selection.  The staged blocks
 // of consecutive items continue one ring sequence (block i of an item sits in
 // buffer (base + i) % 4), so while an item finishes its diagonal block the
 // next item's block list is in LDS (its idx row loaded early into wave 0's
@@ -509,7 +487,7 @@ prefill_fwd_persistent_kernel(const uint16_t* __restrict__ Q, const uint16_t* __
     for (int j = 0; j < 4; ++j) p_prev[j] = as_bf16x8(make_uint4(0, 0, 0, 0));
     if (wave == 0 && has_next) prefetch_list(wn);
 
-    // the online softmax, as in prefill_fwd_kernel
+    // the online softmax, as in prefill_fwd_queries_kernel
     auto update_max = [&](float beta2) {
       float mx = -INFINITY;
 #pragma unroll
@@ -614,7 +592,7 @@ static sas_status launch_pf(const sas_dims& d, const void* Q, const void* K, con
   }
 #define SAS_PF_CASE(HPW)                                                                   \
   if (PQ)                                                                                  \
-    hipLaunchKernelGGL((prefill_fwd_kernel<D, HPW, true>), dim3(n_tiles * (G / HPW),       \
+    hipLaunchKernelGGL((prefill_fwd_queries_kernel<D, HPW>), dim3(n_tiles * (G / HPW),     \
                        d.n_kv_heads, d.batch), dim3(128 * HPW), 0, st,                      \
                        static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),    \
                        static_cast<const uint16_t*>(V), S, d.n_kv_heads, G, d.t_max,        \
