@@ -278,6 +278,48 @@ def test_decode_step_reused_workspace(B, T, k):
         assert torch.equal(o_f, o_r) and torch.equal(lse_f, lse_r), rep
 
 
+@pytest.mark.parametrize("B,T,k", [(1, 20000, 16), (8, 40000, 32)])
+def test_decode_step_graph_replays(B, T, k):
+    """The fused step captured in a HIP graph and replayed several times, with
+    eager work (outputs spoiled) and synchronisations between the replays:
+    every replay gives the eager step's bits.  The merge's arrival counts are
+    reset by a kernel of the step itself (no memset node in the graph)."""
+    S = _sas()
+    wl = synth.custom_workload("decode", batch=B, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                               sel_dim=128, top_k=k, dtype="bf16", seq_len=T,
+                               seq_len_range=(T // 2, T) if B > 1 else None)
+    p = synth.make_problem(wl, 9 + B)
+    q, K, V = dev(p.q), dev(p.K), dev(p.V)
+    lens = torch.from_numpy(p.seq_lens).cuda()
+    Wq, Wk = dev(p.Wq_sel), dev(p.Wk_sel)
+    summ = S.sas_block_summaries(K, lens, Wk)
+    ref = [t.clone() for t in S.sas_decode_step(q, K, V, lens, Wq, summ, k)]
+    dims = S.make_dims(B, 32, 8, 128, 128, k, K.shape[2], S.SAS_BF16)
+    ws = torch.empty(S.sas_workspace_bytes(S.SAS_OP_DECODE_STEP, dims), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty_like(t) for t in ref]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        S.sas_decode_step(q, K, V, lens, Wq, summ, k, idx=outs[0], log_gate=outs[1],
+                          score_lse=outs[2], o=outs[3], lse=outs[4], ws=ws)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.fill_(-3)
+        ws.fill_(rep + 1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("idx", "log_gate", "score_lse", "o", "lse"), ref, outs):
+            assert torch.equal(a, b), (rep, name)
+
+
 def test_block_summaries_range_leaves_other_rows():
     """Refreshing one block range writes exactly those rows."""
     S = _sas()
