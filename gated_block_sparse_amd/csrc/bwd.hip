@@ -38,26 +38,13 @@ __host__ __device__ inline size_t qsel_rows(int n_tiles) {
   return 1 + static_cast<size_t>(n_tiles) * (n_tiles - 1) / 2;
 }
 
-// ------------------------------------------------------------ pre-pass ---
-template <int D>
-__global__ void __launch_bounds__(256)
-bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, size_t n_rows,
-               float* __restrict__ Dq, float* __restrict__ dlg, size_t n_dlg) {
-  constexpr int LPR = D / 8;
-  const size_t g = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const size_t row = g / LPR;
-  const int col = static_cast<int>(g % LPR);
-  float acc = 0.f;
-  if (row < n_rows) {
-    float a[8], c[8];
-    Vec16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(O + row * D + col * 8), a);
-    Vec16<uint16_t>::unpack(*reinterpret_cast<const uint4*>(dO + row * D + col * 8), c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += a[e] * c[e];
-  }
-  acc = group_sum(acc, LPR);
-  if (row < n_rows && col == 0) Dq[row] = acc;
-  for (size_t i = g; i < n_dlg; i += static_cast<size_t>(gridDim.x) * blockDim.x) dlg[i] = 0.f;
+// ------------------------------------------------------------ zeroing ---
+// The per-query backward's block counts start at zero (a kernel, not a
+// memset, so that the backward can be captured in a graph).
+__global__ void __launch_bounds__(256) bwd_zero_kernel(int* __restrict__ p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
 }
 
 // ------------------------------------------------------------ dQ pass ---
@@ -67,15 +54,20 @@ bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, 
 // cursor into the query's ascending idx row, and at a block its query selected
 // it stores the sum of dS over the block's 64 tokens for its head:
 // part[b,h,i,slot], which bwd_qsel_dlg_kernel sums over the group's heads.
+//
+// The pass also forms D_i = dO_i . O_i of its queries (each lane pair holds
+// the query's dO row as its B operand; the O row comes with it) and stores
+// it for the dK/dV pass, and with one selection per tile it zeroes the
+// tile's dlog_gate row (the dK/dV pass then writes the valid slots).
 template <int D, int HPW, bool PQ>
 __global__ void __launch_bounds__(128 * HPW)
 bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-              const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-              const float* __restrict__ lse, const float* __restrict__ Dq, int S, int Hkv, int G,
-              int t_max, int n_tiles, int k, const int32_t* __restrict__ idx,
-              const float* __restrict__ log_gate, float scale2, float scale,
-              const uint32_t* __restrict__ ubits, float* __restrict__ part,
-              uint16_t* __restrict__ dQ) {
+              const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
+              const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+              float* __restrict__ Dq, int S, int Hkv, int G, int t_max, int n_tiles, int k,
+              const int32_t* __restrict__ idx, const float* __restrict__ log_gate, float scale2,
+              float scale, const uint32_t* __restrict__ ubits, float* __restrict__ part,
+              float* __restrict__ dlg, uint16_t* __restrict__ dQ) {
   constexpr int NT = 128 * HPW;
   constexpr int KS = D / 16, CT = D / 32;
   // two buffers: block i is staged in buffer i % 2 while block i-1 is used
@@ -99,20 +91,36 @@ bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const size_t qrow_i = (static_cast<size_t>(b) * Hq + h) * S + (qvalid ? qi : 0);
 
   bf16x8_t qb[KS], db[KS];  // B operands: Q[qi][..], dO[qi][..]
+  float Dv;                 // D = dO . O: this lane's half of the channels, then both halves
+  {
+    uint4 dr[KS], orow[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qb[ks] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(Q + qrow_i * D + 16 * ks + 8 * hi)
-                              : make_uint4(0, 0, 0, 0));
-    db[ks] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(dO + qrow_i * D + 16 * ks + 8 * hi)
-                              : make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t at = qrow_i * D + 16 * ks + 8 * hi;
+      qb[ks] = as_bf16x8(qvalid ? *reinterpret_cast<const uint4*>(Q + at) : make_uint4(0, 0, 0, 0));
+      dr[ks] = qvalid ? *reinterpret_cast<const uint4*>(dO + at) : make_uint4(0, 0, 0, 0);
+      orow[ks] = qvalid ? *reinterpret_cast<const uint4*>(O + at) : make_uint4(0, 0, 0, 0);
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float a[8], c[8];
+      Vec16<uint16_t>::unpack(orow[ks], a);
+      Vec16<uint16_t>::unpack(dr[ks], c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(a[e], c[e], acc);
+      db[ks] = as_bf16x8(dr[ks]);
+    }
+    Dv = acc + __shfl_xor(acc, 32, 64);
+    if (qvalid && hi == 0) Dq[qrow_i] = Dv;
   }
   const float lse2 = qvalid ? lse[qrow_i] * kLog2eF : 0.f;
-  const float Dv = qvalid ? Dq[qrow_i] : 0.f;
   f32x16_t dq[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) zero16(dq[ct]);
 
   const size_t srow = (static_cast<size_t>(b) * Hkv + r) * n_tiles + t;
+  if (!PQ && dlg && hc == 0 && wave == 0 && lane < k) dlg[srow * k + lane] = 0.f;
   const uint16_t* Kg = K + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
   const uint16_t* Vg = V + (static_cast<size_t>(b) * Hkv + r) * static_cast<size_t>(t_max) * D;
 
@@ -1303,21 +1311,18 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   int* qlist = qlists ? reinterpret_cast<int*>(wsb + lay.qlist) : nullptr;
   float* qbeta = qlists ? reinterpret_cast<float*>(wsb + lay.qbeta) : nullptr;
   const size_t groups = static_cast<size_t>(d.batch) * d.n_kv_heads;
-  const size_t n_rows = static_cast<size_t>(d.batch) * d.n_q_heads * S;
-  // The pre-pass zeroes a buffer besides forming D: the tile backward's
-  // dlog_gate (written by its dK/dV pass), or the per-query block counts
-  // (the per-query dlog_gate is written whole by its reduction kernel).
-  float* zero = PQ ? reinterpret_cast<float*>(qcnt) : dlg;
-  const size_t n_zero = PQ ? (qlists ? groups * n_tiles : 0)
-                           : ((d.top_k > 0 && dlg) ? groups * n_tiles * d.top_k : 0);
-  const size_t thr = n_rows * (D / 8);
-  const int pre_blocks = static_cast<int>((thr + 255) / 256);
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3(pre_blocks), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(O), static_cast<const uint16_t*>(dO), n_rows,
-                     Dq, zero, n_zero);
-  sas_status s = check_launch("bwd_pre");
-  if (s != SAS_OK) return s;
+  // D = rowsum(dO * O) is formed by the dQ pass, which also zeroes the tile
+  // backward's dlog_gate; the per-query block counts are zeroed here (the
+  // per-query dlog_gate is written whole by its reduction kernel).
+  sas_status s = SAS_OK;
   if constexpr (PQ) {
+    if (qlists) {
+      const size_t n_zero = groups * n_tiles;
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3(static_cast<unsigned>((n_zero + 255) / 256)),
+                         dim3(256), 0, st, qcnt, n_zero);
+      s = check_launch("bwd_zero");
+      if (s != SAS_OK) return s;
+    }
     hipLaunchKernelGGL(bwd_qsel_prep_kernel, dim3(n_tiles, d.n_kv_heads, d.batch), dim3(256), 0,
                        st, S, d.n_kv_heads, n_tiles, d.top_k, idx, log_gate, ubits, ucnt, gtab,
                        qcnt);
@@ -1341,9 +1346,10 @@ static sas_status launch_bwd_d(const sas_dims& d, const void* Q, const void* K, 
   const uint16_t* dop = static_cast<const uint16_t*>(dO);
 #define SAS_DQ_CASE(HPW)                                                                       \
   hipLaunchKernelGGL((bwd_dq_kernel<D, HPW, PQ>), dim3(n_tiles * (G / HPW), d.n_kv_heads,       \
-                     d.batch), dim3(128 * HPW), 0, st, q, kk, v, dop, lse, Dq, S, d.n_kv_heads, \
-                     G, d.t_max, n_tiles, d.top_k, idx, log_gate, scale2, scale, ubits, part,   \
-                     static_cast<uint16_t*>(dQ))
+                     d.batch), dim3(128 * HPW), 0, st, q, kk, v,                                \
+                     static_cast<const uint16_t*>(O), dop, lse, Dq, S, d.n_kv_heads, G, d.t_max, \
+                     n_tiles, d.top_k, idx, log_gate, scale2, scale, ubits, part,               \
+                     (d.top_k > 0) ? dlg : nullptr, static_cast<uint16_t*>(dQ))
   switch (G) {
     case 1: SAS_DQ_CASE(1); break;
     case 2: SAS_DQ_CASE(2); break;
