@@ -13,7 +13,7 @@
 // unnormalised partial softmax state (max, sum, acc) in the workspace.  Two
 // blocks per unit are used once the grid has enough units to fill the chip:
 // twice the bytes in flight per thread and half the partials to merge.  The
-// k+1 partials of each head are merged in slot order:
+// partials of each head (one per unit) are merged in unit order:
 //   o = sum_u e^{m_u-M} acc_u / sum_u e^{m_u-M} l_u.
 // sas_decode_fwd does it in a second, small kernel that issues all of its
 // loads at once (the kernel boundary orders the two).  The fused decode step
