@@ -139,7 +139,7 @@ selector_bwd_blocks_kernel(const T* __restrict__ K, int Hkv, int t_max, int c_ma
 // (c, half) keeps the DS/2 rows j of column c in registers, and the entries'
 // vectors are staged in LDS.  Stage 2: one thread per weight adds the
 // chunk partials in chunk order.
-constexpr int kSbChunk = 64;
+constexpr int kSbChunk = 16;
 
 template <int D, int DS>
 __global__ void __launch_bounds__(2 * D)
