@@ -602,7 +602,7 @@ def run_prefill(args, wl):
                      "achieved": round(fwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(fwd_tf / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name, PREFILL_KERNELS, PREFILL_SOURCES)},
-        "roofline_bwd": {"bound": "mfma", "kernel": "sas_bwd (pre-pass, dQ, dK/dV kernels)",
+        "roofline_bwd": {"bound": "mfma", "kernel": "sas_bwd (dQ pass with D, dK/dV pass)",
                          "achieved": round(bwd_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4)},
         "wall_s_timed_region": round(wall, 3),
