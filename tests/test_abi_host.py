@@ -139,7 +139,7 @@ def test_selector_bwd_validation(lib):
     sel = (grp * rows * c_max * 4 + 255) // 256 * 256
     rowb = (grp * rows * (2 * 128 + 128) * 4 + 255) // 256 * 256
     blkb = (grp * rows * (128 + 128) * 4 + 255) // 256 * 256
-    chunks = (grp * rows + 63) // 64      # outer-product partials of 64 entries each
+    chunks = (grp * rows + 15) // 16      # outer-product partials of 16 entries each
     assert need == sel + rowb + blkb + 2 * chunks * 128 * 128 * 4
     sb = lambda dims, q_len, ws_bytes, dlg=FAKE, dwk=FAKE: lib.sas_selector_bwd(
         ctypes.byref(dims), FAKE, q_len, FAKE, FAKE, FAKE, FAKE, FAKE, dlg, None, FAKE, dwk,
